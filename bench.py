@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""GDN recurrent-state update benchmark on one MI355X.
+
+Headline: single-token decode of a 16-key-head / 32-value-head layer with
+128 x 128 fp32 states, B = 256 sequences (state pool of 1024 slots, bf16
+q/k/v/a/b, bf16 outputs); a step is one gdn_decode_step (every decode row
+of the hot path: slot lookup, gates, state read + decay, delta, rank-1
+update + output, rounded write-back).  `value` is the algorithmic state-update
+bandwidth in GB/s (1 GB = 1e9 B) with inputs resident in HBM; tokens/s and
+the fraction of the 8 TB/s HBM peak are reported beside it.
+
+Also measured in the same run (under "rows"): bf16/fp16-state decode, the
+ReplaySSM-style replay decode (ring of 16, standard and 5-token verify
+windows) and the chunked prefill of 4 packed sequences, each with its own
+roofline object.  Inputs are seeded synthetic data (workloads/gen.py).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only ROW] [--no-rows] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 matrix
+METRIC = "GDN decode state-update GB/s + tokens/s, % of HBM peak (B=256,H=32,128×128)"
+HK, HV, D = 16, 32, 128
+NUM_SLOTS = 1024
+SB = {"f32": 4, "bf16": 2, "f16": 2}
+CSRC = os.path.join(ROOT, "gated_deltanet_state_gdn_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ byte / flop models
+def decode_bytes(B, sdt, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
+    """Algorithmic bytes of one decode step: state read + write, inputs, gates, slot map, outputs."""
+    state = 2 * B * Hv * d * d * SB[sdt]
+    inputs = B * (2 * Hk * d + Hv * d + 2 * Hv) * ib + 2 * Hv * 4 + B * 4
+    return state + inputs + B * Hv * d * ob
+
+
+def replay_entry_bytes(ib=2, Hk=HK, Hv=HV, d=D):
+    """One ring entry of one sequence: k per key head, v per value head, g and beta per value head."""
+    return (Hk * d + Hv * d) * ib + 2 * Hv * 4
+
+
+def replay_step_bytes(B, sdt, n_before, T, L, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
+    """Algorithmic bytes of one replay step of T tokens when every sequence holds n_before entries."""
+    fold = n_before + T > L
+    state = B * Hv * d * d * SB[sdt] * (2 if fold else 1)
+    entries = B * n_before * replay_entry_bytes(ib, Hk, Hv, d)       # committed entries read
+    appended = B * T * replay_entry_bytes(ib, Hk, Hv, d)             # new entries written
+    inputs = B * T * (2 * Hk * d + Hv * d + 2 * Hv) * ib + 2 * Hv * 4 + B * 4 + 2 * B * 4
+    return state + entries + appended + inputs + B * T * Hv * d * ob
+
+
+def prefill_bytes(lengths, sdt, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
+    T, N = sum(lengths), len(lengths)
+    return (T * (2 * Hk * d + Hv * d + 2 * Hv) * ib + T * Hv * d * ob + 2 * N * Hv * d * d * SB[sdt]
+            + 2 * Hv * 4 + (2 * N + 1) * 4)
+
+
+def prefill_flops(lengths, Hv=HV, d=D, C=64):
+    """FLOPs of the chunked form as computed: per (chunk, value head) K K^T, Q K^T, T R and P U
+    (2 C^2 d each) and [K; Q] S, K~^T U (2 C d^2 each, three)."""
+    chunks = sum((n + C - 1) // C for n in lengths)
+    per = 4 * 2 * C * C * d + 3 * 2 * C * d * d
+    state_kernel = 2 * 2 * C * C * d + 3 * 2 * C * d * d
+    return chunks * Hv * per, chunks * Hv * state_kernel
+
+
+# ------------------------------------------------------------------ timing helpers
+def kernel_sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(key, sources):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC) as f:
+            t = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha256") != kernel_sources_sha(sources):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def timed_launches(torch, fn, n_launch, warmup):
+    """Run fn(i) for i in [0, warmup + n) ; time the last n on the current stream with events."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    t0 = time.perf_counter()
+    for i in range(n_launch):
+        st[i].record()
+        fn(warmup + i)
+        en[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(st, en)]
+    span = st[0].elapsed_time(en[-1])
+    return dict(launch_ms=per, mean_launch_ms=sum(per) / len(per), span_ms=span, wall_s=wall)
+
+
+def roofline_bw(bytes_per_launch, mean_launch_ms, traffic):
+    gbs = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+# ------------------------------------------------------------------ workloads
+def make_pool(torch, gen, cid, slots, sdt, device):
+    import numpy as np
+    pool = torch.zeros((NUM_SLOTS, HV, D, D), dtype={"f32": torch.float32, "bf16": torch.bfloat16,
+                                                      "f16": torch.float16}[sdt], device=device)
+    chunk = 64
+    for i in range(0, len(slots), chunk):
+        sl = list(slots[i:i + chunk])
+        pool[torch.as_tensor(np.asarray(sl, np.int64), device=device)] = gen.to_torch(
+            gen.pool_slots(cid, sl, HV, D, D, sdt), device)
+    return pool
+
+
+def bench_decode(torch, gdn, gen, B, sdt, steps, warmup, cid=1):
+    dev = "cuda"
+    slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
+    pool = make_pool(torch, gen, cid, slot_map, sdt, dev)
+    A_log, dt_bias = gen.head_params(cid, HV)
+    A_d, dt_d = gen.to_torch(A_log, dev), gen.to_torch(dt_bias, dev)
+    sm = torch.from_numpy(slot_map).to(dev)
+    ins = []
+    for s in range(warmup + steps):
+        inp = gen.token_inputs(cid, s, (B,), HK, HV, D, D, "bf16")
+        ins.append([gen.to_torch(inp[x], dev) for x in "qkvab"])
+    out = torch.empty((B, HV, D), dtype=torch.bfloat16, device=dev)
+
+    def fn(i):
+        q, k, v, a, b = ins[i]
+        gdn.gdn_decode_step(q, k, v, a, b, A_d, dt_d, pool, sm, out=out)
+
+    t = timed_launches(torch, fn, steps, warmup)
+    nbytes = decode_bytes(B, sdt)
+    ms = t["span_ms"] / steps
+    res = {
+        "B": B, "state": sdt, "ms_per_step": round(ms, 5), "mean_launch_us": round(t["mean_launch_ms"] * 1e3, 2),
+        "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "bytes_per_step": nbytes,
+        "working_set_MiB": round(B * HV * D * D * SB[sdt] / 2 ** 20, 1),
+    }
+    src = ["gdn_decode.hip", "gdn_device.h"]
+    res["roofline"] = roofline_bw(nbytes, t["mean_launch_ms"], traffic_for(f"decode_{sdt}_B{B}", src))
+    if res["working_set_MiB"] <= 256:
+        res["note"] = "state working set fits the 256 MB Infinity Cache: cache-assisted, not an HBM-only figure"
+    del pool, ins
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
+    """Aligned rings (every sequence starts empty): 1 untimed cycle, then `cycles` timed cycles."""
+    dev = "cuda"
+    steps_per_cycle = L // T if T > 1 else L
+    slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
+    ckpt = make_pool(torch, gen, cid, slot_map, sdt, dev)
+    ring = gdn.new_ring(NUM_SLOTS, HV, L, D, D, torch.bfloat16, dev)
+    A_log, dt_bias = gen.head_params(cid, HV)
+    A_d, dt_d = gen.to_torch(A_log, dev), gen.to_torch(dt_bias, dev)
+    sm = torch.from_numpy(slot_map).to(dev)
+    n_in = steps_per_cycle * 2  # inputs are reused across cycles
+    ins = []
+    for s in range(n_in):
+        inp = gen.token_inputs(cid, s, (B, T), HK, HV, D, D, "bf16")
+        ins.append([gen.to_torch(inp[x], dev) for x in "qkvab"])
+    out = torch.empty((B, T, HV, D), dtype=torch.bfloat16, device=dev)
+    zero_rej = torch.zeros(B, dtype=torch.int32, device=dev)
+    warm = steps_per_cycle
+    n = cycles * steps_per_cycle
+
+    def fn(i):
+        q, k, v, a, b = ins[i % n_in]
+        gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out)
+
+    t = timed_launches(torch, fn, n, warm)
+    # byte model follows the (deterministic) per-slot count of the aligned schedule
+    cnt, nbytes = 0, 0
+    for i in range(warm + n):
+        b_i = replay_step_bytes(B, sdt, cnt, T, L)
+        if cnt + T > L:
+            cnt = 0
+        cnt += T
+        if i >= warm:
+            nbytes += b_i
+    ms = t["span_ms"] / n
+    res = {
+        "B": B, "ckpt": sdt, "L": L, "T": T, "ms_per_step": round(ms, 5),
+        "mean_launch_us": round(t["mean_launch_ms"] * 1e3, 2),
+        "GB_per_s": round(nbytes / n / (ms * 1e-3) / 1e9, 1), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "bytes_per_step_avg": nbytes // n,
+        "vs_decode_bytes": round(nbytes / n / (T * decode_bytes(B, sdt)), 3),
+    }
+    src = ["gdn_replay.hip", "gdn_device.h"]
+    res["roofline"] = roofline_bw(nbytes / n, t["mean_launch_ms"], traffic_for(f"replay_{sdt}_B{B}_T{T}", src))
+    del ckpt, ring, ins
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
+    import numpy as np
+    dev = "cuda"
+    lengths = gen.CONFIGS[3].extra["lengths"]
+    N = len(lengths)
+    cu = gen.seq_lengths_cu(lengths)
+    slot_map = gen.slot_permutation(cid, 16)[:N]
+    pool = torch.zeros((16, HV, D, D), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[sdt], device=dev)
+    pool[torch.as_tensor(slot_map.astype(np.int64), device=dev)] = gen.to_torch(
+        gen.pool_slots(cid, slot_map, HV, D, D, sdt), dev)
+    inp = gen.token_inputs(cid, 0, (int(cu[-1]),), HK, HV, D, D, "bf16")
+    A_log, dt_bias = gen.head_params(cid, HV)
+    args = [gen.to_torch(inp[x], dev) for x in "qkvab"] + [gen.to_torch(A_log, dev), gen.to_torch(dt_bias, dev)]
+    sm, cu_d = torch.from_numpy(slot_map).to(dev), torch.from_numpy(cu).to(dev)
+    out = torch.empty((int(cu[-1]), HV, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.gdn_chunk_prefill_workspace_bytes(HK, HV, D, D, N, int(cu[-1])), dtype=torch.uint8,
+                     device=dev)
+
+    def fn(i):
+        gdn.gdn_chunk_prefill(*args, pool, sm, cu_d, out=out, workspace=ws)
+
+    t = timed_launches(torch, fn, reps, 2)
+    nbytes = prefill_bytes(lengths, sdt)
+    flops, flops_state = prefill_flops(lengths)
+    ms = t["span_ms"] / reps
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "lengths": lengths, "state": sdt, "ms_per_call": round(ms, 4), "tokens_per_s": round(sum(lengths) / (ms * 1e-3)),
+        "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes, "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tf / FP32_MFMA_PEAK_TFS, 4), "traffic": None,
+                     "scope": "whole call (chunk kernel + state kernel), fp32 MFMA peak"},
+        "workspace_MiB": round(ws.numel() / 2 ** 20, 1),
+    }
+    del pool, ws, out, args
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(gen, seconds=12.0):
+    """The CPU oracle on a bounded sample of the headline workload, one thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is present in this image
+        limiter = None
+    import oracle as O
+    B, cid = 256, 1
+    slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
+    A_log, dt_bias = gen.head_params(cid, HV)
+    rows, done, elapsed, step = 16, 0, 0.0, 0
+    pool = gen.pool_slots(cid, slot_map[:rows], HV, D, D, "f32")
+    local = list(range(rows))
+    while elapsed < seconds and step < 64:
+        inp = gen.token_inputs(cid, step, (B,), HK, HV, D, D, "bf16")
+        sub = {k: v[:rows] for k, v in inp.items()}
+        t0 = time.perf_counter()
+        pool, _ = O.decode_step(pool, local, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], A_log, dt_bias)
+        elapsed += time.perf_counter() - t0
+        done += rows
+        step += 1
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    tok_s = done / elapsed
+    return {"value": round(tok_s * decode_bytes(1, "f32") / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(tok_s, 1),
+            "sample": f"{rows} sequences x 32 value heads x {step} decode steps of the B=256 fp32-state layer "
+                      f"({elapsed:.1f} s of oracle compute, float64 numpy, one thread)"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default=None, help="run one row only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
+                                                    "prefill_<dt>")
+    ap.add_argument("--no-rows", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the per-(sequence, head) units shard across GPUs without any exchange, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    from workloads import gen
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdn.lib()
+
+    if args.only:
+        kind, dt, *rest = args.only.split("_")
+        if kind == "decode":
+            r = bench_decode(torch, gdn, gen, int(rest[0][1:]) if rest else 256, dt, args.steps, args.warmup)
+        elif kind == "replay":
+            r = bench_replay(torch, gdn, gen, 512, dt, int(rest[0][1:]) if rest else 1, 2)
+        elif kind == "prefill":
+            r = bench_prefill(torch, gdn, gen, dt, max(args.steps // 8, 2))
+        else:
+            raise SystemExit(f"unknown row {args.only}")
+        print(json.dumps({"row": args.only, **r}))
+        return
+
+    log(f"headline: decode B=256 fp32 state, {args.warmup} warmup + {args.steps} timed steps")
+    head = bench_decode(torch, gdn, gen, 256, "f32", args.steps, args.warmup)
+    log(f"  {head['ms_per_step'] * 1e3:.1f} us/step, {head['GB_per_s']} GB/s")
+    rows = {}
+    if not args.no_rows:
+        for B, dt in ((512, "f32"), (256, "bf16"), (512, "bf16"), (512, "f16"), (64, "bf16"), (1, "bf16")):
+            log(f"row: decode B={B} {dt} state")
+            rows[f"decode_{dt}_B{B}"] = bench_decode(torch, gdn, gen, B, dt, args.steps, args.warmup)
+        for dt, T, cyc in (("f32", 1, 4), ("bf16", 1, 4), ("f32", 5, 8)):
+            log(f"row: replay B=512 {dt} checkpoint T={T}")
+            rows[f"replay_{dt}_B512_T{T}"] = bench_replay(torch, gdn, gen, 512, dt, T, cyc)
+        for dt in ("f32", "bf16"):
+            log(f"row: chunked prefill {dt} state")
+            rows[f"prefill_{dt}"] = bench_prefill(torch, gdn, gen, dt, 8)
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline: oracle sample")
+        cpu = cpu_baseline(gen)
+
+    ms = head["ms_per_step"]
+    line = {
+        "metric": METRIC, "value": head["GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded workloads/gen.py)",
+        "tokens_per_s": head["tokens_per_s"], "hbm_peak_frac": round(head["GB_per_s"] / HBM_PEAK_GBS, 4),
+        "config": {"workload": "gdn_decode_step: B=256 sequences, 16 key / 32 value heads, dk=dv=128, fp32 state "
+                               "in a 1024-slot pool, bf16 q/k/v/a/b, bf16 out, one token per step",
+                   "B": 256, "Hk": HK, "Hv": HV, "dk": D, "dv": D, "state_dtype": "f32",
+                   "bytes_per_step": head["bytes_per_step"]},
+        "roofline": dict(head["roofline"], kernel="gdn_decode_kernel<f32,128>",
+                         mean_launch_us=head["mean_launch_us"]),
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,241 @@
+"""ctypes binding of libgdn.so (include/gdn.h).
+
+Argument marshalling only: shapes are read off torch tensors, pointers and
+sizes are handed to the C ABI, and every step of the computation runs in the
+HIP kernels behind it.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
+
+# every symbol include/gdn.h declares
+EXPORTS = (
+    "gdn_decode_step", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_decode",
+    "gdn_replay_flush", "gdn_replay_rollback", "gdn_status_string", "gdn_last_error",
+)
+
+
+class gdn_dims(ctypes.Structure):
+    _fields_ = [("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class gdn_gates(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
+class gdn_pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("dtype", ctypes.c_int), ("num_slots", ctypes.c_int64)]
+
+
+class gdn_ring(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("start", ctypes.c_void_p), ("count", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
+                ("L", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_state_gdn_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    pd, pg, pp, pr = (ctypes.POINTER(gdn_dims), ctypes.POINTER(gdn_gates), ctypes.POINTER(gdn_pool),
+                      ctypes.POINTER(gdn_ring))
+    sig = {
+        "gdn_decode_step": (INT, [pd, I32, P, P, P, INT, pg, pp, P, P, INT, P]),
+        "gdn_chunk_prefill_workspace_bytes": (SZ, [pd, I32, I64, I32]),
+        "gdn_chunk_prefill": (INT, [pd, I32, P, I64, I32, P, P, P, INT, pg, pp, P, P, INT, P, SZ, P]),
+        "gdn_replay_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P]),
+        "gdn_replay_flush": (INT, [pd, I32, pp, P, pr, P]),
+        "gdn_replay_rollback": (INT, [pd, I32, P, P, pr, P]),
+        "gdn_status_string": (ctypes.c_char_p, [INT]),
+        "gdn_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        L = lib()
+        raise GdnError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    codes = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
+def _ptr(t) -> int:
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the GDN library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dims(Hk, Hv, dk, dv, scale):
+    return gdn_dims(int(Hk), int(Hv), int(dk), int(dv), float(scale) if scale else 0.0)
+
+
+def _gates(a, b, A_log, dt_bias):
+    return gdn_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias))
+
+
+def _pool(pool):
+    return gdn_pool(_ptr(pool), dtype_code(pool.dtype), int(pool.shape[0]))
+
+
+@dataclass
+class Ring:
+    """Per (slot, value head) ring of ReplaySSM inputs (layout of gdn_ring)."""
+    k: object      # [num_slots, Hv, L, dk]
+    v: object      # [num_slots, Hv, L, dv]
+    g: object      # [num_slots, Hv, L] float32
+    beta: object   # [num_slots, Hv, L] float32
+    start: object  # [num_slots, Hv] int32
+    count: object  # [num_slots, Hv] int32
+
+    @property
+    def L(self) -> int:
+        return int(self.g.shape[2])
+
+    def c_struct(self) -> gdn_ring:
+        return gdn_ring(_ptr(self.k), _ptr(self.v), _ptr(self.g), _ptr(self.beta), _ptr(self.start),
+                        _ptr(self.count), int(self.g.shape[0]), self.L, dtype_code(self.k.dtype))
+
+
+def new_ring(num_slots, Hv, L, dk, dv, dtype, device) -> Ring:
+    torch = _torch()
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+    return Ring(k=z((num_slots, Hv, L, dk), dtype), v=z((num_slots, Hv, L, dv), dtype),
+                g=z((num_slots, Hv, L), torch.float32), beta=z((num_slots, Hv, L), torch.float32),
+                start=z((num_slots, Hv), torch.int32), count=z((num_slots, Hv), torch.int32))
+
+
+# ------------------------------------------------------------------ entry points
+def gdn_decode_step(q, k, v, a, b, A_log, dt_bias, pool, slot_map, out=None, out_dtype=None, scale=None,
+                    stream=None):
+    """One decode step; q, k [B, Hk, dk]; v [B, Hv, dv]; a, b [B, Hv]; pool [slots, Hv, dk, dv]."""
+    torch = _torch()
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if out is None:
+        out = torch.empty((B, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+    dims = _dims(Hk, Hv, dk, dv, scale)
+    _check(lib().gdn_decode_step(ctypes.byref(dims), B, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
+                                 ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(pool)),
+                                 _ptr(slot_map), _ptr(out), dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def gdn_chunk_prefill_workspace_bytes(Hk, Hv, dk, dv, N, total_tokens, chunk=64) -> int:
+    dims = _dims(Hk, Hv, dk, dv, None)
+    return int(lib().gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), int(N), int(total_tokens), int(chunk)))
+
+
+def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, pool, slot_map, cu_seqlens, out=None, out_dtype=None,
+                      chunk=64, workspace=None, scale=None, stream=None):
+    """Packed prefill; q, k [T, Hk, dk]; v [T, Hv, dv]; a, b [T, Hv]; cu_seqlens int32 [N+1] (device)."""
+    torch = _torch()
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    N = int(cu_seqlens.shape[0]) - 1
+    if out is None:
+        out = torch.empty((T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+    need = gdn_chunk_prefill_workspace_bytes(Hk, Hv, dk, dv, N, T, chunk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dims = _dims(Hk, Hv, dk, dv, scale)
+    _check(lib().gdn_chunk_prefill(ctypes.byref(dims), N, _ptr(cu_seqlens), T, chunk, _ptr(q), _ptr(k), _ptr(v),
+                                   dtype_code(q.dtype), ctypes.byref(_gates(a, b, A_log, dt_bias)),
+                                   ctypes.byref(_pool(pool)), _ptr(slot_map), _ptr(out), dtype_code(out.dtype),
+                                   ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring, out=None, out_dtype=None,
+                      scale=None, stream=None):
+    """Replay step of T tokens; q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, b [B, T, Hv]."""
+    torch = _torch()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+    dims = _dims(Hk, Hv, dk, dv, scale)
+    rs = ring.c_struct()
+    _check(lib().gdn_replay_decode(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
+                                   ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(ckpt)),
+                                   _ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype),
+                                   _stream(stream)))
+    return out
+
+
+def gdn_replay_flush(ckpt, slot_map, ring: Ring, Hk, stream=None):
+    """Fold every committed ring entry of the mapped slots into their checkpoints."""
+    Hv, dk, dv = ckpt.shape[1], ckpt.shape[2], ckpt.shape[3]
+    dims = _dims(Hk, Hv, dk, dv, None)
+    rs = ring.c_struct()
+    _check(lib().gdn_replay_flush(ctypes.byref(dims), int(slot_map.shape[0]), ctypes.byref(_pool(ckpt)),
+                                  _ptr(slot_map), ctypes.byref(rs), _stream(stream)))
+
+
+def gdn_replay_rollback(slot_map, num_rejected, ring: Ring, Hk, dk, stream=None):
+    """count <- max(count - num_rejected[b], 0) for every value head of row b's slot."""
+    Hv = int(ring.g.shape[1])
+    dims = _dims(Hk, Hv, dk, dk, None)
+    rs = ring.c_struct()
+    _check(lib().gdn_replay_rollback(ctypes.byref(dims), int(slot_map.shape[0]), _ptr(slot_map),
+                                     _ptr(num_rejected), ctypes.byref(rs), _stream(stream)))
+
+
+def gdn_status_string(status: int) -> str:
+    return lib().gdn_status_string(int(status)).decode()
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()

@@ -1,0 +1,270 @@
+// C ABI of the GDN state-update library: argument validation and dispatch.
+//
+// Every entry point validates synchronously on the host and only then
+// enqueues kernels on the caller's stream.  Nothing is allocated and no state
+// is kept between calls except the calling thread's last-error text.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gdn_status ok() {
+  g_last_error[0] = '\0';
+  return GDN_OK;
+}
+
+bool valid_dtype(int dt) { return dt == GDN_F32 || dt == GDN_BF16 || dt == GDN_F16; }
+size_t dtype_bytes(int dt) { return dt == GDN_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define GDN_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define GDN_TRY(expr)                   \
+  do {                                  \
+    gdn_status st_ = (expr);            \
+    if (st_ != GDN_OK) return st_;      \
+  } while (0)
+
+gdn_status check_dims(const gdn_dims* d) {
+  GDN_REQUIRE(d != nullptr, GDN_EINVAL, "dims is NULL");
+  GDN_REQUIRE(d->num_k_heads >= 1 && d->num_v_heads >= 1, GDN_EINVAL, "head counts must be >= 1 (Hk=%d Hv=%d)",
+              d->num_k_heads, d->num_v_heads);
+  GDN_REQUIRE(d->num_v_heads % d->num_k_heads == 0, GDN_EINVAL, "Hv=%d is not a multiple of Hk=%d",
+              d->num_v_heads, d->num_k_heads);
+  GDN_REQUIRE(d->dk >= 1 && d->dv >= 1, GDN_EINVAL, "head dims must be >= 1 (dk=%d dv=%d)", d->dk, d->dv);
+  GDN_REQUIRE(d->dk == d->dv && (d->dk == 16 || d->dk == 32 || d->dk == 64 || d->dk == 128), GDN_EUNSUPPORTED,
+              "head dims dk=%d dv=%d: compiled for dk == dv in {16, 32, 64, 128}", d->dk, d->dv);
+  return GDN_OK;
+}
+
+float eff_scale(const gdn_dims* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->dk); }
+
+gdn_status check_pool(const gdn_pool* p, const char* what) {
+  GDN_REQUIRE(p != nullptr, GDN_EINVAL, "%s pool is NULL", what);
+  GDN_REQUIRE(p->base != nullptr, GDN_EINVAL, "%s pool base is NULL", what);
+  GDN_REQUIRE(valid_dtype(p->dtype), GDN_EINVAL, "%s pool dtype %d is not a gdn_dtype", what, (int)p->dtype);
+  GDN_REQUIRE(aligned(p->base, 16), GDN_EINVAL, "%s pool base is not 16-byte aligned", what);
+  GDN_REQUIRE(p->num_slots >= 1 && p->num_slots <= INT32_MAX, GDN_EINVAL, "%s pool num_slots=%lld out of range",
+              what, (long long)p->num_slots);
+  return GDN_OK;
+}
+
+gdn_status check_gates(const gdn_gates* g, int in_dt) {
+  GDN_REQUIRE(g != nullptr, GDN_EINVAL, "gates is NULL");
+  GDN_REQUIRE(g->a && g->b && g->A_log && g->dt_bias, GDN_EINVAL, "a gate pointer is NULL");
+  const size_t eb = dtype_bytes(in_dt);
+  GDN_REQUIRE(aligned(g->a, eb) && aligned(g->b, eb) && aligned(g->A_log, 4) && aligned(g->dt_bias, 4),
+              GDN_EINVAL, "a gate pointer is misaligned for its dtype");
+  return GDN_OK;
+}
+
+gdn_status check_dtypes(int in_dt, int out_dt) {
+  GDN_REQUIRE(valid_dtype(in_dt), GDN_EINVAL, "in_dtype %d is not a gdn_dtype", in_dt);
+  GDN_REQUIRE(valid_dtype(out_dt), GDN_EINVAL, "out_dtype %d is not a gdn_dtype", out_dt);
+  return GDN_OK;
+}
+
+gdn_status check_io(const void* q, const void* k, const void* v, int in_dt, const void* out, int out_dt) {
+  GDN_TRY(check_dtypes(in_dt, out_dt));
+  GDN_REQUIRE(q && k && v, GDN_EINVAL, "q, k or v is NULL");
+  GDN_REQUIRE(out != nullptr, GDN_EINVAL, "out is NULL");
+  const size_t eb = dtype_bytes(in_dt);
+  GDN_REQUIRE(aligned(q, eb) && aligned(k, eb) && aligned(v, eb), GDN_EINVAL, "q, k or v misaligned for in_dtype");
+  GDN_REQUIRE(aligned(out, dtype_bytes(out_dt)), GDN_EINVAL, "out misaligned for out_dtype");
+  return GDN_OK;
+}
+
+gdn_status check_ring(const gdn_ring* r, int in_dt) {
+  GDN_REQUIRE(r != nullptr, GDN_EINVAL, "ring is NULL");
+  GDN_REQUIRE(r->k && r->v && r->g && r->beta && r->start && r->count, GDN_EINVAL, "a ring pointer is NULL");
+  GDN_REQUIRE(r->num_slots >= 1 && r->num_slots <= INT32_MAX, GDN_EINVAL, "ring num_slots=%lld out of range",
+              (long long)r->num_slots);
+  GDN_REQUIRE(r->L >= 1, GDN_EINVAL, "ring length L=%d must be >= 1", r->L);
+  GDN_REQUIRE(r->L <= 64, GDN_EUNSUPPORTED, "ring length L=%d: at most 64 is supported", r->L);
+  GDN_REQUIRE(valid_dtype(r->dtype), GDN_EINVAL, "ring dtype %d is not a gdn_dtype", (int)r->dtype);
+  if (in_dt >= 0)
+    GDN_REQUIRE((int)r->dtype == in_dt, GDN_EINVAL, "ring dtype %d differs from in_dtype %d", (int)r->dtype, in_dt);
+  const size_t eb = dtype_bytes(r->dtype);
+  GDN_REQUIRE(aligned(r->k, eb) && aligned(r->v, eb) && aligned(r->g, 4) && aligned(r->beta, 4) &&
+                  aligned(r->start, 4) && aligned(r->count, 4),
+              GDN_EINVAL, "a ring pointer is misaligned");
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(GDN_ELAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gdn::RingArgs ring_args(const gdn_ring* r) {
+  return gdn::RingArgs{r->k, r->v, r->g, r->beta, r->start, r->count, r->L};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK: success";
+    case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+    case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: request outside the compiled configurations";
+    case GDN_ELAUNCH: return "GDN_ELAUNCH: kernel launch failed";
+    default: return "unknown gdn_status";
+  }
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+gdn_status gdn_decode_step(const gdn_dims* dims, int32_t B, const void* q, const void* k, const void* v,
+                           gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* state,
+                           const int32_t* slot_map, void* out, gdn_dtype out_dtype, void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_io(q, k, v, in_dtype, out, out_dtype));
+  GDN_TRY(check_gates(gates, in_dtype));
+  GDN_TRY(check_pool(state, "state"));
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::DecodeArgs a{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, state->base, slot_map, out,
+                    state->num_slots, B, dims->num_k_heads, dims->num_v_heads, (int32_t)in_dtype,
+                    (int32_t)out_dtype, eff_scale(dims)};
+  return launched(gdn::launch_decode(a, state->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_chunk_prefill_workspace_bytes(const gdn_dims* dims, int32_t N, int64_t total_tokens, int32_t chunk) {
+  if (dims == nullptr || N <= 0 || total_tokens <= 0 || chunk != 64 || dims->num_v_heads < 1) return 0;
+  return gdn::prefill_workspace_bytes(N, total_tokens, dims->num_v_heads);
+}
+
+gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_seqlens, int64_t total_tokens,
+                             int32_t chunk, const void* q, const void* k, const void* v, gdn_dtype in_dtype,
+                             const gdn_gates* gates, const gdn_pool* state, const int32_t* slot_map, void* out,
+                             gdn_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(N >= 0, GDN_EINVAL, "N=%d must be >= 0", N);
+  GDN_REQUIRE(total_tokens >= 0 && total_tokens <= INT32_MAX, GDN_EINVAL, "total_tokens=%lld out of [0, 2^31)",
+              (long long)total_tokens);
+  GDN_REQUIRE(chunk == 64, GDN_EUNSUPPORTED, "chunk=%d: only 64 is compiled", chunk);
+  GDN_REQUIRE((int64_t)N * dims->num_v_heads <= INT32_MAX / 4, GDN_EINVAL, "N * Hv exceeds the grid limit");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  if (N == 0 || total_tokens == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_io(q, k, v, in_dtype, out, out_dtype));
+  GDN_TRY(check_gates(gates, in_dtype));
+  GDN_TRY(check_pool(state, "state"));
+  GDN_REQUIRE(cu_seqlens != nullptr && aligned(cu_seqlens, 4), GDN_EINVAL, "cu_seqlens is NULL or misaligned");
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  const size_t need = gdn_chunk_prefill_workspace_bytes(dims, N, total_tokens, chunk);
+  GDN_REQUIRE(workspace_bytes >= need, GDN_EINVAL, "workspace of %zu bytes is below the %zu required",
+              workspace_bytes, need);
+  GDN_REQUIRE(need == 0 || (workspace != nullptr && aligned(workspace, 256)), GDN_EINVAL,
+              "workspace is NULL or not 256-byte aligned");
+  GDN_REQUIRE(gdn::prefill_chunk_slots_fit(N, total_tokens, dims->num_v_heads), GDN_EINVAL,
+              "N + total_tokens / 64 chunk slots exceed the grid limit");
+  gdn::PrefillArgs a{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, state->base, slot_map, cu_seqlens,
+                     out, state->num_slots, total_tokens, N, dims->num_k_heads, dims->num_v_heads,
+                     (int32_t)in_dtype, (int32_t)out_dtype, eff_scale(dims)};
+  return launched(gdn::launch_prefill(a, state->dtype, dims->dk, chunk, static_cast<float*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                             const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
+                             const int32_t* slot_map, const gdn_ring* ring, void* out, gdn_dtype out_dtype,
+                             void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  GDN_REQUIRE(ring != nullptr, GDN_EINVAL, "ring is NULL");
+  GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_io(q, k, v, in_dtype, out, out_dtype));
+  GDN_TRY(check_gates(gates, in_dtype));
+  GDN_TRY(check_pool(ckpt, "checkpoint"));
+  GDN_TRY(check_ring(ring, in_dtype));
+  GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
+              (long long)ring->num_slots, (long long)ckpt->num_slots);
+  GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
+  GDN_REQUIRE(gdn::replay_lds_total(ckpt->dtype, dims->dk, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+              "ring length L=%d with window T=%d at dk=%d exceeds the 64 KiB LDS staging budget", ring->L, T,
+              dims->dk);
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::ReplayArgs a{};
+  a.d = gdn::DecodeArgs{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, ckpt->base, slot_map, out,
+                        ckpt->num_slots, B, dims->num_k_heads, dims->num_v_heads, (int32_t)in_dtype,
+                        (int32_t)out_dtype, eff_scale(dims)};
+  a.ring = ring_args(ring);
+  a.T = T;
+  return launched(gdn::launch_replay(a, ckpt->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt, const int32_t* slot_map,
+                            const gdn_ring* ring, void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_pool(ckpt, "checkpoint"));
+  GDN_TRY(check_ring(ring, -1));
+  GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
+              (long long)ring->num_slots, (long long)ckpt->num_slots);
+  GDN_REQUIRE(gdn::replay_lds_total(ckpt->dtype, dims->dk, ring->L, 0) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+              "ring length L=%d at dk=%d exceeds the 64 KiB LDS staging budget", ring->L, dims->dk);
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::ReplayArgs a{};
+  a.d.pool = ckpt->base;
+  a.d.slot_map = slot_map;
+  a.d.num_slots = ckpt->num_slots;
+  a.d.B = B;
+  a.d.Hk = dims->num_k_heads;
+  a.d.Hv = dims->num_v_heads;
+  a.d.in_dt = (int32_t)ring->dtype;
+  a.d.scale = eff_scale(dims);
+  a.ring = ring_args(ring);
+  a.T = 0;
+  return launched(gdn::launch_replay_flush(a, ckpt->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* slot_map, const int32_t* num_rejected,
+                               const gdn_ring* ring, void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_ring(ring, -1));
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  GDN_REQUIRE(num_rejected != nullptr && aligned(num_rejected, 4), GDN_EINVAL, "num_rejected is NULL or misaligned");
+  gdn::ReplayArgs a{};
+  a.d.slot_map = slot_map;
+  a.d.B = B;
+  a.d.Hk = dims->num_k_heads;
+  a.d.Hv = dims->num_v_heads;
+  a.d.num_slots = ring->num_slots;
+  a.ring = ring_args(ring);
+  a.num_rejected = num_rejected;
+  return launched(gdn::launch_replay_rollback(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

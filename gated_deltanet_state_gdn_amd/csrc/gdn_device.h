@@ -1,0 +1,179 @@
+// Device-side helpers shared by the GDN kernels (gfx950, wave64).
+//
+// Storage types: the state and the inputs are f32, bf16 or f16 in memory and
+// always FP32 in registers (vLLM PR #52191 page, implementation item 4: FP32
+// math, narrow storage, one rounding per write-back).  Narrowing uses the
+// gfx950 packed converts (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), which round
+// to nearest-even under the default mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ scalars
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Two floats -> one packed word of two 16-bit values (element 0 in the low half).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x0, float x1);
+template <>
+__device__ __forceinline__ uint32_t pack2<GDN_BF16>(float x0, float x1) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 r = {(__bf16)x0, (__bf16)x1};
+  return __builtin_bit_cast(uint32_t, r);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<GDN_F16>(float x0, float x1) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 r = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack_lo(uint32_t w) {
+  return DT == GDN_BF16 ? bf16_bits_to_f32(w & 0xffffu) : f16_bits_to_f32(w & 0xffffu);
+}
+template <int DT>
+__device__ __forceinline__ float unpack_hi(uint32_t w) {
+  return DT == GDN_BF16 ? __uint_as_float(w & 0xffff0000u) : f16_bits_to_f32(w >> 16);
+}
+
+// Element i of a tensor whose dtype is only known at run time (inputs, outputs,
+// small per-token vectors: never the state stream).
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  if (dt == GDN_F32) return static_cast<const float*>(p)[i];
+  const uint32_t h = static_cast<const uint16_t*>(p)[i];
+  return dt == GDN_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float x, int dt) {
+  if (dt == GDN_F32) {
+    static_cast<float*>(p)[i] = x;
+  } else if (dt == GDN_BF16) {
+    static_cast<__bf16*>(p)[i] = (__bf16)x;
+  } else {
+    static_cast<_Float16*>(p)[i] = (_Float16)x;
+  }
+}
+
+// Raw copy of one element (ring append keeps the input bytes bit-exact).
+__device__ __forceinline__ void copy_elem(void* dst, int64_t di, const void* src, int64_t si, int dt) {
+  if (dt == GDN_F32) {
+    static_cast<uint32_t*>(dst)[di] = static_cast<const uint32_t*>(src)[si];
+  } else {
+    static_cast<uint16_t*>(dst)[di] = static_cast<const uint16_t*>(src)[si];
+  }
+}
+
+// ------------------------------------------------------------------ gates
+// g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b); softplus is the
+// exact max(x,0) + log1p(exp(-|x|)) (no threshold linearisation).
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
+  return -expf(A_log) * softplus_f(a + dt_bias);
+}
+
+// ------------------------------------------------------------------ state tiles
+// Storage element type per state dtype.
+template <int DT> struct StateElem { typedef uint16_t T; static constexpr int BYTES = 2; };
+template <> struct StateElem<GDN_F32> { typedef float T; static constexpr int BYTES = 4; };
+
+// VEC consecutive state elements <-> VEC floats, one 8- or 16-byte access.
+// NT selects non-temporal (streaming) loads and stores.
+template <int DT, int VEC, bool NT>
+struct TileIO {
+  static_assert(VEC * StateElem<DT>::BYTES == 16 || VEC * StateElem<DT>::BYTES == 8, "8/16-byte vectors");
+  static constexpr int WORDS = VEC * StateElem<DT>::BYTES / 4;
+
+  __device__ __forceinline__ static void load(const void* p, float (&f)[VEC]) {
+    if constexpr (WORDS == 4) {
+      u32x4 w = NT ? __builtin_nontemporal_load(static_cast<const u32x4*>(p)) : *static_cast<const u32x4*>(p);
+      unpack<4>(w, f);
+    } else {
+      u32x2 w = NT ? __builtin_nontemporal_load(static_cast<const u32x2*>(p)) : *static_cast<const u32x2*>(p);
+      unpack<2>(w, f);
+    }
+  }
+  __device__ __forceinline__ static void store(void* p, const float (&f)[VEC]) {
+    if constexpr (WORDS == 4) {
+      u32x4 w;
+      pack<4>(f, w);
+      if (NT) __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+      else *static_cast<u32x4*>(p) = w;
+    } else {
+      u32x2 w;
+      pack<2>(f, w);
+      if (NT) __builtin_nontemporal_store(w, static_cast<u32x2*>(p));
+      else *static_cast<u32x2*>(p) = w;
+    }
+  }
+
+ private:
+  template <int N, typename W>
+  __device__ __forceinline__ static void unpack(const W& w, float (&f)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (DT == GDN_F32) {
+        f[i] = __uint_as_float(w[i]);
+      } else {
+        f[2 * i] = unpack_lo<DT>(w[i]);
+        f[2 * i + 1] = unpack_hi<DT>(w[i]);
+      }
+    }
+  }
+  template <int N, typename W>
+  __device__ __forceinline__ static void pack(const float (&f)[VEC], W& w) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (DT == GDN_F32) {
+        w[i] = __float_as_uint(f[i]);
+      } else {
+        w[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------ wave64 reductions
+template <int OFF_FROM>
+__device__ __forceinline__ float xor_sum_from(float x) {
+  // Sum over the lanes that differ only in bits >= log2(OFF_FROM).
+#pragma unroll
+  for (int off = OFF_FROM; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return xor_sum_from<1>(x); }
+
+// ------------------------------------------------------------------ tile geometry
+// A workgroup of NW waves streams one dk x dv tile (dk == dv == D).  Each lane
+// owns VEC consecutive columns of a row; LPR lanes cover a row, a wave covers
+// RPW rows per pass and the workgroup NW * RPW rows per pass.  Lanes with equal
+// (lane % LPR) own the same columns, so column sums over the rows need a
+// butterfly over lane bits >= log2(LPR) and then a sum over the NW waves.
+template <int DT, int D>
+struct TileGeom {
+  static constexpr int BYTES = StateElem<DT>::BYTES;
+  // widest vector (16 B) that still leaves at least one row per wave
+  static constexpr int VEC0 = 16 / BYTES;
+  static constexpr int VEC = (64 / (D / VEC0) > D) ? VEC0 / 2 : VEC0;
+  static constexpr int LPR = D / VEC;
+  static constexpr int RPW = 64 / LPR;
+  static constexpr int NW = (D / RPW) >= 4 ? 4 : (D / RPW);
+  static constexpr int PASSES = D / (RPW * NW);
+  static_assert(LPR * VEC == D && LPR * RPW == 64 && PASSES * RPW * NW == D, "tile geometry");
+};
+
+}  // namespace gdn

@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (gdn_api.cpp) and the kernels.
+// Arguments here are already validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  void* pool;
+  const int32_t* slot_map;
+  void* out;
+  int64_t num_slots;
+  int32_t B, Hk, Hv;
+  int32_t in_dt, out_dt;
+  float scale;
+};
+
+struct RingArgs {
+  void* k;
+  void* v;
+  float* g;
+  float* beta;
+  int32_t* start;
+  int32_t* count;
+  int32_t L;
+};
+
+struct ReplayArgs {
+  DecodeArgs d;  // q, k, v, a, b laid out [B, T, H, d]; pool is the checkpoint pool
+  RingArgs ring;
+  int32_t T;     // 1..L; 0 selects the flush-only kernel
+  const int32_t* num_rejected;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+  void* pool;
+  const int32_t* slot_map;
+  const int32_t* cu_seqlens;
+  void* out;
+  int64_t num_slots;
+  int64_t total_tokens;
+  int32_t N, Hk, Hv;
+  int32_t in_dt, out_dt;
+  float scale;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_decode(const DecodeArgs& a, int state_dt, int D, hipStream_t s);
+hipError_t launch_replay(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
+hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
+hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s);
+
+// Total LDS (static + dynamic) of one replay workgroup; launches need <= 64 KiB.
+size_t replay_lds_total(int state_dt, int D, int L, int T);
+constexpr size_t kMaxLds = 65536;
+
+// Workspace of the chunked prefill: per (chunk slot, value head) the inverse
+// T, the causal decay-weighted Q K^T, gamma and beta of one chunk.
+size_t prefill_workspace_bytes(int N, int64_t total, int Hv);
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hv);
+
+}  // namespace gdn

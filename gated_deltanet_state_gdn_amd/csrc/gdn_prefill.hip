@@ -1,0 +1,390 @@
+// Chunked GDN prefill over packed variable-length sequences.
+//
+// Chunk form of the gated delta rule (the chunkwise WY/UT representation of
+// the Gated Delta Networks paper, restated here for this library's dk x dv
+// state; vLLM PR #52191 page, implementation items 3-4: the inter-chunk
+// recurrence runs its GEMMs in FP32 and scales chunk states by exp(g_last)).
+// Within a chunk of C = 64 tokens t = 0..C-1 (counted from the sequence start
+// of this call), with gamma_t = g_0 + ... + g_t and S the state entering the
+// chunk, every token's update unrolls to
+//     S_t = e^{gamma_t} S + sum_{s<=t} e^{gamma_t - gamma_s} k_s u_s^T
+// where the pseudo-values u solve the unit lower-triangular system
+//     (I + A) U = diag(beta) (V - diag(e^gamma) K S),
+//     A_ts = beta_t e^{gamma_t - gamma_s} k_t.k_s  for s < t.
+// Hence, with T = (I + A)^-1 and P_ts = e^{gamma_t - gamma_s} q_t.k_s (s <= t):
+//     U      = T diag(beta) (V - diag(e^gamma) K S)
+//     O      = scale (diag(e^gamma) Q S + P U)
+//     S_next = e^{gamma_C} S + (diag(e^{gamma_C - gamma}) K)^T U.
+// Only exp(gamma_t - gamma_s) with s <= t and exp(gamma_t) appear, so nothing
+// overflows however strong the decay.  A partial last chunk is padded with
+// k = q = v = 0, g = 0, beta = 0, which leaves every formula exact.
+//
+// Kernel 1 (chunk-parallel, one workgroup per (chunk, value head)): gates,
+// gamma, A and P by MFMA, T by blocked inversion (16x16 diagonal blocks by
+// substitution in registers, off-diagonal blocks by MFMA products), written to
+// the workspace.  Kernel 2 (sequential over chunks, one workgroup per
+// (sequence, value head, 32-column dv block); each dv column of S evolves on
+// its own given k, g and beta): the S-dependent products [K;Q] S, T R, P U and
+// K~^T U on fp32 MFMA with the state block resident in LDS, the state read
+// from its slot once and written back, rounded, once.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int kC = 64;                        // chunk length
+constexpr int kWsFloats = 2 * kC * kC + 2 * kC;  // T, P, gamma, beta per (chunk slot, head)
+
+// Chunk slot of chunk c of sequence n: n + floor(cu[n] / C) + c.  It is unique
+// and below N + ceil(total / C) (floor((x+l)/C) >= floor(x/C) + ceil(l/C) - 1).
+__host__ __device__ inline int64_t prefill_chunk_slots(int64_t N, int64_t total) {
+  return N + (total + kC - 1) / kC;
+}
+
+size_t prefill_workspace_bytes(int N, int64_t total, int Hv) {
+  return (size_t)prefill_chunk_slots(N, total) * (size_t)Hv * kWsFloats * sizeof(float);
+}
+
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hv) {
+  const int64_t units = ((int64_t)N * Hv + 7) / 8 * 8 * 4;
+  return prefill_chunk_slots(N, total) <= INT32_MAX && Hv <= 65535 && units <= INT32_MAX;
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// acc[16x16] += A[16 x K] B[K x 16] on v_mfma_f32_16x16x4_f32.  Operand
+// layout: lane l supplies A(l % 16, k0 + l / 16) and B(k0 + l / 16, l % 16);
+// result element r of lane l is C(4 (l / 16) + r, l % 16).
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4_t mma16(f32x4_t acc, const FA& A, const FB& B, int lane) {
+  const int i = lane & 15, kk = lane >> 4;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i, k0 + kk), B(k0 + kk, i), acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4) + r; }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
+
+// ---------------------------------------------------------------- kernel 1
+template <int D>
+__global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
+  constexpr int LDK = D + 4, LDT = kC + 4;
+  __shared__ float s_k[kC][LDK], s_q[kC][LDK];
+  __shared__ float s_A[kC][LDT], s_T[kC][LDT];
+  __shared__ float s_M[4][16][20];
+  __shared__ float s_g[kC], s_beta[kC], s_gam[kC];
+
+  const int cs = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int* cu = p.cu_seqlens;
+  // largest n with n + cu[n] / C <= cs (the key is strictly increasing in n)
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mid + cu[mid] / kC <= cs) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo;
+  const int c = cs - (n + cu[n] / kC);
+  const int seq_lo = cu[n], seq_hi = cu[n + 1];
+  if (c < 0 || (int64_t)c * kC >= (int64_t)(seq_hi - seq_lo)) return;  // unused chunk slot
+  const int slot = p.slot_map[n];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded sequence: kernel 2 writes zeros
+  const int t0 = seq_lo + c * kC;
+  const int len = min(kC, seq_hi - t0);
+  const int hk = h / (p.Hv / p.Hk);
+
+  for (int i = tid; i < kC * D; i += 256) {
+    const int t = i / D, d = i - t * D;
+    float kv = 0.f, qv = 0.f;
+    if (t < len) {
+      const int64_t off = ((int64_t)(t0 + t) * p.Hk + hk) * D + d;
+      kv = load_elem(p.k, off, p.in_dt);
+      qv = load_elem(p.q, off, p.in_dt);
+    }
+    s_k[t][d] = kv;
+    s_q[t][d] = qv;
+  }
+  if (tid < kC) {
+    float g = 0.f, be = 0.f;
+    if (tid < len) {
+      const int64_t gi = (int64_t)(t0 + tid) * p.Hv + h;
+      g = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
+      be = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+    }
+    s_g[tid] = g;
+    s_beta[tid] = be;
+  }
+  __syncthreads();
+  if (wave == 0) {  // inclusive prefix sum of g over the chunk
+    float x = s_g[lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    s_gam[lane] = x;
+  }
+  __syncthreads();
+
+  float* wsp = ws + ((int64_t)cs * p.Hv + h) * kWsFloats;
+  float* ws_T = wsp;
+  float* ws_P = wsp + kC * kC;
+  // A (strictly lower, to LDS) and P (causal, to the workspace): 2 x 16 tiles
+  for (int job = wave; job < 32; job += 4) {
+    const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (J <= I) {
+      if (isP)
+        acc = mma16<D>(acc, [&](int i, int k) { return s_q[16 * I + i][k]; },
+                       [&](int k, int j) { return s_k[16 * J + j][k]; }, lane);
+      else
+        acc = mma16<D>(acc, [&](int i, int k) { return s_k[16 * I + i][k]; },
+                       [&](int k, int j) { return s_k[16 * J + j][k]; }, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * I + acc_row(lane, r), s = 16 * J + acc_col(lane);
+      if (isP) {
+        ws_P[t * kC + s] = (s <= t) ? expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
+      } else {
+        s_A[t][s] = (s < t) ? s_beta[t] * expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, lane = (block, column)
+  if (wave == 0) {
+    const int blk = lane >> 4, j = lane & 15, base = 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+#pragma unroll
+      for (int s = 0; s < i; ++s) x[i] = fmaf(-s_A[base + i][base + s], x[s], x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_T[base + i][base + j] = x[i];
+  }
+  for (int i = tid; i < kC * kC; i += 256) {  // blocks above the diagonal are zero
+    const int r = i / kC, cc = i - r * kC;
+    if ((cc >> 4) > (r >> 4)) s_T[r][cc] = 0.f;
+  }
+  __syncthreads();
+  // off-diagonal blocks, one level (I - J = lev) at a time:
+  //   T_IJ = -T_II (sum_{k=J}^{I-1} A_Ik T_kJ)
+  for (int lev = 1; lev < 4; ++lev) {
+    const int J = wave, I = wave + lev;
+    const bool act = I < 4;
+    if (act) {
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < 16 * lev; k0 += 16) {
+        m = mma16<16>(m, [&](int i, int k) { return s_A[16 * I + i][16 * J + k0 + k]; },
+                      [&](int k, int jj) { return s_T[16 * J + k0 + k][16 * J + jj]; }, lane);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_M[wave][acc_row(lane, r)][acc_col(lane)] = m[r];
+    }
+    __syncthreads();
+    if (act) {
+      f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+      t = mma16<16>(t, [&](int i, int k) { return s_T[16 * I + i][16 * I + k]; },
+                    [&](int k, int jj) { return s_M[wave][k][jj]; }, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_T[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = -t[r];
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < kC * kC; i += 256) ws_T[i] = s_T[i / kC][i % kC];
+  if (tid < kC) {
+    wsp[2 * kC * kC + tid] = s_gam[tid];
+    wsp[2 * kC * kC + kC + tid] = s_beta[tid];
+  }
+}
+
+// ---------------------------------------------------------------- kernel 2
+template <int D>
+struct PrefillGeom {
+  static constexpr int BV = D < 32 ? D : 32;  // dv columns per workgroup
+  static constexpr int NB = D / BV;
+  static constexpr int NJ = BV / 16;
+};
+
+template <int SDT, int D>
+__global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArgs p, const float* __restrict__ ws) {
+  using G = PrefillGeom<D>;
+  constexpr int BV = G::BV, NB = G::NB, NJ = G::NJ;
+  constexpr int LDK = D + 4, LDV = BV + 4, LDT = kC + 4;
+  constexpr int QRU = (kC * LDK > 2 * kC * LDV) ? kC * LDK : 2 * kC * LDV;
+  __shared__ float s_k[kC][LDK];
+  __shared__ float s_qru[QRU];  // Q [C][LDK], then R [C][LDV] and U [C][LDV]
+  __shared__ float s_v[kC][LDV];
+  __shared__ float s_T[kC][LDT], s_P[kC][LDT];
+  __shared__ float s_S[D][LDV];
+  __shared__ float s_X[2 * kC][LDV];  // K S (rows 0..C-1), Q S (rows C..2C-1)
+  __shared__ float s_beta[kC], s_eg[kC], s_dec[kC], s_egC;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
+  const int bid = blockIdx.x;
+  const int x8 = bid & 7, y = bid >> 3;
+  const int blk = y % NB;
+  const int unit = (y / NB) * 8 + x8;
+  if (unit >= p.N * p.Hv) return;
+  const int n = unit / p.Hv, h = unit - n * p.Hv;
+  const int hk = h / (p.Hv / p.Hk);
+  const int seq_lo = p.cu_seqlens[n], seq_hi = p.cu_seqlens[n + 1];
+  const int len = seq_hi - seq_lo;
+  if (len <= 0) return;
+  const int col0 = blk * BV;
+  const int slot = p.slot_map[n];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) {  // padded sequence: zero outputs
+    for (int i = tid; i < len * BV; i += 256) {
+      const int t = i / BV, j = i - t * BV;
+      store_elem(p.out, ((int64_t)(seq_lo + t) * p.Hv + h) * D + col0 + j, 0.f, p.out_dt);
+    }
+    return;
+  }
+  using ST = typename StateElem<SDT>::T;
+  ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot * p.Hv + h) * (int64_t)(D * D);
+  for (int i = tid; i < D * BV; i += 256) {
+    const int r = i / BV, j = i - r * BV;
+    s_S[r][j] = load_elem(tile, (int64_t)r * D + col0 + j, SDT);
+  }
+
+  float* s_q = s_qru;
+  float* s_R = s_qru;
+  float* s_U = s_qru + kC * LDV;
+  const int nch = (len + kC - 1) / kC;
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = seq_lo + c * kC;
+    const int L = min(kC, seq_hi - t0);
+    const float* wsp = ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats;
+    for (int i = tid; i < kC * D; i += 256) {
+      const int t = i / D, d = i - t * D;
+      float kv = 0.f, qv = 0.f;
+      if (t < L) {
+        const int64_t off = ((int64_t)(t0 + t) * p.Hk + hk) * D + d;
+        kv = load_elem(p.k, off, p.in_dt);
+        qv = load_elem(p.q, off, p.in_dt);
+      }
+      s_k[t][d] = kv;
+      s_q[t * LDK + d] = qv;
+    }
+    for (int i = tid; i < kC * BV; i += 256) {
+      const int t = i / BV, j = i - t * BV;
+      s_v[t][j] = (t < L) ? load_elem(p.v, ((int64_t)(t0 + t) * p.Hv + h) * D + col0 + j, p.in_dt) : 0.f;
+    }
+    for (int i = tid; i < kC * kC; i += 256) {
+      s_T[i / kC][i % kC] = wsp[i];
+      s_P[i / kC][i % kC] = wsp[kC * kC + i];
+    }
+    if (tid < kC) {
+      const float gt = wsp[2 * kC * kC + tid];
+      const float gC = wsp[2 * kC * kC + kC - 1];
+      s_beta[tid] = wsp[2 * kC * kC + kC + tid];
+      s_eg[tid] = expf(gt);
+      s_dec[tid] = expf(gC - gt);
+      if (tid == 0) s_egC = expf(gC);
+    }
+    __syncthreads();
+
+    // X = [K; Q] S
+    for (int job = wave; job < 8 * NJ; job += 4) {
+      const int I = job / NJ, J = job - I * NJ;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if (I < 4)
+        acc = mma16<D>(acc, [&](int i, int k) { return s_k[16 * I + i][k]; },
+                       [&](int k, int j) { return s_S[k][16 * J + j]; }, lane);
+      else
+        acc = mma16<D>(acc, [&](int i, int k) { return s_q[(16 * (I - 4) + i) * LDK + k]; },
+                       [&](int k, int j) { return s_S[k][16 * J + j]; }, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_X[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = acc[r];
+    }
+    __syncthreads();
+    // R = diag(beta) (V - diag(e^gamma) K S)   (overwrites Q)
+    for (int i = tid; i < kC * BV; i += 256) {
+      const int t = i / BV, j = i - t * BV;
+      s_R[t * LDV + j] = s_beta[t] * (s_v[t][j] - s_eg[t] * s_X[t][j]);
+    }
+    __syncthreads();
+    // U = T R
+    for (int job = wave; job < 4 * NJ; job += 4) {
+      const int I = job / NJ, J = job - I * NJ;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mma16<kC>(acc, [&](int i, int k) { return s_T[16 * I + i][k]; },
+                      [&](int k, int j) { return s_R[k * LDV + 16 * J + j]; }, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_U[(16 * I + acc_row(lane, r)) * LDV + 16 * J + acc_col(lane)] = acc[r];
+    }
+    __syncthreads();
+    // O = scale (diag(e^gamma) Q S + P U)  and  S <- e^{gamma_C} S + (diag(dec) K)^T U
+    const float egC = s_egC;
+    for (int job = wave; job < (4 + D / 16) * NJ; job += 4) {
+      const int I = job / NJ, J = job - I * NJ;
+      f32x4_t acc;
+      if (I < 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * I + acc_row(lane, r);
+          acc[r] = s_eg[t] * s_X[kC + t][16 * J + acc_col(lane)];
+        }
+        acc = mma16<kC>(acc, [&](int i, int k) { return s_P[16 * I + i][k]; },
+                        [&](int k, int j) { return s_U[k * LDV + 16 * J + j]; }, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * I + acc_row(lane, r);
+          if (t < L)
+            store_elem(p.out, ((int64_t)(t0 + t) * p.Hv + h) * D + col0 + 16 * J + acc_col(lane), p.scale * acc[r],
+                       p.out_dt);
+        }
+      } else {
+        const int Is = I - 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = egC * s_S[16 * Is + acc_row(lane, r)][16 * J + acc_col(lane)];
+        acc = mma16<kC>(acc, [&](int i, int k) { return s_k[k][16 * Is + i] * s_dec[k]; },
+                        [&](int k, int j) { return s_U[k * LDV + 16 * J + j]; }, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_S[16 * Is + acc_row(lane, r)][16 * J + acc_col(lane)] = acc[r];
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < D * BV; i += 256) {
+    const int r = i / BV, j = i - r * BV;
+    store_elem(tile, (int64_t)r * D + col0 + j, s_S[r][j], SDT);
+  }
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
+  const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens);
+  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D>), dim3((unsigned)ncs, (unsigned)a.Hv), dim3(256), 0, s, a, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)a.N * a.Hv;
+  const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
+  switch (state_dt) {
+    case GDN_F32: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
+    case GDN_BF16: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
+    case GDN_F16: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s) {
+  if (chunk != kC) return hipErrorInvalidValue;
+  switch (D) {
+    case 16: return launch_prefill_d<16>(a, state_dt, ws, s);
+    case 32: return launch_prefill_d<32>(a, state_dt, ws, s);
+    case 64: return launch_prefill_d<64>(a, state_dt, ws, s);
+    case 128: return launch_prefill_d<128>(a, state_dt, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

@@ -1,0 +1,200 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet (GDN) recurrent-state update library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated
+ * Delta Networks", 2024) as run by hybrid-model decode and prefill.  With a
+ * per-(sequence, value head) state S of dk x dv and, per token, a key k and
+ * query q (dk), a value v (dv), a log-decay g and a write strength beta:
+ *
+ *     S <- exp(g) S                                  (decay)
+ *     S <- S + beta k (v - S^T k)^T                  (delta-rule correction)
+ *     o  = scale * S^T q                             (read-out, scale = dk^-1/2)
+ *
+ * with the fused sigmoid gating g = -exp(A_log[h]) * softplus(a + dt_bias[h])
+ * and beta = sigmoid(b).  Sources: vLLM PR #52191 summary page (prhub.com.cn),
+ * implementation section items 3-4 (decode, chunked and spec kernels templated
+ * on the state type; FP32 math with the state read and written in its storage
+ * type, one rounding per write-back; chunk states scaled by exp(g_last)); AREX
+ * feed article on ReplaySSM, "bottleneck" and "cache inputs, not state"
+ * sections (full-state read and write per decode step; checkpoint plus ring
+ * of inputs folded every L steps; q never cached).
+ *
+ * Conventions for every entry point
+ *   - All math is FP32.  The state is stored as f32, bf16 or f16 and rounded
+ *     to nearest-even once per write-back.
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *     struct arguments themselves live in host memory and are read during
+ *     the call only.  The caller allocates and owns every buffer; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Calls only validate and enqueue work on `stream` (a hipStream_t; NULL
+ *     is the default stream).  They return before the work runs.
+ *   - Tensors are dense and row-major with the last dimension fastest.
+ *     Inputs q, k, v, a, b share one dtype `in_dtype`.
+ *   - State pools are [num_slots, Hv, dk, dv] (dv fastest), 16-byte aligned.
+ *     Value head h reads key head h / (Hv / Hk) (contiguous groups).
+ *   - A slot index outside [0, num_slots) marks a padded row: its outputs
+ *     are written as zero and no state or ring entry is touched.
+ *   - Slots named by one call must be distinct (not checked).
+ *   - Errors: invalid arguments are rejected synchronously, before anything
+ *     is enqueued, with GDN_EINVAL or GDN_EUNSUPPORTED; a failed launch gives
+ *     GDN_ELAUNCH.  gdn_last_error() describes the last failure of the
+ *     calling thread.  There is no silent fallback and no logging.
+ *   - Supported head dims: dk == dv in {16, 32, 64, 128}; Hv % Hk == 0.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = 1,       /* null pointer, bad size, misaligned buffer, bad dtype value */
+  GDN_EUNSUPPORTED = 2, /* valid request outside the compiled set (head dim, chunk, ring length) */
+  GDN_ELAUNCH = 3       /* the HIP runtime refused a kernel launch */
+} gdn_status;
+
+/* Layer shape.  scale <= 0 selects dk^-1/2. */
+typedef struct {
+  int32_t num_k_heads; /* Hk */
+  int32_t num_v_heads; /* Hv, a multiple of Hk */
+  int32_t dk;
+  int32_t dv;
+  float scale;
+} gdn_dims;
+
+/* Gate inputs.  a, b: [rows, Hv] in the call's in_dtype (rows = tokens of the
+ * call); A_log, dt_bias: float32 [Hv]. */
+typedef struct {
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+} gdn_gates;
+
+/* State pool [num_slots, Hv, dk, dv] of `dtype`, 16-byte aligned. */
+typedef struct {
+  void* base;
+  gdn_dtype dtype;
+  int64_t num_slots;
+} gdn_pool;
+
+/* ReplaySSM ring, one per (slot, value head), caller-allocated and separate
+ * from the checkpoint pool:
+ *   k    [num_slots, Hv, L, dk]  copies of the keys, in `dtype`
+ *   v    [num_slots, Hv, L, dv]  copies of the values, in `dtype`
+ *   g    [num_slots, Hv, L]      float32 log-decays
+ *   beta [num_slots, Hv, L]      float32 write strengths
+ *   start, count [num_slots, Hv] int32; live entry i (0 <= i < count) sits at
+ *                                ring index (start + i) mod L.
+ * q is never stored.  Before first use, start and count must be zero (or any
+ * 0 <= start < L, 0 <= count <= L).  k and v are stored per value head so
+ * that each (slot, value head) unit owns its ring entries outright. */
+typedef struct {
+  void* k;
+  void* v;
+  float* g;
+  float* beta;
+  int32_t* start;
+  int32_t* count;
+  int64_t num_slots; /* slots the ring arrays hold; equals the checkpoint pool's */
+  int32_t L;         /* 1 <= L <= 64 */
+  gdn_dtype dtype;   /* dtype of k and v entries; must equal the calls' in_dtype */
+} gdn_ring;
+
+/* Single-token decode for B sequences (vLLM PR #52191 page, implementation
+ * item 3: the fused sigmoid-gating delta-rule update; AREX ReplaySSM article,
+ * "bottleneck" section: the whole state is read and written every step).
+ *   q, k     [B, Hk, dk] in_dtype
+ *   v        [B, Hv, dv] in_dtype
+ *   gates    a, b [B, Hv]
+ *   state    pool; slot_map[b] (device int32 [B]) selects the slot of row b
+ *   out      [B, Hv, dv] out_dtype; o is read from the updated state before
+ *            its write-back rounding.
+ * Each touched (slot, head) state is read once and written once, rounded. */
+gdn_status gdn_decode_step(const gdn_dims* dims, int32_t B, const void* q, const void* k,
+                           const void* v, gdn_dtype in_dtype, const gdn_gates* gates,
+                           const gdn_pool* state, const int32_t* slot_map, void* out,
+                           gdn_dtype out_dtype, void* stream);
+
+/* Chunked prefill of N packed variable-length sequences (vLLM PR #52191 page,
+ * implementation items 3-4: the chunked inter-chunk recurrence; chunk states
+ * are scaled by exp(g_last); FP32 buffers, slot read at the start and written
+ * at the end).
+ *   cu_seqlens  device int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[N] = total_tokens
+ *   q, k        [total_tokens, Hk, dk] in_dtype
+ *   v           [total_tokens, Hv, dv] in_dtype
+ *   gates       a, b [total_tokens, Hv]
+ *   state       sequence n starts from slot slot_map[n] and its final state is
+ *               written back there, rounded once per call; a zero-length
+ *               sequence leaves its slot untouched.  The state is carried
+ *               exactly across calls: two calls over a split sequence equal
+ *               one call up to that one extra rounding.
+ *   out         [total_tokens, Hv, dv] out_dtype
+ *   chunk       tokens per chunk, counted from each sequence's start in this
+ *               call: 64 (the only compiled size).
+ *   workspace   device scratch of at least gdn_chunk_prefill_workspace_bytes()
+ *               bytes, 256-byte aligned, owned by the caller, not read before
+ *               it is written; NULL is allowed when that size is 0.
+ * A sequence longer than 2^31 - 1 tokens is rejected. */
+size_t gdn_chunk_prefill_workspace_bytes(const gdn_dims* dims, int32_t N, int64_t total_tokens,
+                                         int32_t chunk);
+gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_seqlens,
+                             int64_t total_tokens, int32_t chunk, const void* q, const void* k,
+                             const void* v, gdn_dtype in_dtype, const gdn_gates* gates,
+                             const gdn_pool* state, const int32_t* slot_map, void* out,
+                             gdn_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* ReplaySSM-style decode of a window of T tokens per sequence (AREX ReplaySSM
+ * article, "cache inputs, not state": checkpoint S0 plus a ring of the last
+ * inputs, folded into S0 every L steps; other steps read outputs from S0 and
+ * the ring without writing the state; a verify window is evaluated in one
+ * pass and rejected drafts are dropped by moving the ring pointer).
+ *   q, k   [B, T, Hk, dk] in_dtype;  v [B, T, Hv, dv];  gates a, b [B, T, Hv]
+ *   ckpt   checkpoint pool; slot_map[b] selects the slot of row b
+ *   ring   the ring; T must satisfy 1 <= T <= ring->L
+ *   out    [B, T, Hv, dv] out_dtype
+ * Per (sequence, value head): if count + T > L, every committed entry is
+ * first folded into the checkpoint (one rounding) and the ring emptied
+ * (start += count mod L, count = 0); then the T new entries are appended at
+ * ring indices (start + count + t) mod L and count += T; window position t
+ * outputs scale * S_t^T q_t where S_t is the checkpoint advanced over the
+ * first count_before + t + 1 live entries (computed without writing it). */
+gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q,
+                             const void* k, const void* v, gdn_dtype in_dtype,
+                             const gdn_gates* gates, const gdn_pool* ckpt,
+                             const int32_t* slot_map, const gdn_ring* ring, void* out,
+                             gdn_dtype out_dtype, void* stream);
+
+/* Fold every committed ring entry of the mapped slots into their checkpoints
+ * (one rounding each) and empty their rings.  After it, the checkpoint is the
+ * plain decode state and the other entry points may use the slot. */
+gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt,
+                            const int32_t* slot_map, const gdn_ring* ring, void* stream);
+
+/* Drop the last num_rejected[b] live entries of row b's slot, for every value
+ * head: count <- max(count - r, 0) (the pointer move that replaces a state
+ * rollback).  num_rejected: device int32 [B], each >= 0. */
+gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* slot_map,
+                               const int32_t* num_rejected, const gdn_ring* ring, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* Description of the last failure reported to the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

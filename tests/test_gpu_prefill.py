@@ -1,0 +1,155 @@
+"""GPU parity of gdn_chunk_prefill (chunked form, MFMA) against the CPU oracle's
+token-by-token recurrence: ragged lengths around the chunk size, every head
+dim, fp32 / bf16 / fp16 states, the two-call split, padded sequences, and the
+full-size 4-sequence workload on sampled (sequence, head) pairs.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import gen
+
+from gpu_util import DEV, assert_close, dev, host, poisoned_pool, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_prefill(cid, lengths, Hk, Hv, D, sdt, in_dt="bf16", num_slots=None, slot_map=None, a_shift=0.0,
+                sample=None, pool=None, states=None, step=0, check=True):
+    """One prefill call on the GPU and on the oracle (optionally only sampled (seq, head) pairs)."""
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    N = len(lengths)
+    num_slots = num_slots or N + 3
+    if slot_map is None:
+        slot_map = gen.slot_permutation(cid, num_slots)[:N]
+    slot_map = np.asarray(slot_map, np.int32)
+    valid = [int(s) for s in slot_map if 0 <= s < num_slots]
+    if pool is None:
+        pool, st = poisoned_pool(num_slots, Hv, D, D, sdt, valid, cid)
+        states = {s: st[i] for i, s in enumerate(valid)}
+    cu = gen.seq_lengths_cu(lengths)
+    inp = gen.token_inputs(cid, step, (int(cu[-1]),), Hk, Hv, D, D, in_dt, a_shift)
+    A_log, dt_bias = gen.head_params(cid, Hv)
+    say(f"prefill cid={cid} lengths={list(lengths)[:8]} Hk={Hk} Hv={Hv} D={D} state={sdt} in={in_dt}")
+    out = gdn.gdn_chunk_prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]),
+                                dev(A_log), dev(dt_bias), pool, torch.from_numpy(slot_map).to(DEV),
+                                torch.from_numpy(cu).to(DEV))
+    torch.cuda.synchronize()
+    o = host(out)
+    assert np.all(np.isfinite(o)), "non-finite output"
+    if not check:
+        return pool, states, o, inp
+    # oracle over a mini pool: local slot i holds sequence i's state
+    order = [n for n in range(N) if 0 <= slot_map[n] < num_slots]
+    mini = np.stack([states[int(slot_map[n])] for n in order]) if order else None
+    mini_map = np.full(N, -1, np.int32)
+    for i, n in enumerate(order):
+        mini_map[n] = i
+    heads = None if sample is None else sorted({h for _, h in sample})
+    seqs = None if sample is None else sorted({n for n, _ in sample})
+    if mini is None:
+        mini = np.zeros((1, Hv, D, D), np.float32)
+    ref_pool, o_ref = O.chunk_prefill(mini, mini_map, cu, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], A_log,
+                                      dt_bias, heads=heads, seqs=seqs)
+    got_pool = host(pool)
+    pairs = sample if sample is not None else [(n, h) for n in range(N) for h in range(Hv)]
+    for n, h in pairs:
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        assert_close(o[sl, h], o_ref[sl, h], "f32", f"o seq {n} head {h}")
+        if mini_map[n] >= 0 and cu[n + 1] > cu[n]:
+            assert_close(got_pool[slot_map[n], h], ref_pool[mini_map[n], h], sdt, f"state seq {n} head {h}")
+            states[int(slot_map[n])] = np.array(states[int(slot_map[n])], copy=True)
+            states[int(slot_map[n])][h] = ref_pool[mini_map[n], h]
+    return pool, states, o, inp
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
+def test_prefill_ragged_lengths(sdt):
+    """Lengths 1, 63, 64, 65, 0 and 130: partial chunks, exact chunks, an empty sequence."""
+    run_prefill(70, [1, 63, 64, 65, 0, 130], 2, 4, 32, sdt, a_shift=-1.0)
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_prefill_head_dims(D):
+    run_prefill(71 + D, [100, 37, 192], 1, 2, D, "f32")
+
+
+def test_prefill_fp32_inputs_slow_decay():
+    """fp32 inputs and slow decay (a - 6): the state carries across many chunks."""
+    run_prefill(72, [700, 129], 2, 2, 64, "f32", in_dt="f32", a_shift=-6.0)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_prefill_two_call_split_equals_one_call(sdt):
+    """First 55% of each sequence, then the rest, equals one call: the state is carried exactly
+    (one extra rounding at the split for a bf16 state)."""
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    lengths = [300, 129, 64]
+    first, second = gen.split_lengths(lengths)
+    Hk, Hv, D, cid = 2, 4, 64, 73
+    N = len(lengths)
+    slot_map = gen.slot_permutation(cid, 6)[:N]
+    pool1, st = poisoned_pool(6, Hv, D, D, sdt, [int(s) for s in slot_map], cid)
+    pool2 = pool1.clone()
+    cu = gen.seq_lengths_cu(lengths)
+    inp = gen.token_inputs(cid, 0, (int(cu[-1]),), Hk, Hv, D, D, "bf16", -3.0)
+    A_log, dt_bias = gen.head_params(cid, Hv)
+    args = (dev(A_log), dev(dt_bias))
+    sm = torch.from_numpy(slot_map).to(DEV)
+    say("prefill two-call split: one call")
+    o_one = gdn.gdn_chunk_prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]), *args,
+                                  pool1, sm, torch.from_numpy(cu).to(DEV))
+    o_two = torch.empty_like(o_one)
+    off = [0] * N
+    for part in (first, second):
+        idx = np.concatenate([np.arange(cu[n] + off[n], cu[n] + off[n] + part[n]) for n in range(N)])
+        sub = {k: v[idx] for k, v in inp.items()}
+        say(f"prefill two-call split: part {part}")
+        o_p = gdn.gdn_chunk_prefill(dev(sub["q"]), dev(sub["k"]), dev(sub["v"]), dev(sub["a"]), dev(sub["b"]),
+                                    *args, pool2, sm, torch.from_numpy(gen.seq_lengths_cu(part)).to(DEV))
+        o_two[torch.from_numpy(idx).to(DEV)] = o_p
+        off = [o_ + p for o_, p in zip(off, part)]
+    torch.cuda.synchronize()
+    assert_close(host(o_two), host(o_one), "f32" if sdt == "f32" else "bf16", "outputs")
+    assert_close(host(pool2)[slot_map], host(pool1)[slot_map], sdt, "final states")
+    # and the split path against the oracle's two calls
+    mini = np.stack([st[i] for i in range(N)])
+    ref = mini
+    ref_o = np.zeros((int(cu[-1]), Hv, D))
+    off = [0] * N
+    for part in (first, second):
+        idx = np.concatenate([np.arange(cu[n] + off[n], cu[n] + off[n] + part[n]) for n in range(N)])
+        sub = {k: v[idx] for k, v in inp.items()}
+        ref, o_p = O.chunk_prefill(ref, np.arange(N), gen.seq_lengths_cu(part), sub["q"], sub["k"], sub["v"],
+                                   sub["a"], sub["b"], A_log, dt_bias)
+        ref_o[idx] = o_p
+        off = [o_ + p for o_, p in zip(off, part)]
+    assert_close(host(o_two), ref_o, "f32" if sdt == "f32" else "bf16", "split outputs vs oracle")
+    assert_close(host(pool2)[slot_map], ref, sdt, "split states vs oracle")
+
+
+def test_prefill_padded_sequence():
+    """slot -1: zero outputs, nothing written; the other sequences are unaffected."""
+    import torch
+    slot_map = np.int32([2, -1, 0])
+    pool, states, o, inp = run_prefill(74, [70, 50, 10], 1, 2, 16, "f32", num_slots=4, slot_map=slot_map)
+    assert np.all(o[70:120] == 0)
+    del torch, states, inp
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_prefill_workload_sampled(sdt):
+    """Full-size workload: 4 packed sequences of 1024, 3000, 8192, 8192 tokens, 16 key / 32 value
+    heads, 128 x 128 states read from slots; sampled (sequence, head) pairs against the oracle."""
+    cfg = gen.CONFIGS[3]
+    s = cfg.shape
+    lengths = cfg.extra["lengths"]
+    sample = [(0, 0), (1, 31), (2, 17), (3, 6)]
+    run_prefill(3, lengths, s.Hk, s.Hv, s.dk, sdt, num_slots=cfg.num_slots, sample=sample)

@@ -1,0 +1,179 @@
+"""GPU parity of the ReplaySSM-style entry points (gdn_replay_decode, gdn_replay_flush,
+gdn_replay_rollback) against the CPU oracle.
+
+Ring pointers (start, count) and the live k / v entries must match bit for
+bit; stored gates within FP32 transcendental error; outputs and checkpoints
+within the state-dtype tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import gen
+
+from gpu_util import DEV, assert_close, dev, host, poisoned_pool, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class ReplayCase:
+    def __init__(self, cid, B, Hk, Hv, D, L, sdt, num_slots, sample=None, in_dt="bf16"):
+        import torch
+        import gated_deltanet_state_gdn_amd as gdn
+        self.cid, self.B, self.Hk, self.Hv, self.D, self.L, self.sdt = cid, B, Hk, Hv, D, L, sdt
+        self.num_slots, self.in_dt = num_slots, in_dt
+        self.slot_map = gen.slot_permutation(cid, num_slots)[:B]
+        self.ckpt_d, states = poisoned_pool(num_slots, Hv, D, D, sdt, [int(s) for s in self.slot_map], cid)
+        self.ring_d = gdn.new_ring(num_slots, Hv, L, D, D, {"bf16": torch.bfloat16, "f32": torch.float32}[in_dt], DEV)
+        self.rows = list(range(B)) if sample is None else list(sample)
+        # oracle: mini pool / ring over the sampled rows' slots, local slot i = sample row i
+        self.ref_ckpt = states[self.rows]
+        self.ref_ring = O.new_ring(len(self.rows), Hv, L, D, D, in_dt)
+        self.ref_map = np.arange(len(self.rows), dtype=np.int32)
+        self.A_log, self.dt_bias = gen.head_params(cid, Hv)
+        self.A_d, self.dt_d = dev(self.A_log), dev(self.dt_bias)
+        self.slot_d = torch.from_numpy(self.slot_map).to(DEV)
+
+    def step(self, step, T, a_shift=0.0):
+        import torch
+        import gated_deltanet_state_gdn_amd as gdn
+        inp = gen.token_inputs(self.cid, step, (self.B, T), self.Hk, self.Hv, self.D, self.D, self.in_dt, a_shift)
+        say(f"replay cid={self.cid} B={self.B} D={self.D} L={self.L} T={T} ckpt={self.sdt} step={step}")
+        out = gdn.gdn_replay_decode(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]),
+                                    self.A_d, self.dt_d, self.ckpt_d, self.slot_d, self.ring_d)
+        torch.cuda.synchronize()
+        sub = {k: v[self.rows] for k, v in inp.items()}
+        self.ref_ckpt, self.ref_ring, o_ref = O.replay_decode(self.ref_ckpt, self.ref_ring, self.ref_map, sub["q"],
+                                                              sub["k"], sub["v"], sub["a"], sub["b"], self.A_log,
+                                                              self.dt_bias)
+        o = host(out)
+        assert np.all(np.isfinite(o)), "non-finite output"
+        assert_close(o[self.rows], o_ref, "f32" if self.sdt == "f32" else "bf16", f"o step {step}")
+        return inp
+
+    def rollback(self, step, r):
+        import torch
+        import gated_deltanet_state_gdn_amd as gdn
+        say(f"replay rollback cid={self.cid} step={step}")
+        gdn.gdn_replay_rollback(self.slot_d, torch.from_numpy(r).to(DEV), self.ring_d, self.Hk, self.D)
+        torch.cuda.synchronize()
+        self.ref_ring = O.replay_rollback(self.ref_ring, self.ref_map, r[self.rows])
+
+    def flush(self):
+        import torch
+        import gated_deltanet_state_gdn_amd as gdn
+        say(f"replay flush cid={self.cid}")
+        gdn.gdn_replay_flush(self.ckpt_d, self.slot_d, self.ring_d, self.Hk)
+        torch.cuda.synchronize()
+        self.ref_ckpt, self.ref_ring = O.replay_flush(self.ref_ckpt, self.ref_ring, self.ref_map)
+
+    def check_state(self, what):
+        import torch
+        slots = torch.as_tensor(self.slot_map[self.rows].astype(np.int64), device=DEV)
+        ck = host(self.ckpt_d[slots])
+        assert_close(ck, self.ref_ckpt, self.sdt, f"{what}: checkpoint")
+        st, cnt = host(self.ring_d.start[slots]), host(self.ring_d.count[slots])
+        assert np.array_equal(st, self.ref_ring.start), f"{what}: ring start"
+        assert np.array_equal(cnt, self.ref_ring.count), f"{what}: ring count"
+        rk, rv = host(self.ring_d.k[slots]), host(self.ring_d.v[slots])
+        rg, rb = host(self.ring_d.g[slots]), host(self.ring_d.beta[slots])
+        L = self.L
+        for i in range(len(self.rows)):
+            for h in range(self.Hv):
+                live = [(int(st[i, h]) + e) % L for e in range(int(cnt[i, h]))]
+                if not live:
+                    continue
+                assert np.array_equal(rk[i, h, live], self.ref_ring.k[i, h, live]), f"{what}: ring k"
+                assert np.array_equal(rv[i, h, live], self.ref_ring.v[i, h, live]), f"{what}: ring v"
+                np.testing.assert_allclose(rg[i, h, live], self.ref_ring.g[i, h, live], rtol=1e-5, atol=1e-8)
+                np.testing.assert_allclose(rb[i, h, live], self.ref_ring.beta[i, h, live], rtol=1e-5, atol=1e-8)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 128])
+def test_replay_standard_decode_with_folds(sdt, D):
+    """T = 1, L = 4, 11 steps (folds at steps 5 and 9), every row checked, then a flush."""
+    c = ReplayCase(30 + D, 5, 1, 2, D, 4, sdt, 8)
+    for step in range(11):
+        c.step(step, 1, a_shift=-2.0)
+        c.check_state(f"step {step}")
+    c.flush()
+    c.check_state("flush")
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_replay_spec_windows_with_rollback(sdt):
+    """T = 3 windows on L = 8 with seeded rejections; then a flush."""
+    c = ReplayCase(40, 6, 2, 4, 32, 8, sdt, 10)
+    for step in range(7):
+        c.step(step, 3, a_shift=-2.0)
+        c.check_state(f"step {step}")
+        c.rollback(step, gen.rejected_counts(40, step, c.B, 2))
+        c.check_state(f"rollback {step}")
+    c.flush()
+    c.check_state("flush")
+
+
+def test_replay_L1_matches_decode_on_gpu():
+    """L = 1 folds every step: outputs and checkpoint equal the decode kernel's."""
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    c = ReplayCase(50, 4, 1, 2, 64, 1, "bf16", 6)
+    pool_d = c.ckpt_d.clone()
+    for step in range(5):
+        inp = c.step(step, 1, a_shift=-2.0)
+        o_dec = gdn.gdn_decode_step(dev(inp["q"][:, 0]), dev(inp["k"][:, 0]), dev(inp["v"][:, 0]),
+                                    dev(inp["a"][:, 0]), dev(inp["b"][:, 0]), c.A_d, c.dt_d, pool_d, c.slot_d)
+        torch.cuda.synchronize()
+    c.flush()
+    sl = c.slot_map.astype(np.int64)
+    assert_close(host(c.ckpt_d)[sl], host(pool_d)[sl], "bf16", "checkpoint vs decode pool")
+    del o_dec
+
+
+def test_replay_layer_f32_sampled_over_a_fold():
+    """Full-size layer: B = 512, 128 x 128 fp32 checkpoints, L = 16, 20 steps (fold at 17)."""
+    cfg = gen.CONFIGS[4]
+    s = cfg.shape
+    c = ReplayCase(4, s.B, s.Hk, s.Hv, s.dk, cfg.extra["L"], "f32", cfg.num_slots, sample=[0, 211, 511])
+    for step in range(20):
+        c.step(step, 1)
+        if step in (0, 15, 16, 19):
+            c.check_state(f"step {step}")
+
+
+def test_replay_layer_bf16_spec_sampled():
+    """Full-size layer, bf16 checkpoints, verify windows of T = 5 with rollback of 0..4 tokens."""
+    cfg = gen.CONFIGS[4]
+    s = cfg.shape
+    c = ReplayCase(41, s.B, s.Hk, s.Hv, s.dk, cfg.extra["L"], "bf16", cfg.num_slots, sample=[3, 300])
+    T = cfg.extra["T_spec"]
+    for step in range(8):
+        c.step(step, T)
+        c.rollback(step, gen.rejected_counts(41, step, s.B, T - 1))
+    c.check_state("after spec steps")
+    c.flush()
+    c.check_state("flush")
+
+
+def test_replay_padded_rows():
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    c = ReplayCase(60, 3, 1, 2, 16, 4, "f32", 4)
+    c.slot_d = torch.tensor([-1, int(c.slot_map[1]), 4], dtype=torch.int32, device=DEV)
+    before = host(c.ckpt_d)
+    inp = gen.token_inputs(60, 0, (3, 2), 1, 2, 16, 16, "bf16")
+    out = gdn.gdn_replay_decode(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]), c.A_d,
+                                c.dt_d, c.ckpt_d, c.slot_d, c.ring_d)
+    torch.cuda.synchronize()
+    o = host(out)
+    assert np.all(o[0] == 0) and np.all(o[2] == 0) and np.any(o[1] != 0)
+    cnt = host(c.ring_d.count)
+    assert cnt[int(c.slot_map[1])].tolist() == [2, 2]
+    assert cnt.sum() == 4
+    assert np.array_equal(host(c.ckpt_d).view(np.uint32), before.view(np.uint32))  # no fold, nothing written
