@@ -37,24 +37,26 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), lib_path: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link ``lib_path``; ``defines`` are extra -D tuning macros."""
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
+    dflags = [f"-D{d}" for d in defines]
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

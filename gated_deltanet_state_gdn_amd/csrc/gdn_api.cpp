@@ -87,8 +87,7 @@ gdn_status check_io(const void* q, const void* k, const void* v, int in_dt, cons
   GDN_TRY(check_dtypes(in_dt, out_dt));
   GDN_REQUIRE(q && k && v, GDN_EINVAL, "q, k or v is NULL");
   GDN_REQUIRE(out != nullptr, GDN_EINVAL, "out is NULL");
-  const size_t eb = dtype_bytes(in_dt);
-  GDN_REQUIRE(aligned(q, eb) && aligned(k, eb) && aligned(v, eb), GDN_EINVAL, "q, k or v misaligned for in_dtype");
+  GDN_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16), GDN_EINVAL, "q, k or v is not 16-byte aligned");
   GDN_REQUIRE(aligned(out, dtype_bytes(out_dt)), GDN_EINVAL, "out misaligned for out_dtype");
   return GDN_OK;
 }
@@ -103,8 +102,7 @@ gdn_status check_ring(const gdn_ring* r, int in_dt) {
   GDN_REQUIRE(valid_dtype(r->dtype), GDN_EINVAL, "ring dtype %d is not a gdn_dtype", (int)r->dtype);
   if (in_dt >= 0)
     GDN_REQUIRE((int)r->dtype == in_dt, GDN_EINVAL, "ring dtype %d differs from in_dtype %d", (int)r->dtype, in_dt);
-  const size_t eb = dtype_bytes(r->dtype);
-  GDN_REQUIRE(aligned(r->k, eb) && aligned(r->v, eb) && aligned(r->g, 4) && aligned(r->beta, 4) &&
+  GDN_REQUIRE(aligned(r->k, 16) && aligned(r->v, 16) && aligned(r->g, 4) && aligned(r->beta, 4) &&
                   aligned(r->start, 4) && aligned(r->count, 4),
               GDN_EINVAL, "a ring pointer is misaligned");
   return GDN_OK;

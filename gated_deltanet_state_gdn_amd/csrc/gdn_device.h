@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn.h"
 
 namespace gdn {
@@ -96,6 +98,19 @@ template <int DT, int VEC, bool NT>
 struct TileIO {
   static_assert(VEC * StateElem<DT>::BYTES == 16 || VEC * StateElem<DT>::BYTES == 8, "8/16-byte vectors");
   static constexpr int WORDS = VEC * StateElem<DT>::BYTES / 4;
+  typedef unsigned int Raw __attribute__((ext_vector_type(WORDS)));
+
+  // Raw (still packed) access: a 16-bit tile stays packed in registers and is
+  // widened on use, halving the registers that hold it.
+  __device__ __forceinline__ static Raw load_raw(const void* p) {
+    return NT ? __builtin_nontemporal_load(static_cast<const Raw*>(p)) : *static_cast<const Raw*>(p);
+  }
+  __device__ __forceinline__ static void widen(const Raw& w, float (&f)[VEC]) { unpack<WORDS>(w, f); }
+  __device__ __forceinline__ static Raw pack_raw(const float (&f)[VEC]) {
+    Raw w;
+    pack<WORDS>(f, w);
+    return w;
+  }
 
   __device__ __forceinline__ static void load(const void* p, float (&f)[VEC]) {
     if constexpr (WORDS == 4) {
@@ -146,6 +161,66 @@ struct TileIO {
   }
 };
 
+// ------------------------------------------------------------------ batched row staging
+// Stages MAXR rows of ROWLEN elements (element size EB bytes: 4 for f32, 2 for
+// bf16/f16) from global memory into LDS as floats.  issue() starts every
+// 16-byte load of the block at once (one memory round trip for the whole
+// block; rows >= nrows read as zero); commit() waits for them, widens and
+// stores to LDS.  Keeping the two apart lets a caller overlap the loads of
+// the next block with work on the current one.  Row r starts at element
+// row_off(r) of the source, which must be 16-byte aligned.
+template <int ROWLEN, int MAXR, int NTH, int EB>
+struct RowStager {
+  static constexpr int VE = 16 / EB;               // elements per 16-byte load
+  static_assert(ROWLEN % VE == 0, "rows are whole 16-byte vectors");
+  static constexpr int CPR = ROWLEN / VE;          // loads per row
+  static constexpr int TOTAL = MAXR * CPR;
+  static constexpr int IT = (TOTAL + NTH - 1) / NTH;
+  u32x4 v[IT];
+
+  template <class RowOff>
+  __device__ __forceinline__ void issue(const void* src, int nrows, const RowOff& row_off) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * NTH;
+      const int r = idx / CPR, c = (idx - r * CPR) * VE;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (idx < TOTAL && r < nrows)
+        x = *reinterpret_cast<const u32x4*>(static_cast<const char*>(src) + ((int64_t)row_off(r) + c) * EB);
+      v[it] = x;
+    }
+  }
+
+  // dt selects bf16 or f16 widening when EB == 2; rows >= nrows are not written.
+  __device__ __forceinline__ void commit(float* dst, int ldd, int dt, int nrows = MAXR) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * NTH;
+      const int r = idx / CPR, c = (idx - r * CPR) * VE;
+      if (idx >= TOTAL || r >= nrows) continue;
+      float* d = dst + r * ldd + c;
+      if constexpr (EB == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = __uint_as_float(v[it][e]);
+      } else if (dt == GDN_BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d[2 * e] = unpack_lo<GDN_BF16>(v[it][e]);
+          d[2 * e + 1] = unpack_hi<GDN_BF16>(v[it][e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d[2 * e] = unpack_lo<GDN_F16>(v[it][e]);
+          d[2 * e + 1] = unpack_hi<GDN_F16>(v[it][e]);
+        }
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------ wave64 reductions
 template <int OFF_FROM>
 __device__ __forceinline__ float xor_sum_from(float x) {
@@ -157,13 +232,39 @@ __device__ __forceinline__ float xor_sum_from(float x) {
 
 __device__ __forceinline__ float wave_sum(float x) { return xor_sum_from<1>(x); }
 
+// Sum over the 64 lanes of a wave on the DPP path (row shifts within 16-lane
+// rows, then row broadcasts), result returned uniformly from lane 63.  A
+// handful of dependent VALU ops instead of six LDS-crossbar permutes.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  auto dpp = [](float v, auto ctrl, auto rmask) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                 decltype(rmask)::value, 0xf, true));
+  };
+  using c_shr1 = std::integral_constant<int, 0x111>;
+  using c_shr2 = std::integral_constant<int, 0x112>;
+  using c_shr4 = std::integral_constant<int, 0x114>;
+  using c_shr8 = std::integral_constant<int, 0x118>;
+  using c_bc15 = std::integral_constant<int, 0x142>;
+  using c_bc31 = std::integral_constant<int, 0x143>;
+  using all_rows = std::integral_constant<int, 0xf>;
+  using rows_13 = std::integral_constant<int, 0xa>;
+  using rows_23 = std::integral_constant<int, 0xc>;
+  x += dpp(x, c_shr1{}, all_rows{});
+  x += dpp(x, c_shr2{}, all_rows{});
+  x += dpp(x, c_shr4{}, all_rows{});
+  x += dpp(x, c_shr8{}, all_rows{});   // lane 16r + 15 holds the sum of row r
+  x += dpp(x, c_bc15{}, rows_13{});    // lane 31 / 63: rows 0+1 / 2+3
+  x += dpp(x, c_bc31{}, rows_23{});    // lane 63: all four rows
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // ------------------------------------------------------------------ tile geometry
 // A workgroup of NW waves streams one dk x dv tile (dk == dv == D).  Each lane
 // owns VEC consecutive columns of a row; LPR lanes cover a row, a wave covers
 // RPW rows per pass and the workgroup NW * RPW rows per pass.  Lanes with equal
 // (lane % LPR) own the same columns, so column sums over the rows need a
 // butterfly over lane bits >= log2(LPR) and then a sum over the NW waves.
-template <int DT, int D>
+template <int DT, int D, int MAXW = 4>
 struct TileGeom {
   static constexpr int BYTES = StateElem<DT>::BYTES;
   // widest vector (16 B) that still leaves at least one row per wave
@@ -171,7 +272,7 @@ struct TileGeom {
   static constexpr int VEC = (64 / (D / VEC0) > D) ? VEC0 / 2 : VEC0;
   static constexpr int LPR = D / VEC;
   static constexpr int RPW = 64 / LPR;
-  static constexpr int NW = (D / RPW) >= 4 ? 4 : (D / RPW);
+  static constexpr int NW = (D / RPW) >= MAXW ? MAXW : (D / RPW);
   static constexpr int PASSES = D / (RPW * NW);
   static_assert(LPR * VEC == D && LPR * RPW == 64 && PASSES * RPW * NW == D, "tile geometry");
 };

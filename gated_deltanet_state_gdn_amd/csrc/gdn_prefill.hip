@@ -67,7 +67,7 @@ __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4)
 __device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
 
 // ---------------------------------------------------------------- kernel 1
-template <int D>
+template <int D, int EB>
 __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
   constexpr int LDK = D + 4, LDT = kC + 4;
   __shared__ float s_k[kC][LDK], s_q[kC][LDK];
@@ -94,16 +94,13 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   const int len = min(kC, seq_hi - t0);
   const int hk = h / (p.Hv / p.Hk);
 
-  for (int i = tid; i < kC * D; i += 256) {
-    const int t = i / D, d = i - t * D;
-    float kv = 0.f, qv = 0.f;
-    if (t < len) {
-      const int64_t off = ((int64_t)(t0 + t) * p.Hk + hk) * D + d;
-      kv = load_elem(p.k, off, p.in_dt);
-      qv = load_elem(p.q, off, p.in_dt);
-    }
-    s_k[t][d] = kv;
-    s_q[t][d] = qv;
+  {
+    RowStager<D, kC, 256, EB> sk, sq;
+    auto row = [&](int t) { return ((int64_t)(t0 + t) * p.Hk + hk) * D; };
+    sk.issue(p.k, len, row);
+    sq.issue(p.q, len, row);
+    sk.commit(&s_k[0][0], LDK, p.in_dt);
+    sq.commit(&s_q[0][0], LDK, p.in_dt);
   }
   if (tid < kC) {
     float g = 0.f, be = 0.f;
@@ -212,7 +209,7 @@ struct PrefillGeom {
   static constexpr int NJ = BV / 16;
 };
 
-template <int SDT, int D>
+template <int SDT, int D, int EB>
 __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArgs p, const float* __restrict__ ws) {
   using G = PrefillGeom<D>;
   constexpr int BV = G::BV, NB = G::NB, NJ = G::NJ;
@@ -224,7 +221,8 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
   __shared__ float s_T[kC][LDT], s_P[kC][LDT];
   __shared__ float s_S[D][LDV];
   __shared__ float s_X[2 * kC][LDV];  // K S (rows 0..C-1), Q S (rows C..2C-1)
-  __shared__ float s_beta[kC], s_eg[kC], s_dec[kC], s_egC;
+  __shared__ float s_gb[2][kC];  // gamma, beta of the chunk
+  __shared__ float s_eg[kC], s_dec[kC], s_egC;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
@@ -257,39 +255,46 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
   float* s_q = s_qru;
   float* s_R = s_qru;
   float* s_U = s_qru + kC * LDV;
+  const float* s_beta = s_gb[1];
   const int nch = (len + kC - 1) / kC;
-  for (int c = 0; c < nch; ++c) {
+
+  // chunk inputs are staged through registers: the loads of chunk c + 1 are
+  // issued right after chunk c reaches LDS and complete under its GEMMs
+  RowStager<D, kC, 256, EB> stk, stq;
+  RowStager<BV, kC, 256, EB> stv;
+  RowStager<kC, kC, 256, 4> stT, stP;
+  RowStager<kC, 2, 256, 4> stg;
+  auto issue = [&](int c) {
     const int t0 = seq_lo + c * kC;
     const int L = min(kC, seq_hi - t0);
     const float* wsp = ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats;
-    for (int i = tid; i < kC * D; i += 256) {
-      const int t = i / D, d = i - t * D;
-      float kv = 0.f, qv = 0.f;
-      if (t < L) {
-        const int64_t off = ((int64_t)(t0 + t) * p.Hk + hk) * D + d;
-        kv = load_elem(p.k, off, p.in_dt);
-        qv = load_elem(p.q, off, p.in_dt);
-      }
-      s_k[t][d] = kv;
-      s_q[t * LDK + d] = qv;
-    }
-    for (int i = tid; i < kC * BV; i += 256) {
-      const int t = i / BV, j = i - t * BV;
-      s_v[t][j] = (t < L) ? load_elem(p.v, ((int64_t)(t0 + t) * p.Hv + h) * D + col0 + j, p.in_dt) : 0.f;
-    }
-    for (int i = tid; i < kC * kC; i += 256) {
-      s_T[i / kC][i % kC] = wsp[i];
-      s_P[i / kC][i % kC] = wsp[kC * kC + i];
-    }
-    if (tid < kC) {
-      const float gt = wsp[2 * kC * kC + tid];
-      const float gC = wsp[2 * kC * kC + kC - 1];
-      s_beta[tid] = wsp[2 * kC * kC + kC + tid];
+    auto krow = [&](int t) { return ((int64_t)(t0 + t) * p.Hk + hk) * D; };
+    stk.issue(p.k, L, krow);
+    stq.issue(p.q, L, krow);
+    stv.issue(p.v, L, [&](int t) { return ((int64_t)(t0 + t) * p.Hv + h) * D + col0; });
+    auto mrow = [](int r) { return (int64_t)r * kC; };
+    stT.issue(wsp, kC, mrow);
+    stP.issue(wsp + kC * kC, kC, mrow);
+    stg.issue(wsp + 2 * kC * kC, 2, mrow);
+  };
+  issue(0);
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = seq_lo + c * kC;
+    const int L = min(kC, seq_hi - t0);
+    stk.commit(&s_k[0][0], LDK, p.in_dt);
+    stq.commit(s_q, LDK, p.in_dt);
+    stv.commit(&s_v[0][0], LDV, p.in_dt);
+    stT.commit(&s_T[0][0], LDT, GDN_F32);
+    stP.commit(&s_P[0][0], LDT, GDN_F32);
+    stg.commit(&s_gb[0][0], kC, GDN_F32);
+    __syncthreads();
+    if (c + 1 < nch) issue(c + 1);
+    if (tid < kC) {  // read after the next barrier
+      const float gt = s_gb[0][tid], gC = s_gb[0][kC - 1];
       s_eg[tid] = expf(gt);
       s_dec[tid] = expf(gC - gt);
       if (tid == 0) s_egC = expf(gC);
     }
-    __syncthreads();
 
     // X = [K; Q] S
     for (int job = wave; job < 8 * NJ; job += 4) {
@@ -359,30 +364,41 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
   }
 }
 
-template <int D>
+template <int D, int EB>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
   const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens);
-  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D>), dim3((unsigned)ncs, (unsigned)a.Hv), dim3(256), 0, s, a, ws);
+  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB>), dim3((unsigned)ncs, (unsigned)a.Hv), dim3(256), 0, s, a, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.N * a.Hv;
   const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
   switch (state_dt) {
-    case GDN_F32: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
-    case GDN_BF16: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
-    case GDN_F16: hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D>), dim3(grid), dim3(256), 0, s, a, ws); break;
+    case GDN_F32:
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      break;
+    case GDN_BF16:
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      break;
+    case GDN_F16:
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_prefill_eb(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
+  return a.in_dt == GDN_F32 ? launch_prefill_d<D, 4>(a, state_dt, ws, s) : launch_prefill_d<D, 2>(a, state_dt, ws, s);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s) {
   if (chunk != kC) return hipErrorInvalidValue;
   switch (D) {
-    case 16: return launch_prefill_d<16>(a, state_dt, ws, s);
-    case 32: return launch_prefill_d<32>(a, state_dt, ws, s);
-    case 64: return launch_prefill_d<64>(a, state_dt, ws, s);
-    case 128: return launch_prefill_d<128>(a, state_dt, ws, s);
+    case 16: return launch_prefill_eb<16>(a, state_dt, ws, s);
+    case 32: return launch_prefill_eb<32>(a, state_dt, ws, s);
+    case 64: return launch_prefill_eb<64>(a, state_dt, ws, s);
+    case 128: return launch_prefill_eb<128>(a, state_dt, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,50 +10,50 @@
 //      rank-1 updates on the tile held in VGPRs, one column reduction per
 //      entry), write S0 back rounded once, and empty the ring;
 //   2. append the T new entries at (start + count + t) mod L;
-//   3. window position t outputs scale * S_t^T q_t with S_t = S0 advanced over
-//      the live entries up to t, WITHOUT materialising S_t.  Unrolling
-//      S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T and transposing
-//      gives the adjoint chain
-//          w <- q;  for i = n-1 .. 0:  c = b_i (k_i . w);  acc += c v_i;
-//                                        w <- a_i (w - c k_i)
-//          S_n^T q = S0^T w + acc
-//      (a_i = exp(g_i)), so each position costs O(n (dk + dv)) for its chain
-//      and all T positions share ONE read pass over S0: o = S0^T W + ACC.
-// The chains depend only on the ring, so they run while the S0 loads are in
-// flight.
+//   3. window position t outputs scale * S_t^T q_t, S_t being S0 advanced
+//      over live entries first..e_t, without materialising S_t.
+//
+// Step 3 unrolls S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T
+// (a_i = exp(g_i)).  Transposing gives S_n^T q = S0^T w + sum_j c_j v_j with
+//     w   = e^{G_n} q - sum_j e^{G_j} c_j k_j
+//     c_i = b_i (e^{G_n - G_i} (k_i . q) - sum_{j > i} e^{G_j - G_i} (k_i . k_j) c_j)
+// where G_j is the sum of g over the live entries first..j (all exponents are
+// <= 0).  The c are one small back substitution over the Gram matrix k_i . k_j
+// and the products k_i . q_t, so every window position costs O(n (dk + dv))
+// plus O(n^2) scalars, and all T positions share ONE read pass over S0:
+// o = scale (S0^T W + ACC).  Everything before that pass depends only on the
+// ring and the inputs, so it runs while the S0 loads are in flight.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
+// streaming (non-temporal) checkpoint loads and stores for fp32 checkpoints
+#ifndef GDN_REPLAY_NT_F32
+#define GDN_REPLAY_NT_F32 1
+#endif
+
 namespace gdn {
 
-constexpr int kReplayTB = 4;  // window positions reduced per output pass
+constexpr int kStageRows = 16;  // entry rows staged per batch of loads
 
-template <int DT>
-__device__ __forceinline__ float storage_roundtrip(float x) {
-  if constexpr (DT == GDN_F32) {
-    return x;
-  } else {
-    return unpack_lo<DT>(pack2<DT>(x, 0.f));
-  }
-}
-
-// Dynamic LDS: staged entries (k, v, alpha, g, beta) for E = L + T slots, then
-// the chain results w and acc for T window positions.
+// Dynamic LDS (floats): staged entries k, v [E][D+1] (E = L + T), window
+// queries [T][D+1], gates (exp(g), g, beta, prefix G) [E] each, Gram matrix
+// [E][E], key / query products [E][T], coefficients [T][E], chain vectors w
+// and acc [T][D].
 __host__ __device__ inline size_t replay_lds_bytes(int D, int L, int T) {
   const size_t E = (size_t)L + (size_t)T;
-  return (E * (2 * (size_t)D + 3) + 2 * (size_t)T * D) * sizeof(float);
+  return (2 * E * (D + 1) + (size_t)T * (D + 1) + 4 * E + E * E + 2 * E * T + 2 * (size_t)T * D) * sizeof(float);
 }
 
-template <int SDT, int D, bool NT>
+template <int SDT, int D, bool NT, int TB, int EB>
 __global__ void __launch_bounds__((TileGeom<SDT, D>::NW * 64))
 gdn_replay_kernel(const ReplayArgs P) {
   using G = TileGeom<SDT, D>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
   constexpr int NTH = NW * 64;
-  constexpr int DL = (D + 63) / 64;  // chain elements per lane
-  constexpr int TB = kReplayTB;
+  constexpr int LDE = D + 1;  // padded entry rows: per-thread dot products hit distinct banks
   using IO = TileIO<SDT, VEC, NT>;
   using ST = typename StateElem<SDT>::T;
+  using Stager = RowStager<D, kStageRows, NTH, EB>;
 
   extern __shared__ float s_dyn[];
   __shared__ float s_red[2][NW][D];
@@ -91,90 +91,145 @@ gdn_replay_kernel(const ReplayArgs P) {
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
 
-  float s[PASSES][VEC];
+  typename IO::Raw raw[PASSES];
 #pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) IO::load(tile + (r0 + pp * NW * RPW) * D + c0, s[pp]);
+  for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
 
   // ---- stage live entries in LDS: committed ones (live order), then the window
   const int E = L + T;
-  float* e_k = s_dyn;              // [E][D]
-  float* e_v = e_k + E * D;        // [E][D]
-  float* e_a = e_v + E * D;        // [E]  exp(g)
-  float* e_g = e_a + E;            // [E]
-  float* e_b = e_g + E;            // [E]
-  float* s_w = e_b + E;            // [T][D]
-  float* s_acc = s_w + T * D;      // [T][D]
+  float* e_k = s_dyn;               // [E][LDE]
+  float* e_v = e_k + E * LDE;       // [E][LDE]
+  float* e_q = e_v + E * LDE;       // [T][LDE] window queries
+  float* e_a = e_q + T * LDE;       // [E] exp(g)
+  float* e_g = e_a + E;             // [E] g
+  float* e_b = e_g + E;             // [E] beta
+  float* e_G = e_b + E;             // [E] prefix sum of g over the live entries
+  float* s_gram = e_G + E;          // [E][E]
+  float* s_kq = s_gram + E * E;     // [E][T]
+  float* s_c = s_kq + E * T;        // [T][E]
+  float* s_w = s_c + T * E;         // [T][D]
+  float* s_acc = s_w + T * D;       // [T][D]
 
   const int64_t ring_e = unit * L;  // first ring entry of this unit
-  for (int i = tid; i < cnt * D; i += NTH) {
-    const int e = i / D, c = i - e * D;
-    const int j = (st + e) % L;
-    e_k[e * D + c] = load_elem(R.k, (ring_e + j) * D + c, p.in_dt);
-    e_v[e * D + c] = load_elem(R.v, (ring_e + j) * D + c, p.in_dt);
+  for (int t = tid; t < cnt + T; t += NTH) {
+    if (t < cnt) {
+      const int j = (st + t) % L;
+      const float g = R.g[ring_e + j];
+      e_g[t] = g;
+      e_a[t] = expf(g);
+      e_b[t] = R.beta[ring_e + j];
+    } else {
+      const int64_t gi = ((int64_t)b * T + (t - cnt)) * p.Hv + h;
+      const float g = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
+      e_g[t] = g;
+      e_a[t] = expf(g);
+      e_b[t] = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+    }
   }
-  for (int e = tid; e < cnt; e += NTH) {
-    const int j = (st + e) % L;
-    const float g = R.g[ring_e + j];
-    e_g[e] = g;
-    e_a[e] = expf(g);
-    e_b[e] = R.beta[ring_e + j];
+  for (int r0s = 0; r0s < cnt; r0s += kStageRows) {  // committed entries, 16 rows per round trip
+    Stager sk, sv;
+    auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
+    const int nr = min(kStageRows, cnt - r0s);
+    sk.issue(R.k, nr, ring_row);
+    sv.issue(R.v, nr, ring_row);
+    sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
+    sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
   }
-  for (int i = tid; i < T * D; i += NTH) {
-    const int t = i / D, c = i - t * D;
-    e_k[(cnt + t) * D + c] = load_elem(p.k, (((int64_t)b * T + t) * p.Hk + hk) * D + c, p.in_dt);
-    e_v[(cnt + t) * D + c] = load_elem(p.v, (((int64_t)b * T + t) * p.Hv + h) * D + c, p.in_dt);
-  }
-  for (int t = tid; t < T; t += NTH) {
-    const int64_t gi = ((int64_t)b * T + t) * p.Hv + h;
-    const float g = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
-    e_g[cnt + t] = g;
-    e_a[cnt + t] = expf(g);
-    e_b[cnt + t] = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+  for (int t0s = 0; t0s < T; t0s += kStageRows) {  // the window's keys, values and queries
+    Stager sk, sv, sq;
+    const int nr = min(kStageRows, T - t0s);
+    auto key_row = [&](int t) { return (((int64_t)b * T + t0s + t) * p.Hk + hk) * D; };
+    sk.issue(p.k, nr, key_row);
+    sv.issue(p.v, nr, [&](int t) { return (((int64_t)b * T + t0s + t) * p.Hv + h) * D; });
+    sq.issue(p.q, nr, key_row);
+    sk.commit(e_k + (cnt + t0s) * LDE, LDE, p.in_dt, nr);
+    sv.commit(e_v + (cnt + t0s) * LDE, LDE, p.in_dt, nr);
+    sq.commit(e_q + t0s * LDE, LDE, p.in_dt, nr);
   }
   __syncthreads();
 
-  // ---- window chains (independent of S0; overlap the tile loads)
   const int first = fold ? cnt : 0;  // first live entry after an eventual fold
-  for (int t = wave; t < T; t += NW) {
-    float w[DL], acc[DL];
+  const int n_all = cnt + T - first;  // live entries of the last window position (<= L)
+  if (T > 0) {
+    // prefix sums of g over the live entries (one wave; n_all <= 64)
+    if (wave == 0) {
+      float x = (lane < n_all) ? e_g[first + lane] : 0.f;
 #pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const int c = lane + 64 * j;
-      w[j] = (c < D) ? load_elem(p.q, (((int64_t)b * T + t) * p.Hk + hk) * D + c, p.in_dt) : 0.f;
-      acc[j] = 0.f;
-    }
-    for (int i = cnt + t; i >= first; --i) {
-      float dot = 0.f;
-#pragma unroll
-      for (int j = 0; j < DL; ++j) {
-        const int c = lane + 64 * j;
-        if (c < D) dot = fmaf(e_k[i * D + c], w[j], dot);
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
       }
-      const float cf = e_b[i] * wave_sum(dot);
-      const float al = e_a[i];
-#pragma unroll
-      for (int j = 0; j < DL; ++j) {
-        const int c = lane + 64 * j;
-        if (c < D) {
-          acc[j] = fmaf(cf, e_v[i * D + c], acc[j]);
-          w[j] = al * fmaf(-cf, e_k[i * D + c], w[j]);
+      if (lane < n_all) e_G[first + lane] = x;
+    }
+    // Gram matrix of the live keys (upper triangle) and the key / query products
+    const int n_gram = n_all * (n_all - 1) / 2;
+    for (int task = tid; task < n_gram + n_all * T; task += NTH) {
+      float acc = 0.f;
+      if (task < n_gram) {  // pair (i, j), i < j, row-major over the upper triangle
+        int i = 0, rem = task;
+        while (rem >= n_all - 1 - i) {
+          rem -= n_all - 1 - i;
+          ++i;
         }
+        const int j = i + 1 + rem;
+        const float* ki = e_k + (first + i) * LDE;
+        const float* kj = e_k + (first + j) * LDE;
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) acc = fmaf(ki[c], kj[c], acc);
+        s_gram[(first + i) * E + first + j] = acc;
+      } else {
+        const int x = task - n_gram, i = x / T, t = x - i * T;
+        const float* ki = e_k + (first + i) * LDE;
+        const float* qt = e_q + t * LDE;
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) acc = fmaf(ki[c], qt[c], acc);
+        s_kq[(first + i) * T + t] = acc;
       }
     }
-#pragma unroll
-    for (int j = 0; j < DL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < D) {
-        s_w[t * D + c] = w[j];
-        s_acc[t * D + c] = acc[j];
-      }
+  }
+  __syncthreads();
+
+  // ---- back substitution for the coefficients of each window position (one wave each)
+  for (int t = wave; t < T; t += NW) {
+    const int e_last = cnt + t;  // last live entry of position t
+    const float Gn = e_G[e_last];
+    const int j = first + lane;  // lane holds the residual of live entry j
+    const bool live = j <= e_last;
+    const float Gj = live ? e_G[j] : 0.f;
+    float r = live ? expf(Gn - Gj) * s_kq[j * T + t] : 0.f;
+    float cj = 0.f;
+    for (int i = e_last; i >= first; --i) {
+      // c_i = beta_i * residual_i, then every earlier entry drops its term
+      const float ci = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e_b[i] * r), i - first));
+      if (j == i) cj = ci;
+      if (live && j < i) r = fmaf(-expf(e_G[i] - Gj) * s_gram[j * E + i], ci, r);
     }
+    if (live) s_c[t * E + j] = cj;
+  }
+  __syncthreads();
+  // chain vectors: w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j,  acc_t = sum_j c_j v_j
+  for (int x = tid; x < T * D; x += NTH) {
+    const int t = x / D, c = x - t * D;
+    const int e_last = cnt + t;
+    float w = expf(e_G[e_last]) * e_q[t * LDE + c];
+    float acc = 0.f;
+    for (int jj = first; jj <= e_last; ++jj) {
+      const float cj = s_c[t * E + jj];
+      w = fmaf(-expf(e_G[jj]) * cj, e_k[jj * LDE + c], w);
+      acc = fmaf(cj, e_v[jj * LDE + c], acc);
+    }
+    s_w[t * D + c] = w;
+    s_acc[t * D + c] = acc;
   }
 
   // ---- fold the committed entries into the tile, write the checkpoint back
   if (fold) {
+    float s[PASSES][VEC];
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
     for (int i = 0; i < cnt; ++i) {
-      const float* ki = e_k + i * D;
+      const float* ki = e_k + i * LDE;
       float kvp[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) kvp[e] = 0.f;
@@ -199,7 +254,7 @@ gdn_replay_kernel(const ReplayArgs P) {
         float kv = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) kv += red[w * D + c0 + e];
-        delta[e] = be * (e_v[i * D + c0 + e] - al * kv);
+        delta[e] = be * (e_v[i * LDE + c0 + e] - al * kv);
       }
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) {
@@ -208,11 +263,11 @@ gdn_replay_kernel(const ReplayArgs P) {
         for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr * delta[e]);
       }
     }
+    // one rounding: the stored checkpoint and the tile the outputs read are the rounded values
 #pragma unroll
     for (int pp = 0; pp < PASSES; ++pp) {
+      raw[pp] = IO::pack_raw(s[pp]);
       IO::store(tile + (r0 + pp * NW * RPW) * D + c0, s[pp]);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s[pp][e] = storage_roundtrip<SDT>(s[pp][e]);
     }
   }
 
@@ -249,12 +304,14 @@ gdn_replay_kernel(const ReplayArgs P) {
 #pragma unroll
     for (int pp = 0; pp < PASSES; ++pp) {
       const int r = r0 + pp * NW * RPW;
+      float sv[VEC];
+      IO::widen(raw[pp], sv);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         if (tb < nt) {
           const float wr = s_w[(t0 + tb) * D + r];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) part[tb][e] = fmaf(s[pp][e], wr, part[tb][e]);
+          for (int e = 0; e < VEC; ++e) part[tb][e] = fmaf(sv[e], wr, part[tb][e]);
         }
       }
     }
@@ -296,13 +353,22 @@ __global__ void gdn_replay_rollback_kernel(const ReplayArgs P) {
   *cnt = c < 0 ? 0 : c;
 }
 
-template <int SDT, int D>
-static hipError_t launch_replay_t(const ReplayArgs& a, hipStream_t s) {
+template <int SDT, int D, int TB, int EB>
+static hipError_t launch_replay_k(const ReplayArgs& a, hipStream_t s) {
   using G = TileGeom<SDT, D>;
+  constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   const size_t lds = replay_lds_bytes(D, a.ring.L, a.T);
-  hipLaunchKernelGGL((gdn_replay_kernel<SDT, D, false>), dim3(grid), dim3(G::NW * 64), lds, s, a);
+  hipLaunchKernelGGL((gdn_replay_kernel<SDT, D, NT, TB, EB>), dim3(grid), dim3(G::NW * 64), lds, s, a);
   return hipGetLastError();
+}
+
+template <int SDT, int D>
+static hipError_t launch_replay_t(const ReplayArgs& a, hipStream_t s) {
+  const bool f32_in = a.d.in_dt == GDN_F32;
+  if (a.T <= 1)
+    return f32_in ? launch_replay_k<SDT, D, 1, 4>(a, s) : launch_replay_k<SDT, D, 1, 2>(a, s);
+  return f32_in ? launch_replay_k<SDT, D, 4, 4>(a, s) : launch_replay_k<SDT, D, 4, 2>(a, s);
 }
 
 template <int SDT>
@@ -340,10 +406,11 @@ hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// static LDS of the widest instantiation (TB = 4)
 template <int SDT, int D>
 static size_t replay_static_lds() {
   using G = TileGeom<SDT, D>;
-  return (size_t)(2 + kReplayTB) * G::NW * D * sizeof(float);
+  return (size_t)(2 + 4) * G::NW * D * sizeof(float);
 }
 
 template <int SDT>

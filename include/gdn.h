@@ -30,7 +30,8 @@
  *   - Calls only validate and enqueue work on `stream` (a hipStream_t; NULL
  *     is the default stream).  They return before the work runs.
  *   - Tensors are dense and row-major with the last dimension fastest.
- *     Inputs q, k, v, a, b share one dtype `in_dtype`.
+ *     Inputs q, k, v, a, b share one dtype `in_dtype`; q, k, v (and ring k,
+ *     v) must be 16-byte aligned (they are read with 16-byte vector loads).
  *   - State pools are [num_slots, Hv, dk, dv] (dv fastest), 16-byte aligned.
  *     Value head h reads key head h / (Hv / Hk) (contiguous groups).
  *   - A slot index outside [0, num_slots) marks a padded row: its outputs

@@ -85,6 +85,7 @@ def _decode(L, dims=None, B=4, q=FAKE, k=FAKE, v=FAKE, in_dt=gdn.GDN_BF16, gates
     (dict(q=None), gdn.GDN_EINVAL),
     (dict(out=None), gdn.GDN_EINVAL),
     (dict(q=FAKE + 1), gdn.GDN_EINVAL),                                       # misaligned bf16
+    (dict(k=FAKE + 8), gdn.GDN_EINVAL),                                       # not 16-byte aligned
     (dict(out=FAKE + 2), gdn.GDN_EINVAL),                                     # misaligned f32 out
     (dict(in_dt=7), gdn.GDN_EINVAL),
     (dict(out_dt=-1), gdn.GDN_EINVAL),
