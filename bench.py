@@ -190,13 +190,13 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
         inp = gen.token_inputs(cid, s, (B, T), HK, HV, D, D, "bf16")
         ins.append([gen.to_torch(inp[x], dev) for x in "qkvab"])
     out = torch.empty((B, T, HV, D), dtype=torch.bfloat16, device=dev)
-    zero_rej = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(gdn.gdn_replay_workspace_bytes(HK, HV, D, D, B, T), dtype=torch.uint8, device=dev)
     warm = steps_per_cycle
     n = cycles * steps_per_cycle
 
     def fn(i):
         q, k, v, a, b = ins[i % n_in]
-        gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out)
+        gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out, workspace=ws)
 
     t = timed_launches(torch, fn, n, warm)
     # byte model follows the (deterministic) per-slot count of the aligned schedule
@@ -218,7 +218,7 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
     }
     src = ["gdn_replay.hip", "gdn_device.h"]
     res["roofline"] = roofline_bw(nbytes / n, t["mean_launch_ms"], traffic_for(f"replay_{sdt}_B{B}_T{T}", src))
-    del ckpt, ring, ins
+    del ckpt, ring, ins, ws
     torch.cuda.empty_cache()
     return res
 

@@ -10,5 +10,6 @@ missing).
 from ._binding import (  # noqa: F401
     EXPORTS, GDN_BF16, GDN_EINVAL, GDN_ELAUNCH, GDN_EUNSUPPORTED, GDN_F16, GDN_F32, GDN_OK, GdnError, LIB_PATH, Ring,
     dtype_code, gdn_chunk_prefill, gdn_chunk_prefill_workspace_bytes, gdn_decode_step, gdn_last_error,
-    gdn_replay_decode, gdn_replay_flush, gdn_replay_rollback, gdn_status_string, lib, new_ring,
+    gdn_replay_decode, gdn_replay_flush, gdn_replay_rollback, gdn_replay_workspace_bytes, gdn_status_string, lib,
+    new_ring,
 )

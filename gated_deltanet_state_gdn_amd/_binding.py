@@ -20,7 +20,8 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
 
 # every symbol include/gdn.h declares
 EXPORTS = (
-    "gdn_decode_step", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_decode",
+    "gdn_decode_step", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
+    "gdn_replay_decode",
     "gdn_replay_flush", "gdn_replay_rollback", "gdn_status_string", "gdn_last_error",
 )
 
@@ -69,7 +70,8 @@ def lib() -> ctypes.CDLL:
         "gdn_decode_step": (INT, [pd, I32, P, P, P, INT, pg, pp, P, P, INT, P]),
         "gdn_chunk_prefill_workspace_bytes": (SZ, [pd, I32, I64, I32]),
         "gdn_chunk_prefill": (INT, [pd, I32, P, I64, I32, P, P, P, INT, pg, pp, P, P, INT, P, SZ, P]),
-        "gdn_replay_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P]),
+        "gdn_replay_workspace_bytes": (SZ, [pd, I32, I32]),
+        "gdn_replay_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P, SZ, P]),
         "gdn_replay_flush": (INT, [pd, I32, pp, P, pr, P]),
         "gdn_replay_rollback": (INT, [pd, I32, P, P, pr, P]),
         "gdn_status_string": (ctypes.c_char_p, [INT]),
@@ -198,20 +200,30 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, pool, slot_map, cu_seqlens,
     return out
 
 
+def gdn_replay_workspace_bytes(Hk, Hv, dk, dv, B, T) -> int:
+    dims = _dims(Hk, Hv, dk, dv, None)
+    return int(lib().gdn_replay_workspace_bytes(ctypes.byref(dims), int(B), int(T)))
+
+
 def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring, out=None, out_dtype=None,
-                      scale=None, stream=None):
+                      workspace=None, scale=None, stream=None):
     """Replay step of T tokens; q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, b [B, T, Hv]."""
     torch = _torch()
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     if out is None:
         out = torch.empty((B, T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+    need = gdn_replay_workspace_bytes(Hk, Hv, dk, dv, B, T)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dims = _dims(Hk, Hv, dk, dv, scale)
     rs = ring.c_struct()
     _check(lib().gdn_replay_decode(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
                                    ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(ckpt)),
-                                   _ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype),
-                                   _stream(stream)))
+                                   _ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype), ws_ptr,
+                                   ws_bytes, _stream(stream)))
     return out
 
 

@@ -187,10 +187,15 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_replay_workspace_bytes(const gdn_dims* dims, int32_t B, int32_t T) {
+  if (dims == nullptr || B <= 0 || T <= 0 || dims->num_v_heads < 1 || dims->dv < 1) return 0;
+  return gdn::replay_workspace_bytes(B, dims->num_v_heads, T, dims->dv);
+}
+
 gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
                              const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
                              const int32_t* slot_map, const gdn_ring* ring, void* out, gdn_dtype out_dtype,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   GDN_TRY(check_dims(dims));
   GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
   GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
@@ -205,9 +210,14 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
   GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
               (long long)ring->num_slots, (long long)ckpt->num_slots);
   GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
-  GDN_REQUIRE(gdn::replay_lds_total(ckpt->dtype, dims->dk, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+  GDN_REQUIRE(gdn::replay_lds_total(dims->dk, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
               "ring length L=%d with window T=%d at dk=%d exceeds the 64 KiB LDS staging budget", ring->L, T,
               dims->dk);
+  const size_t need = gdn_replay_workspace_bytes(dims, B, T);
+  GDN_REQUIRE(workspace_bytes >= need, GDN_EINVAL, "workspace of %zu bytes is below the %zu required",
+              workspace_bytes, need);
+  GDN_REQUIRE(workspace != nullptr && aligned(workspace, 256), GDN_EINVAL,
+              "workspace is NULL or not 256-byte aligned");
   GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
   gdn::ReplayArgs a{};
   a.d = gdn::DecodeArgs{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, ckpt->base, slot_map, out,
@@ -215,7 +225,8 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
                         (int32_t)out_dtype, eff_scale(dims)};
   a.ring = ring_args(ring);
   a.T = T;
-  return launched(gdn::launch_replay(a, ckpt->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+  return launched(gdn::launch_replay(a, ckpt->dtype, dims->dk, static_cast<float*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt, const int32_t* slot_map,
@@ -228,7 +239,7 @@ gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckp
   GDN_TRY(check_ring(ring, -1));
   GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
               (long long)ring->num_slots, (long long)ckpt->num_slots);
-  GDN_REQUIRE(gdn::replay_lds_total(ckpt->dtype, dims->dk, ring->L, 0) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+  GDN_REQUIRE(gdn::replay_lds_total(dims->dk, ring->L, 0) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
               "ring length L=%d at dk=%d exceeds the 64 KiB LDS staging budget", ring->L, dims->dk);
   GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
   gdn::ReplayArgs a{};

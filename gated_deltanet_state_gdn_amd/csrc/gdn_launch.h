@@ -64,14 +64,18 @@ struct PrefillArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeArgs& a, int state_dt, int D, hipStream_t s);
-hipError_t launch_replay(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
+hipError_t launch_replay(const ReplayArgs& a, int state_dt, int D, float* ws, hipStream_t s);
 hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
 hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s);
 
-// Total LDS (static + dynamic) of one replay workgroup; launches need <= 64 KiB.
-size_t replay_lds_total(int state_dt, int D, int L, int T);
+// Largest LDS footprint of the replay kernels for this shape; launches need <= 64 KiB.
+size_t replay_lds_total(int D, int L, int T);
 constexpr size_t kMaxLds = 65536;
+
+// Workspace of gdn_replay_decode: w_t and acc_t (dv floats each) per
+// (sequence, value head, window position).
+size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D);
 
 // Workspace of the chunked prefill: per (chunk slot, value head) the inverse
 // T, the causal decay-weighted Q K^T, gamma and beta of one chunk.

@@ -164,17 +164,26 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
  *   ckpt   checkpoint pool; slot_map[b] selects the slot of row b
  *   ring   the ring; T must satisfy 1 <= T <= ring->L
  *   out    [B, T, Hv, dv] out_dtype
+ *   workspace  device scratch of at least gdn_replay_workspace_bytes() bytes,
+ *          256-byte aligned, owned by the caller, not read before it is
+ *          written (it carries per-unit vectors between the kernels of one
+ *          call); calls that share a workspace must not overlap.
  * Per (sequence, value head): if count + T > L, every committed entry is
  * first folded into the checkpoint (one rounding) and the ring emptied
  * (start += count mod L, count = 0); then the T new entries are appended at
  * ring indices (start + count + t) mod L and count += T; window position t
  * outputs scale * S_t^T q_t where S_t is the checkpoint advanced over the
- * first count_before + t + 1 live entries (computed without writing it). */
+ * first count_before + t + 1 live entries (computed without writing it).
+ * L and T are limited by a 64 KiB LDS staging budget:
+ * 4 ((L+T)(2 dk + 6) + T (dk + 1) + (L+T)^2 + 3 (L+T) T) bytes (at dk = 128,
+ * L = 16 allows every T <= 16). */
+size_t gdn_replay_workspace_bytes(const gdn_dims* dims, int32_t B, int32_t T);
 gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q,
                              const void* k, const void* v, gdn_dtype in_dtype,
                              const gdn_gates* gates, const gdn_pool* ckpt,
                              const int32_t* slot_map, const gdn_ring* ring, void* out,
-                             gdn_dtype out_dtype, void* stream);
+                             gdn_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Fold every committed ring entry of the mapped slots into their checkpoints
  * (one rounding each) and empty their rings.  After it, the checkpoint is the

@@ -110,12 +110,12 @@ def _ring(L_=16, n=8, dtype=gdn.GDN_BF16, k=FAKE, count=FAKE):
     return bd.gdn_ring(k, FAKE, FAKE, FAKE, FAKE, count, n, L_, dtype)
 
 
-def _replay(L, B=4, T=1, ring=None, pool=None, dims=None, in_dt=gdn.GDN_BF16):
+def _replay(L, B=4, T=1, ring=None, pool=None, dims=None, in_dt=gdn.GDN_BF16, ws=FAKE, wsb=1 << 30):
     ring = _ring() if ring is None else ring
     pool = _pool() if pool is None else pool
     dims = _dims() if dims is None else dims
     return L.gdn_replay_decode(ctypes.byref(dims), B, T, FAKE, FAKE, FAKE, in_dt, ctypes.byref(_gates()),
-                               ctypes.byref(pool), FAKE, ctypes.byref(ring), FAKE, gdn.GDN_F32, None)
+                               ctypes.byref(pool), FAKE, ctypes.byref(ring), FAKE, gdn.GDN_F32, ws, wsb, None)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -129,6 +129,9 @@ def _replay(L, B=4, T=1, ring=None, pool=None, dims=None, in_dt=gdn.GDN_BF16):
     (dict(ring=_ring(n=7)), gdn.GDN_EINVAL),                        # ring slots != pool slots
     (dict(ring=_ring(k=None)), gdn.GDN_EINVAL),
     (dict(ring=_ring(count=FAKE + 2)), gdn.GDN_EINVAL),
+    (dict(ws=None), gdn.GDN_EINVAL),
+    (dict(ws=FAKE + 16), gdn.GDN_EINVAL),                           # 256-byte alignment
+    (dict(wsb=4 * 32 * 1 * 2 * 128 * 4 - 1), gdn.GDN_EINVAL),       # B * Hv * T * 2 * dv floats needed
 ])
 def test_replay_validation(L, case, expect):
     if expect == gdn.GDN_OK:
