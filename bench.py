@@ -262,6 +262,18 @@ def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
     return res
 
 
+def bench_copy(torch, nbytes=1 << 30, reps=4):
+    """A plain device-to-device copy of known size (the counter calibration for HBM traffic)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed_launches(torch, lambda i: dst.copy_(src), reps, 2)
+    res = {"bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+           "GB_per_s": round(2 * nbytes / (t["mean_launch_ms"] * 1e-3) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 def cpu_baseline(gen, seconds=12.0):
     """The CPU oracle on a bounded sample of the headline workload, one thread."""
@@ -300,8 +312,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default=None, help="run one row only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
-                                                    "prefill_<dt>")
+    ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
+                                                    "prefill_<dt> | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -320,16 +332,20 @@ def main():
     gdn.lib()
 
     if args.only:
-        kind, dt, *rest = args.only.split("_")
-        if kind == "decode":
-            r = bench_decode(torch, gdn, gen, int(rest[0][1:]) if rest else 256, dt, args.steps, args.warmup)
-        elif kind == "replay":
-            r = bench_replay(torch, gdn, gen, 512, dt, int(rest[0][1:]) if rest else 1, 2)
-        elif kind == "prefill":
-            r = bench_prefill(torch, gdn, gen, dt, max(args.steps // 8, 2))
-        else:
-            raise SystemExit(f"unknown row {args.only}")
-        print(json.dumps({"row": args.only, **r}))
+        for row in args.only.split(","):
+            kind, *rest = row.split("_")
+            if kind == "decode":
+                r = bench_decode(torch, gdn, gen, int(rest[1][1:]) if len(rest) > 1 else 256, rest[0], args.steps,
+                                 args.warmup)
+            elif kind == "replay":
+                r = bench_replay(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 1, 2)
+            elif kind == "prefill":
+                r = bench_prefill(torch, gdn, gen, rest[0], max(args.steps // 8, 2))
+            elif kind == "copy":
+                r = bench_copy(torch)
+            else:
+                raise SystemExit(f"unknown row {row}")
+            print(json.dumps({"row": row, **r}), flush=True)
         return
 
     log(f"headline: decode B=256 fp32 state, {args.warmup} warmup + {args.steps} timed steps")
