@@ -41,17 +41,7 @@ template <int SDT, int D>
 using ReplayGeom = TileGeom<SDT, D, GDN_REPLAY_WAVES>;
 
 constexpr int kStageRows = 16;  // entry rows staged per batch of loads
-constexpr int kPrepThreads = 256;
 constexpr int kStreamTB = 4;    // window positions reduced per pass over the tile
-
-// Dynamic LDS of the prep kernel (floats): entries k, v [E][D+1] (E = L + T),
-// window queries [T][D+1], gates (g, beta, prefix G, spare) [E] each, Gram
-// matrix [E][E], key / query products [E][T], coefficients c and e^G c
-// [T][E] each.
-__host__ __device__ inline size_t replay_prep_lds_bytes(int D, int L, int T) {
-  const size_t E = (size_t)L + (size_t)T;
-  return (2 * E * (D + 1) + (size_t)T * (D + 1) + 4 * E + E * E + 3 * E * T) * sizeof(float);
-}
 
 // Dynamic LDS of the fold kernel (floats): committed entries k, v [L][D+1], exp(g) and beta [L].
 __host__ __device__ inline size_t replay_fold_lds_bytes(int D, int L) {
@@ -178,93 +168,249 @@ gdn_replay_fold_kernel(const ReplayArgs P) {
 }
 
 // ---------------------------------------------------------------- prep
+// One wave per unit.  Loads are issued in two independent rounds: the window
+// rows (which need only the row index) together with the slot, then the
+// unit's whole ring block in ring order, its gates and its pointers (which
+// need only the slot); the live entries are picked out of the block in LDS.
+// Keys and values stay packed (input dtype) in LDS and are widened on use.
+template <int EB>
+struct PackedRow {
+  // element c of a packed row (EB = 4: f32 words; EB = 2: bf16 / f16 pairs)
+  __device__ __forceinline__ static float get(const uint32_t* row, int c, int dt) {
+    if constexpr (EB == 4) {
+      return __uint_as_float(row[c]);
+    } else {
+      const uint32_t w = row[c >> 1];
+      const uint32_t h16 = (c & 1) ? (w >> 16) : (w & 0xffffu);
+      return dt == GDN_BF16 ? bf16_bits_to_f32(h16) : f16_bits_to_f32(h16);
+    }
+  }
+};
+
+// One 16 x 16 tile of X Y^T over D columns on MFMA, X and Y packed rows in
+// LDS (row stride ldw words); rows at or beyond nx / ny read as zero.  Lane l
+// supplies X[l % 16][k-block l / 16] and Y[l % 16][same block]; element r of
+// the result is (4 (l / 16) + r, l % 16).  16-bit rows use the gfx950
+// 16x16x32 bf16 / f16 instructions (products of two 16-bit values are exact in
+// FP32), f32 rows the 16x16x4 f32 one.
 template <int D, int EB>
-__global__ void __launch_bounds__(kPrepThreads) gdn_replay_prep_kernel(const ReplayArgs P, float* __restrict__ ws) {
-  constexpr int NTH = kPrepThreads, NW = NTH / 64;
-  constexpr int LDE = D + 1;  // padded rows: the split dot products hit distinct banks
-  using Stager = RowStager<D, kStageRows, NTH, EB>;
-  extern __shared__ float s_dyn[];
+__device__ __forceinline__ f32x4 tile_xyt(const uint32_t* X, int nx, const uint32_t* Y, int ny, int ldw, int dt,
+                                          int lane) {
+  const int i = lane & 15, kb = lane >> 4;
+  const bool xv = i < nx, yv = i < ny;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (EB == 2) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int s = 0; s < (D + 31) / 32; ++s) {
+      const int w0 = 16 * s + 4 * kb;  // word of element 32 s + 8 kb; words past D / 2 read as zero
+      const bool kv = w0 < D / 2;
+      u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (xv && kv) a[w] = X[i * ldw + w0 + w];
+        if (yv && kv) b[w] = Y[i * ldw + w0 + w];
+      }
+      if (dt == GDN_BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                     0, 0, 0);
+    }
+  } else {
+#pragma unroll 8
+    for (int s = 0; s < D / 4; ++s) {
+      const float a = xv ? __uint_as_float(X[i * ldw + 4 * s + kb]) : 0.f;
+      const float b = yv ? __uint_as_float(Y[i * ldw + 4 * s + kb]) : 0.f;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// Dynamic LDS of the prep kernel: packed keys and values [E][D * EB / 4 + 1]
+// words each (E = L + T), packed window queries [T][...], then floats: gates
+// (g, beta, prefix G) [E] each, Gram matrix [E][E], key / query products
+// [E][T], coefficients c and e^G c [T][E] each.
+__host__ __device__ inline size_t replay_prep_words(int D, int EB, int L, int T) {
+  const size_t E = (size_t)L + (size_t)T, row = (size_t)D * EB / 4 + 1;
+  return 2 * E * row + (size_t)T * row + 3 * E + E * E + 3 * E * T;
+}
+__host__ __device__ inline size_t replay_prep_lds_bytes(int D, int L, int T) {
+  return replay_prep_words(D, 4, L, T) * sizeof(float);  // the f32-input size bounds both
+}
+
+template <int D, int EB>
+__global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P, float* __restrict__ ws) {
+  constexpr int VE = 16 / EB;             // elements per 16-byte load
+  constexpr int CPR = D / VE;             // 16-byte loads per row
+  constexpr int LDW = D * EB / 4 + 1;     // LDS words per packed row (+1: bank spread)
+  constexpr int RB = (64 / CPR) > 0 ? 64 / CPR : 1;  // rows per wave-wide load round
+  static_assert(64 % CPR == 0, "a wave covers whole rows");
+  using Row = PackedRow<EB>;
+  extern __shared__ uint32_t s_words[];
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
   const int T = P.T, L = R.L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int b = blockIdx.x / p.Hv;
   const int h = blockIdx.x - b * p.Hv;
   const int hk = h / (p.Hv / p.Hk);
+  const int E = L + T;
+  uint32_t* e_k = s_words;                  // [E][LDW] live order: committed, then window
+  uint32_t* e_v = e_k + E * LDW;            // [E][LDW]
+  uint32_t* e_q = e_v + E * LDW;            // [T][LDW]
+  float* e_g = reinterpret_cast<float*>(e_q + T * LDW);  // [E]
+  float* e_b = e_g + E;                     // [E]
+  float* e_G = e_b + E;                     // [E]
+  float* s_gram = e_G + E;                  // [E][E]
+  float* s_kq = s_gram + E * E;             // [E][T]
+  float* s_c = s_kq + E * T;                // [T][E]
+  float* s_ec = s_c + T * E;                // [T][E]
+
+  const int lr = lane / CPR, lc = (lane - lr * CPR) * VE;  // this lane's row offset and column in a round
+  const char* kin = static_cast<const char*>(p.k);
+  const char* vin = static_cast<const char*>(p.v);
+  const char* qin = static_cast<const char*>(p.q);
+
+  // Batches of 4 load rounds (RB rows each) through registers; `rowptr(r)`
+  // gives the global address of row r, `dst(r)` its LDS row (or null to skip).
+  auto load_batch = [&](int r0, int nrows, auto rowptr, u32x4 (&x)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (r0 + u) * RB + lr;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (r < nrows) z = *reinterpret_cast<const u32x4*>(rowptr(r) + lc * EB);
+      x[u] = z;
+    }
+  };
+  auto commit_batch = [&](int r0, int nrows, auto dst, const u32x4 (&x)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (r0 + u) * RB + lr;
+      uint32_t* d = (r < nrows) ? dst(r) : nullptr;
+      if (d != nullptr) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) d[lc * EB / 4 + w] = x[u][w];
+      }
+    }
+  };
+  auto win_k = [&](int t) { return kin + (((int64_t)b * T + t) * p.Hk + hk) * D * EB; };
+  auto win_v = [&](int t) { return vin + (((int64_t)b * T + t) * p.Hv + h) * D * EB; };
+  auto win_q = [&](int t) { return qin + (((int64_t)b * T + t) * p.Hk + hk) * D * EB; };
+
+  // ---- round 1: the slot, the first window rows and the window gate inputs
   const int slot = p.slot_map[b];
-  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // the stream kernel writes the zeros
+  u32x4 wk[4], wv[4], wq[4];
+  load_batch(0, T, win_k, wk);
+  load_batch(0, T, win_v, wv);
+  load_batch(0, T, win_q, wq);
+  float ga = 0.f, gb = 0.f;
+  if (lane < T) {
+    const int64_t gi = ((int64_t)b * T + lane) * p.Hv + h;
+    ga = load_elem(p.a, gi, p.in_dt);
+    gb = load_elem(p.b, gi, p.in_dt);
+  }
+  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
+
+  // ---- round 2: the unit's whole ring block (ring order), its gates and pointers
+  const int64_t ring_e = unit * L;
+  const char* rk = static_cast<const char*>(R.k) + ring_e * D * EB;
+  const char* rv = static_cast<const char*>(R.v) + ring_e * D * EB;
+  auto ring_k = [&](int j) { return rk + (int64_t)j * D * EB; };
+  auto ring_v = [&](int j) { return rv + (int64_t)j * D * EB; };
+  u32x4 xk[4], xv[4];
+  load_batch(0, L, ring_k, xk);
+  load_batch(0, L, ring_v, xv);
+  float rg = 0.f, rb = 0.f;
+  if (lane < L) {
+    rg = R.g[ring_e + lane];
+    rb = R.beta[ring_e + lane];
+  }
   const RingPos rp = ring_pos(R, unit);
   const int st = rp.st;
   const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
 
-  const int E = L + T;
-  float* e_k = s_dyn;               // [E][LDE]
-  float* e_v = e_k + E * LDE;       // [E][LDE]
-  float* e_q = e_v + E * LDE;       // [T][LDE]
-  float* e_g = e_q + T * LDE;       // [E] g
-  float* e_b = e_g + E;             // [E] beta
-  float* e_G = e_b + E;             // [E] prefix sums of g
-  float* s_gram = e_G + 2 * E;      // [E][E] (one spare gate row before it)
-  float* s_kq = s_gram + E * E;     // [E][T]
-  float* s_c = s_kq + E * T;        // [T][E]
-  float* s_ec = s_c + T * E;        // [T][E]
-
-  const int64_t ring_e = unit * L;
-  for (int t = tid; t < cnt + T; t += NTH) {
-    if (t < cnt) {
-      const int j = (st + t) % L;
-      e_g[t] = R.g[ring_e + j];
-      e_b[t] = R.beta[ring_e + j];
-    } else {
-      const int64_t gi = ((int64_t)b * T + (t - cnt)) * p.Hv + h;
-      e_g[t] = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
-      e_b[t] = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+  // ---- commit in live order: committed entries 0..cnt-1, then the window
+  auto live_k = [&](int j) -> uint32_t* {  // ring index j -> its live row, if live
+    const int live = (j - st + L) % L;
+    return live < cnt ? e_k + live * LDW : nullptr;
+  };
+  auto live_v = [&](int j) -> uint32_t* {
+    const int live = (j - st + L) % L;
+    return live < cnt ? e_v + live * LDW : nullptr;
+  };
+  auto wdst_k = [&](int t) -> uint32_t* { return e_k + (cnt + t) * LDW; };
+  auto wdst_v = [&](int t) -> uint32_t* { return e_v + (cnt + t) * LDW; };
+  auto wdst_q = [&](int t) -> uint32_t* { return e_q + t * LDW; };
+  commit_batch(0, T, wdst_k, wk);
+  commit_batch(0, T, wdst_v, wv);
+  commit_batch(0, T, wdst_q, wq);
+  commit_batch(0, L, live_k, xk);
+  commit_batch(0, L, live_v, xv);
+  for (int r0 = 4; r0 * RB < T; r0 += 4) {  // longer windows
+    load_batch(r0, T, win_k, wk);
+    load_batch(r0, T, win_v, wv);
+    load_batch(r0, T, win_q, wq);
+    commit_batch(r0, T, wdst_k, wk);
+    commit_batch(r0, T, wdst_v, wv);
+    commit_batch(r0, T, wdst_q, wq);
+  }
+  for (int r0 = 4; r0 * RB < L; r0 += 4) {  // longer rings
+    load_batch(r0, L, ring_k, xk);
+    load_batch(r0, L, ring_v, xv);
+    commit_batch(r0, L, live_k, xk);
+    commit_batch(r0, L, live_v, xv);
+  }
+  // gates in live order: committed from the ring block, the window from its inputs
+  if (lane < L) {
+    const int live = (lane - st + L) % L;
+    if (live < cnt) {
+      e_g[live] = rg;
+      e_b[live] = rb;
     }
   }
-  for (int r0s = 0; r0s < cnt; r0s += kStageRows) {  // committed entries
-    Stager sk, sv;
-    auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
-    const int nr = min(kStageRows, cnt - r0s);
-    sk.issue(R.k, nr, ring_row);
-    sv.issue(R.v, nr, ring_row);
-    sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
-    sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
-  }
-  for (int t0s = 0; t0s < T; t0s += kStageRows) {  // the window's keys, values and queries
-    Stager sk, sv, sq;
-    const int nr = min(kStageRows, T - t0s);
-    auto key_row = [&](int t) { return (((int64_t)b * T + t0s + t) * p.Hk + hk) * D; };
-    sk.issue(p.k, nr, key_row);
-    sv.issue(p.v, nr, [&](int t) { return (((int64_t)b * T + t0s + t) * p.Hv + h) * D; });
-    sq.issue(p.q, nr, key_row);
-    sk.commit(e_k + (cnt + t0s) * LDE, LDE, p.in_dt, nr);
-    sv.commit(e_v + (cnt + t0s) * LDE, LDE, p.in_dt, nr);
-    sq.commit(e_q + t0s * LDE, LDE, p.in_dt, nr);
-  }
-  // append the window to the ring (raw input bytes); the slots written were
-  // not live, so nothing staged above is overwritten
-  const int base = (st + cnt) % L;
-  for (int i = tid; i < T * D; i += NTH) {
-    const int t = i / D, c = i - t * D;
-    const int64_t j = ring_e + (base + t) % L;
-    copy_elem(R.k, j * D + c, p.k, (((int64_t)b * T + t) * p.Hk + hk) * D + c, p.in_dt);
-    copy_elem(R.v, j * D + c, p.v, (((int64_t)b * T + t) * p.Hv + h) * D + c, p.in_dt);
+  float wg = 0.f, wbeta = 0.f;
+  if (lane < T) {
+    wg = gate_g(ga, p.A_log[h], p.dt_bias[h]);
+    wbeta = sigmoid_f(gb);
+    e_g[cnt + lane] = wg;
+    e_b[cnt + lane] = wbeta;
   }
   __syncthreads();
-  for (int t = tid; t < T; t += NTH) {  // gates as fp32
-    const int64_t j = ring_e + (base + t) % L;
-    R.g[j] = e_g[cnt + t];
-    R.beta[j] = e_b[cnt + t];
-  }
-  if (tid == 0) {
-    R.start[unit] = st;
-    R.count[unit] = cnt + T;
+
+  // ---- append the window to the ring (raw input bytes) and move the pointers
+  const int base = (st + cnt) % L;
+  {
+    const char* kin2 = static_cast<const char*>(p.k);
+    for (int x = lane; x < T * CPR; x += 64) {
+      const int t = x / CPR, c = (x - t * CPR) * VE;
+      const int64_t j = ring_e + (base + t) % L;
+      const int64_t ko = ((((int64_t)b * T + t) * p.Hk + hk) * D + c) * EB;
+      const int64_t vo = ((((int64_t)b * T + t) * p.Hv + h) * D + c) * EB;
+      *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (j * D + c) * EB) =
+          *reinterpret_cast<const u32x4*>(kin2 + ko);
+      *reinterpret_cast<u32x4*>(static_cast<char*>(R.v) + (j * D + c) * EB) =
+          *reinterpret_cast<const u32x4*>(vin + vo);
+    }
+    if (lane < T) {
+      const int64_t j = ring_e + (base + lane) % L;
+      R.g[j] = wg;
+      R.beta[j] = wbeta;
+    }
+    if (lane == 0) {
+      R.start[unit] = st;
+      R.count[unit] = cnt + T;
+    }
   }
 
-  const int n_all = cnt + T;  // live entries of the last window position (<= L)
-  if (wave == 0) {            // prefix sums of g over the live entries
+  // ---- prefix sums of g over the live entries
+  const int n_all = cnt + T;
+  {
     float x = (lane < n_all) ? e_g[lane] : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -273,49 +419,38 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_replay_prep_kernel(const Rep
     }
     if (lane < n_all) e_G[lane] = x;
   }
-  // Gram matrix (upper triangle) and key / query products, four lanes per dot product
-  const int n_gram = n_all * (n_all - 1) / 2;
-  const int n_dots = n_gram + n_all * T;
-  for (int base4 = 0; base4 < n_dots * 4; base4 += NTH) {
-    const int task = (base4 + tid) >> 2, part = tid & 3;
-    const bool act = task < n_dots;
-    const float* x0 = e_k;
-    const float* x1 = e_k;
-    float* dst = nullptr;
-    if (act) {
-      if (task < n_gram) {  // pair (i, j), i < j, row-major over the upper triangle
-        int i = 0, rem = task;
-        while (rem >= n_all - 1 - i) {
-          rem -= n_all - 1 - i;
-          ++i;
+  // ---- Gram matrix of the live keys and key / query products, 16 x 16 MFMA tiles
+  {
+    const int nt = (n_all + 15) >> 4, qt = (T + 15) >> 4;
+    const int i4 = 4 * (lane >> 4), jc = lane & 15;
+    for (int I = 0; I < nt; ++I) {
+      for (int J = I; J < nt; ++J) {
+        const f32x4 g = tile_xyt<D, EB>(e_k + 16 * I * LDW, n_all - 16 * I, e_k + 16 * J * LDW, n_all - 16 * J, LDW,
+                                        p.in_dt, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * I + i4 + r, j = 16 * J + jc;
+          if (i < n_all && j < n_all) s_gram[i * E + j] = g[r];
         }
-        const int j = i + 1 + rem;
-        x0 = e_k + i * LDE;
-        x1 = e_k + j * LDE;
-        dst = s_gram + i * E + j;
-      } else {
-        const int y = task - n_gram, i = y / T, t = y - i * T;
-        x0 = e_k + i * LDE;
-        x1 = e_q + t * LDE;
-        dst = s_kq + i * T + t;
+      }
+      for (int J = 0; J < qt; ++J) {
+        const f32x4 g = tile_xyt<D, EB>(e_k + 16 * I * LDW, n_all - 16 * I, e_q + 16 * J * LDW, T - 16 * J, LDW,
+                                        p.in_dt, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * I + i4 + r, t = 16 * J + jc;
+          if (i < n_all && t < T) s_kq[i * T + t] = g[r];
+        }
       }
     }
-    float acc = 0.f;
-    if (act) {
-#pragma unroll 8
-      for (int c = part; c < D; c += 4) acc = fmaf(x0[c], x1[c], acc);
-    }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    if (act && part == 0) *dst = acc;
   }
   __syncthreads();
 
-  // back substitution for the coefficients of each window position (one wave each)
-  for (int t = wave; t < T; t += NW) {
-    const int e_last = cnt + t;  // last live entry of position t
+  // ---- back substitution for each window position: lane j holds the residual of live entry j
+  for (int t = 0; t < T; ++t) {
+    const int e_last = cnt + t;
     const float Gn = e_G[e_last];
-    const int j = lane;  // lane j holds the residual of live entry j
+    const int j = lane;
     const bool live = j <= e_last;
     const float Gj = live ? e_G[j] : 0.f;
     float r = live ? expf(Gn - Gj) * s_kq[j * T + t] : 0.f;
@@ -333,16 +468,16 @@ __global__ void __launch_bounds__(kPrepThreads) gdn_replay_prep_kernel(const Rep
     }
   }
   __syncthreads();
-  // w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j and acc_t = sum_j c_j v_j, to the workspace
+  // ---- w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j and acc_t = sum_j c_j v_j, to the workspace
   float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
-  for (int x = tid; x < T * D; x += NTH) {
+  for (int x = lane; x < T * D; x += 64) {
     const int t = x / D, c = x - t * D;
     const int e_last = cnt + t;
-    float w = expf(e_G[e_last]) * e_q[t * LDE + c];
+    float w = expf(e_G[e_last]) * Row::get(e_q + t * LDW, c, p.in_dt);
     float acc = 0.f;
     for (int jj = 0; jj <= e_last; ++jj) {
-      w = fmaf(-s_ec[t * E + jj], e_k[jj * LDE + c], w);
-      acc = fmaf(s_c[t * E + jj], e_v[jj * LDE + c], acc);
+      w = fmaf(-s_ec[t * E + jj], Row::get(e_k + jj * LDW, c, p.in_dt), w);
+      acc = fmaf(s_c[t * E + jj], Row::get(e_v + jj * LDW, c, p.in_dt), acc);
     }
     wsu[(2 * t) * D + c] = w;
     wsu[(2 * t + 1) * D + c] = acc;
@@ -466,11 +601,12 @@ static hipError_t launch_replay_t(const ReplayArgs& a, float* ws, hipStream_t s)
   hipError_t e = f32_in ? launch_fold<SDT, D, 4>(a, s) : launch_fold<SDT, D, 2>(a, s);
   if (e != hipSuccess || a.T == 0) return e;
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
-  const size_t lds = replay_prep_lds_bytes(D, a.ring.L, a.T);
   if (f32_in)
-    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 4>), dim3(grid), dim3(kPrepThreads), lds, s, a, ws);
+    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 4>), dim3(grid), dim3(64),
+                       replay_prep_words(D, 4, a.ring.L, a.T) * sizeof(float), s, a, ws);
   else
-    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 2>), dim3(grid), dim3(kPrepThreads), lds, s, a, ws);
+    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 2>), dim3(grid), dim3(64),
+                       replay_prep_words(D, 2, a.ring.L, a.T) * sizeof(float), s, a, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds_w = (size_t)a.T * D * sizeof(float);

@@ -29,7 +29,8 @@ class ReplayCase:
         self.num_slots, self.in_dt = num_slots, in_dt
         self.slot_map = gen.slot_permutation(cid, num_slots)[:B]
         self.ckpt_d, states = poisoned_pool(num_slots, Hv, D, D, sdt, [int(s) for s in self.slot_map], cid)
-        self.ring_d = gdn.new_ring(num_slots, Hv, L, D, D, {"bf16": torch.bfloat16, "f32": torch.float32}[in_dt], DEV)
+        self.ring_d = gdn.new_ring(num_slots, Hv, L, D, D, {"bf16": torch.bfloat16, "f32": torch.float32,
+                                                           "f16": torch.float16}[in_dt], DEV)
         self.rows = list(range(B)) if sample is None else list(sample)
         # oracle: mini pool / ring over the sampled rows' slots, local slot i = sample row i
         self.ref_ckpt = states[self.rows]
@@ -115,6 +116,19 @@ def test_replay_spec_windows_with_rollback(sdt):
         c.check_state(f"step {step}")
         c.rollback(step, gen.rejected_counts(40, step, c.B, 2))
         c.check_state(f"rollback {step}")
+    c.flush()
+    c.check_state("flush")
+
+
+@pytest.mark.parametrize("in_dt", ["f32", "f16"])
+@pytest.mark.parametrize("D", [16, 64])
+def test_replay_input_dtypes(in_dt, D):
+    """fp32 and fp16 inputs (rings of the same dtype), L = 6, windows of 2 with rollback, over folds."""
+    c = ReplayCase(45 + D, 4, 1, 2, D, 6, "f32", 6, in_dt=in_dt)
+    for step in range(7):
+        c.step(step, 2, a_shift=-2.0)
+        c.check_state(f"step {step}")
+        c.rollback(step, gen.rejected_counts(45, step, c.B, 1))
     c.flush()
     c.check_state("flush")
 
