@@ -20,11 +20,14 @@
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
-// Launch tuning: waves per workgroup, and streaming (non-temporal) state
-// access for fp32 / 16-bit states (measured: +7% for fp32 tiles, -1..-5% for
-// 16-bit ones).
+// Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles,
+// 2 for 16-bit ones, which then carry as many bytes per lane), and streaming
+// (non-temporal) state access (+7% for fp32 tiles, no gain for 16-bit ones).
 #ifndef GDN_DECODE_WAVES
 #define GDN_DECODE_WAVES 4
+#endif
+#ifndef GDN_DECODE_WAVES_16
+#define GDN_DECODE_WAVES_16 2
 #endif
 #ifndef GDN_DECODE_NT_F32
 #define GDN_DECODE_NT_F32 1
@@ -36,7 +39,7 @@
 namespace gdn {
 
 template <int SDT, int D>
-using DecodeGeom = TileGeom<SDT, D, GDN_DECODE_WAVES>;
+using DecodeGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_DECODE_WAVES : GDN_DECODE_WAVES_16>;
 
 template <int SDT, int D, bool NT>
 __global__ void __launch_bounds__((DecodeGeom<SDT, D>::NW * 64))
@@ -121,6 +124,15 @@ gdn_decode_kernel(const DecodeArgs p) {
   }
   __syncthreads();
 
+  // Keep only the packed tile live across the barrier: without this the
+  // compiler reuses the widened values of the first pass (twice the VGPRs for
+  // a 16-bit tile, half the tiles in flight per CU).
+  if constexpr (SDT != GDN_F32) {
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+      for (int w = 0; w < IO::WORDS; ++w) asm volatile("" : "+v"(raw[pp][w]));
+  }
   const float kq = s_kq;
   float delta[VEC];
 #pragma unroll

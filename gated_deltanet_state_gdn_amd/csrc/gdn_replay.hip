@@ -34,11 +34,14 @@
 #ifndef GDN_REPLAY_WAVES
 #define GDN_REPLAY_WAVES 4
 #endif
+#ifndef GDN_REPLAY_WAVES_16
+#define GDN_REPLAY_WAVES_16 2
+#endif
 
 namespace gdn {
 
 template <int SDT, int D>
-using ReplayGeom = TileGeom<SDT, D, GDN_REPLAY_WAVES>;
+using ReplayGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_REPLAY_WAVES : GDN_REPLAY_WAVES_16>;
 
 constexpr int kStageRows = 16;  // entry rows staged per batch of loads
 constexpr int kStreamTB = 4;    // window positions reduced per pass over the tile
