@@ -11,7 +11,8 @@ the fraction of the 8 TB/s HBM peak are reported beside it.
 
 Also measured in the same run (under "rows"): bf16/fp16-state decode, the
 ReplaySSM-style replay decode (ring of 16, standard and 5-token verify
-windows) and the chunked prefill of 4 packed sequences, each with its own
+windows), the speculative window that keeps one state per position (the
+baseline replay replaces) and the chunked prefill of 4 packed sequences, each with its own
 roofline object.  Inputs are seeded synthetic data (workloads/gen.py).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--only ROW] [--no-rows] [--no-cpu]
@@ -63,6 +64,14 @@ def replay_step_bytes(B, sdt, n_before, T, L, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
     appended = B * T * replay_entry_bytes(ib, Hk, Hv, d)             # new entries written
     inputs = B * T * (2 * Hk * d + Hv * d + 2 * Hv) * ib + 2 * Hv * 4 + B * 4 + 2 * B * 4
     return state + entries + appended + inputs + B * T * Hv * d * ob
+
+
+def spec_bytes(B, sdt, T, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
+    """Algorithmic bytes of one speculative window that keeps every state: the source read once, T
+    destination states written, inputs, gates, slot tables and outputs."""
+    state = B * Hv * d * d * SB[sdt] * (1 + T)
+    inputs = B * T * (2 * Hk * d + Hv * d + 2 * Hv) * ib + 2 * Hv * 4 + B * (1 + T) * 4
+    return state + inputs + B * T * Hv * d * ob
 
 
 def prefill_bytes(lengths, sdt, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
@@ -223,6 +232,47 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
     return res
 
 
+def bench_spec(torch, gdn, gen, B, sdt, T, reps, cid=4):
+    """Speculative window of T tokens keeping one state per position (source + T destinations per row)."""
+    import numpy as np
+    dev = "cuda"
+    num_slots = B * (T + 1)
+    perm = gen.slot_permutation(cid, num_slots)
+    src, dst = perm[:B].copy(), perm[B:].reshape(B, T).copy()
+    pool = torch.zeros((num_slots, HV, D, D), dtype={"f32": torch.float32, "bf16": torch.bfloat16,
+                                                     "f16": torch.float16}[sdt], device=dev)
+    for i in range(0, B, 64):
+        sl = src[i:i + 64]
+        pool[torch.as_tensor(sl.astype(np.int64), device=dev)] = gen.to_torch(
+            gen.pool_slots(cid, sl, HV, D, D, sdt), dev)
+    A_log, dt_bias = gen.head_params(cid, HV)
+    A_d, dt_d = gen.to_torch(A_log, dev), gen.to_torch(dt_bias, dev)
+    src_d, dst_d = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    ins = []
+    for s in range(2):
+        inp = gen.token_inputs(cid, s, (B, T), HK, HV, D, D, "bf16")
+        ins.append([gen.to_torch(inp[x], dev) for x in "qkvab"])
+    out = torch.empty((B, T, HV, D), dtype=torch.bfloat16, device=dev)
+
+    def fn(i):
+        q, k, v, a, b = ins[i % 2]
+        gdn.gdn_spec_decode(q, k, v, a, b, A_d, dt_d, pool, src_d, dst_d, out=out)
+
+    t = timed_launches(torch, fn, reps, 2)
+    nbytes = spec_bytes(B, sdt, T)
+    ms = t["span_ms"] / reps
+    res = {
+        "B": B, "state": sdt, "T": T, "ms_per_step": round(ms, 5), "mean_launch_us": round(t["mean_launch_ms"] * 1e3, 2),
+        "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "bytes_per_step": nbytes, "state_MiB": round(num_slots * HV * D * D * SB[sdt] / 2 ** 20, 1),
+    }
+    src_files = ["gdn_spec.hip", "gdn_device.h"]
+    res["roofline"] = roofline_bw(nbytes, t["mean_launch_ms"], traffic_for(f"spec_{sdt}_B{B}_T{T}", src_files))
+    del pool, ins, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
     import numpy as np
     dev = "cuda"
@@ -313,7 +363,7 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
-                                                    "prefill_<dt> | copy")
+                                                    "spec_<dt>_T<t> | prefill_<dt> | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -339,6 +389,9 @@ def main():
                                  args.warmup)
             elif kind == "replay":
                 r = bench_replay(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 1, 2)
+            elif kind == "spec":
+                r = bench_spec(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 5,
+                               max(args.steps // 4, 4))
             elif kind == "prefill":
                 r = bench_prefill(torch, gdn, gen, rest[0], max(args.steps // 8, 2))
             elif kind == "copy":
@@ -359,6 +412,9 @@ def main():
         for dt, T, cyc in (("f32", 1, 4), ("bf16", 1, 4), ("f32", 5, 8)):
             log(f"row: replay B=512 {dt} checkpoint T={T}")
             rows[f"replay_{dt}_B512_T{T}"] = bench_replay(torch, gdn, gen, 512, dt, T, cyc)
+        for dt in ("f32", "bf16"):
+            log(f"row: speculative window B=512 T=5 {dt} state, one state per position")
+            rows[f"spec_{dt}_B512_T5"] = bench_spec(torch, gdn, gen, 512, dt, 5, 16)
         for dt in ("f32", "bf16"):
             log(f"row: chunked prefill {dt} state")
             rows[f"prefill_{dt}"] = bench_prefill(torch, gdn, gen, dt, 8)

@@ -20,7 +20,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
 
 # every symbol include/gdn.h declares
 EXPORTS = (
-    "gdn_decode_step", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
+    "gdn_decode_step", "gdn_spec_decode", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
     "gdn_replay_decode",
     "gdn_replay_flush", "gdn_replay_rollback", "gdn_status_string", "gdn_last_error",
 )
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
                       ctypes.POINTER(gdn_ring))
     sig = {
         "gdn_decode_step": (INT, [pd, I32, P, P, P, INT, pg, pp, P, P, INT, P]),
+        "gdn_spec_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, P, P, INT, P]),
         "gdn_chunk_prefill_workspace_bytes": (SZ, [pd, I32, I64, I32]),
         "gdn_chunk_prefill": (INT, [pd, I32, P, I64, I32, P, P, P, INT, pg, pp, P, P, INT, P, SZ, P]),
         "gdn_replay_workspace_bytes": (SZ, [pd, I32, I32]),
@@ -170,6 +171,23 @@ def gdn_decode_step(q, k, v, a, b, A_log, dt_bias, pool, slot_map, out=None, out
     _check(lib().gdn_decode_step(ctypes.byref(dims), B, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
                                  ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(pool)),
                                  _ptr(slot_map), _ptr(out), dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def gdn_spec_decode(q, k, v, a, b, A_log, dt_bias, pool, src_slots, dst_slots, out=None, out_dtype=None,
+                    scale=None, stream=None):
+    """Speculative window keeping every state; q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, b [B, T, Hv];
+    src_slots int32 [B]; dst_slots int32 [B, T] (device)."""
+    torch = _torch()
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+    dims = _dims(Hk, Hv, dk, dv, scale)
+    _check(lib().gdn_spec_decode(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
+                                 ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(pool)),
+                                 _ptr(src_slots), _ptr(dst_slots), _ptr(out), dtype_code(out.dtype),
+                                 _stream(stream)))
     return out
 
 

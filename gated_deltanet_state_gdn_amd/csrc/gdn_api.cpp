@@ -151,6 +151,33 @@ gdn_status gdn_decode_step(const gdn_dims* dims, int32_t B, const void* q, const
   return launched(gdn::launch_decode(a, state->dtype, dims->dk, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_spec_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k, const void* v,
+                           gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* state,
+                           const int32_t* src_slots, const int32_t* dst_slots, void* out, gdn_dtype out_dtype,
+                           void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE(T >= 1, GDN_EINVAL, "window T=%d must be >= 1", T);
+  GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
+  GDN_REQUIRE((int64_t)B * T * dims->num_v_heads * dims->dv <= INT64_MAX / 8, GDN_EINVAL, "B * T too large");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  GDN_REQUIRE(gdn::spec_lds_bytes(dims->dk, T) <= gdn::kSpecMaxLds, GDN_EUNSUPPORTED,
+              "window T=%d at dk=%d exceeds the 48 KiB LDS staging budget", T, dims->dk);
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_io(q, k, v, in_dtype, out, out_dtype));
+  GDN_TRY(check_gates(gates, in_dtype));
+  GDN_TRY(check_pool(state, "state"));
+  GDN_REQUIRE(src_slots != nullptr && aligned(src_slots, 4), GDN_EINVAL, "src_slots is NULL or misaligned");
+  GDN_REQUIRE(dst_slots != nullptr && aligned(dst_slots, 4), GDN_EINVAL, "dst_slots is NULL or misaligned");
+  gdn::SpecArgs a{};
+  a.d = gdn::DecodeArgs{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, state->base, src_slots, out,
+                        state->num_slots, B, dims->num_k_heads, dims->num_v_heads, (int32_t)in_dtype,
+                        (int32_t)out_dtype, eff_scale(dims)};
+  a.dst_slots = dst_slots;
+  a.T = T;
+  return launched(gdn::launch_spec(a, state->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_dims* dims, int32_t N, int64_t total_tokens, int32_t chunk) {
   if (dims == nullptr || N <= 0 || total_tokens <= 0 || chunk != 64 || dims->num_v_heads < 1) return 0;
   return gdn::prefill_workspace_bytes(N, total_tokens, dims->num_v_heads);

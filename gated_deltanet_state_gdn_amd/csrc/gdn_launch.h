@@ -43,6 +43,12 @@ struct ReplayArgs {
   const int32_t* num_rejected;
 };
 
+struct SpecArgs {
+  DecodeArgs d;  // q, k, v, a, b laid out [B, T, H, d]; slot_map holds the source slots
+  const int32_t* dst_slots;  // [B, T]
+  int32_t T;
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -68,6 +74,11 @@ hipError_t launch_replay(const ReplayArgs& a, int state_dt, int D, float* ws, hi
 hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
 hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s);
+hipError_t launch_spec(const SpecArgs& a, int state_dt, int D, hipStream_t s);
+
+// Dynamic LDS of the speculative-decode kernel; launches need <= kSpecMaxLds.
+size_t spec_lds_bytes(int D, int T);
+constexpr size_t kSpecMaxLds = 49152;
 
 // Largest LDS footprint of the replay kernels for this shape; launches need <= 64 KiB.
 size_t replay_lds_total(int D, int L, int T);

@@ -125,6 +125,30 @@ gdn_status gdn_decode_step(const gdn_dims* dims, int32_t B, const void* q, const
                            const gdn_pool* state, const int32_t* slot_map, void* out,
                            gdn_dtype out_dtype, void* stream);
 
+/* Speculative decode keeping one full state per window position, the
+ * per-draft-token baseline (vLLM PR #52191 page, implementation item 3: the
+ * speculative update kernel with separate source and destination state
+ * pointers; AREX ReplaySSM article, "bottleneck" section: (1 + num_spec)
+ * full states written per step whether or not drafts are accepted).
+ *   q, k       [B, T, Hk, dk] in_dtype
+ *   v          [B, T, Hv, dv] in_dtype
+ *   gates      a, b [B, T, Hv]
+ *   state      pool holding both the sources and the destinations
+ *   src_slots  device int32 [B]: the state row b starts from (outside the
+ *              pool: padded row, zero outputs, nothing written)
+ *   dst_slots  device int32 [B, T]: where the state after position t is
+ *              written, rounded once (outside the pool: that write is skipped)
+ *   out        [B, T, Hv, dv] out_dtype; position t reads the state after
+ *              its own token, before rounding.
+ * The chain between positions carries the unrounded FP32 state.  Destination
+ * slots must be distinct and must not be any row's source slot in the same
+ * call (not checked).  1 <= T and 4 T (3 dk + 3) bytes <= 48 KiB (T <= 31 at
+ * dk = 128), else GDN_EUNSUPPORTED. */
+gdn_status gdn_spec_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                           const void* v, gdn_dtype in_dtype, const gdn_gates* gates,
+                           const gdn_pool* state, const int32_t* src_slots,
+                           const int32_t* dst_slots, void* out, gdn_dtype out_dtype, void* stream);
+
 /* Chunked prefill of N packed variable-length sequences (vLLM PR #52191 page,
  * implementation items 3-4: the chunked inter-chunk recurrence; chunk states
  * are scaled by exp(g_last); FP32 buffers, slot read at the start and written

@@ -106,6 +106,30 @@ def test_decode_validation(L, case, expect):
         assert gdn.gdn_last_error() == ""
 
 
+def _spec(L, B=4, T=5, dims=None, src=FAKE, dst=FAKE, pool=None):
+    dims = _dims() if dims is None else dims
+    pool = _pool() if pool is None else pool
+    return L.gdn_spec_decode(ctypes.byref(dims), B, T, FAKE, FAKE, FAKE, gdn.GDN_BF16, ctypes.byref(_gates()),
+                             ctypes.byref(pool), src, dst, FAKE, gdn.GDN_F32, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(T=0), gdn.GDN_EINVAL),
+    (dict(B=-2), gdn.GDN_EINVAL),
+    (dict(T=32), gdn.GDN_EUNSUPPORTED),                             # 48 KiB staging budget at dk = 128
+    (dict(T=31, B=0), gdn.GDN_OK),                                  # fits; B = 0 keeps it a no-op
+    (dict(T=64, dims=bd.gdn_dims(2, 2, 32, 32, 0.0), B=0), gdn.GDN_OK),
+    (dict(src=None), gdn.GDN_EINVAL),
+    (dict(dst=None), gdn.GDN_EINVAL),
+    (dict(dst=FAKE + 2), gdn.GDN_EINVAL),
+    (dict(pool=bd.gdn_pool(FAKE + 4, gdn.GDN_F32, 8)), gdn.GDN_EINVAL),
+    (dict(dims=bd.gdn_dims(16, 32, 128, 64, 0.0)), gdn.GDN_EUNSUPPORTED),
+])
+def test_spec_validation(L, case, expect):
+    st = _spec(L, **case)
+    assert st == expect, gdn.gdn_last_error()
+
+
 def _ring(L_=16, n=8, dtype=gdn.GDN_BF16, k=FAKE, count=FAKE):
     return bd.gdn_ring(k, FAKE, FAKE, FAKE, FAKE, count, n, L_, dtype)
 
