@@ -312,6 +312,28 @@ def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
     return res
 
 
+def bench_copy_blocks(torch, gdn, reps=8, P=16, slots=64, jobs=32):
+    """Prefix-caching state-block copy: `jobs` slot copies in each of P layer-state tensors of
+    [slots, 32, 128, 128] fp32 (2 MiB slots)."""
+    import numpy as np
+    dev = "cuda"
+    tensors = [torch.empty((slots, HV, D, D), dtype=torch.float32, device=dev).normal_() for _ in range(P)]
+    perm = np.random.default_rng(48109).permutation(slots).astype(np.int32)
+    src_d = torch.from_numpy(perm[:jobs].copy()).to(dev)
+    dst_d = torch.from_numpy(perm[jobs:2 * jobs].copy()).to(dev)
+    table = gdn.make_state_table(tensors, dev)
+    t = timed_launches(torch, lambda i: gdn.gdn_copy_state_blocks(tensors, src_d, dst_d, table=table), reps, 2)
+    slot_bytes = HV * D * D * 4
+    nbytes = 2 * jobs * P * slot_bytes + P * 24 + 2 * jobs * 4
+    ms = t["span_ms"] / reps
+    res = {"P": P, "jobs": jobs, "slot_MiB": slot_bytes / 2 ** 20, "ms_per_call": round(ms, 4),
+           "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes,
+           "roofline": roofline_bw(nbytes, t["mean_launch_ms"], None)}
+    del tensors
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy(torch, nbytes=1 << 30, reps=4):
     """A plain device-to-device copy of known size (the counter calibration for HBM traffic)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -363,7 +385,7 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
-                                                    "spec_<dt>_T<t> | prefill_<dt> | copy")
+                                                    "spec_<dt>_T<t> | prefill_<dt> | blockcopy | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -396,6 +418,8 @@ def main():
                 r = bench_prefill(torch, gdn, gen, rest[0], max(args.steps // 8, 2))
             elif kind == "copy":
                 r = bench_copy(torch)
+            elif kind == "blockcopy":
+                r = bench_copy_blocks(torch, gdn)
             else:
                 raise SystemExit(f"unknown row {row}")
             print(json.dumps({"row": row, **r}), flush=True)
@@ -415,6 +439,8 @@ def main():
         for dt in ("f32", "bf16"):
             log(f"row: speculative window B=512 T=5 {dt} state, one state per position")
             rows[f"spec_{dt}_B512_T5"] = bench_spec(torch, gdn, gen, 512, dt, 5, 16)
+        log("row: state-block copy, 32 jobs x 16 tensors of 2 MiB slots")
+        rows["state_block_copy"] = bench_copy_blocks(torch, gdn)
         for dt in ("f32", "bf16"):
             log(f"row: chunked prefill {dt} state")
             rows[f"prefill_{dt}"] = bench_prefill(torch, gdn, gen, dt, 8)

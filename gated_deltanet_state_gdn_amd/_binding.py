@@ -20,10 +20,14 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
 
 # every symbol include/gdn.h declares
 EXPORTS = (
-    "gdn_decode_step", "gdn_spec_decode", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
+    "gdn_decode_step", "gdn_spec_decode", "gdn_copy_state_blocks", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
     "gdn_replay_decode",
     "gdn_replay_flush", "gdn_replay_rollback", "gdn_status_string", "gdn_last_error",
 )
+
+
+class gdn_state_ref(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64), ("num_slots", ctypes.c_uint64)]
 
 
 class gdn_dims(ctypes.Structure):
@@ -69,6 +73,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "gdn_decode_step": (INT, [pd, I32, P, P, P, INT, pg, pp, P, P, INT, P]),
         "gdn_spec_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, P, P, INT, P]),
+        "gdn_copy_state_blocks": (INT, [P, I32, ctypes.c_uint64, P, P, I32, P]),
         "gdn_chunk_prefill_workspace_bytes": (SZ, [pd, I32, I64, I32]),
         "gdn_chunk_prefill": (INT, [pd, I32, P, I64, I32, P, P, P, INT, pg, pp, P, P, INT, P, SZ, P]),
         "gdn_replay_workspace_bytes": (SZ, [pd, I32, I32]),
@@ -189,6 +194,49 @@ def gdn_spec_decode(q, k, v, a, b, A_log, dt_bias, pool, src_slots, dst_slots, o
                                  _ptr(src_slots), _ptr(dst_slots), _ptr(out), dtype_code(out.dtype),
                                  _stream(stream)))
     return out
+
+
+def state_refs_bytes(entries) -> bytes:
+    """Pack (base address, slot bytes, slot count) triples as the gdn_state_ref table: three
+    little-endian unsigned 64-bit fields each, so an address at or above 2^63 keeps every bit."""
+    import struct
+    return b"".join(struct.pack("<QQQ", int(b), int(sb), int(n)) for b, sb, n in entries)
+
+
+def make_state_table(tensors, device):
+    """Device gdn_state_ref table for contiguous [num_slots, ...] device tensors:
+    returns (table uint8 tensor, P, max_slot_bytes).  Reusable while the tensors live."""
+    torch = _torch()
+    entries = []
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError("state tensors must be contiguous")
+        entries.append((t.data_ptr(), t[0].numel() * t.element_size(), t.shape[0]))
+    host_table = torch.frombuffer(bytearray(state_refs_bytes(entries)), dtype=torch.uint8)
+    return host_table.to(device), len(entries), max((e[1] for e in entries), default=0)
+
+
+def gdn_copy_state_blocks(tensors, src_slots, dst_slots, stream=None, table=None):
+    """Copy slot src_slots[j] over dst_slots[j] in every tensor (each contiguous [num_slots, ...] on the
+    device); src_slots, dst_slots int32 [n] (device).  `table` may be a prebuilt make_state_table()
+    result for the same tensors; otherwise one is built and uploaded on the copy's stream."""
+    torch = _torch()
+    n = int(src_slots.shape[0])
+    if len(tensors) == 0 or n == 0:
+        return
+    if table is None:
+        if stream is None or isinstance(stream, torch.cuda.Stream):
+            # upload on the stream the copy runs on, so the kernel is ordered after it
+            with torch.cuda.stream(stream or torch.cuda.current_stream()):
+                table = make_state_table(tensors, src_slots.device)
+            if stream is not None:
+                table[0].record_stream(stream)
+        else:  # a raw stream handle: finish the upload before enqueueing
+            table = make_state_table(tensors, src_slots.device)
+            torch.cuda.current_stream().synchronize()
+    dev_table, P, max_bytes = table
+    _check(lib().gdn_copy_state_blocks(_ptr(dev_table), P, max_bytes, _ptr(src_slots), _ptr(dst_slots), n,
+                                       _stream(stream)))
 
 
 def gdn_chunk_prefill_workspace_bytes(Hk, Hv, dk, dv, N, total_tokens, chunk=64) -> int:

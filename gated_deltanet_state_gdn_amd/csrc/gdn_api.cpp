@@ -178,6 +178,20 @@ gdn_status gdn_spec_decode(const gdn_dims* dims, int32_t B, int32_t T, const voi
   return launched(gdn::launch_spec(a, state->dtype, dims->dk, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_copy_state_blocks(const gdn_state_ref* refs, int32_t P, uint64_t max_slot_bytes,
+                                 const int32_t* src_slots, const int32_t* dst_slots, int32_t n, void* stream) {
+  GDN_REQUIRE(P >= 0 && P <= 65535, GDN_EINVAL, "P=%d out of [0, 65535]", P);
+  GDN_REQUIRE(n >= 0 && n <= 65535, GDN_EINVAL, "n=%d out of [0, 65535]", n);
+  if (P == 0 || n == 0) return ok();  // nothing is read or written
+  GDN_REQUIRE(refs != nullptr && aligned(refs, 8), GDN_EINVAL, "refs is NULL or not 8-byte aligned");
+  GDN_REQUIRE(src_slots != nullptr && aligned(src_slots, 4), GDN_EINVAL, "src_slots is NULL or misaligned");
+  GDN_REQUIRE(dst_slots != nullptr && aligned(dst_slots, 4), GDN_EINVAL, "dst_slots is NULL or misaligned");
+  GDN_REQUIRE(max_slot_bytes >= 1 && (max_slot_bytes + gdn::kCopyChunk - 1) / gdn::kCopyChunk <= INT32_MAX,
+              GDN_EINVAL, "max_slot_bytes=%llu out of [1, 2^31 chunks]", (unsigned long long)max_slot_bytes);
+  gdn::CopyArgs a{refs, src_slots, dst_slots, P, n};
+  return launched(gdn::launch_copy_blocks(a, max_slot_bytes, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_dims* dims, int32_t N, int64_t total_tokens, int32_t chunk) {
   if (dims == nullptr || N <= 0 || total_tokens <= 0 || chunk != 64 || dims->num_v_heads < 1) return 0;
   return gdn::prefill_workspace_bytes(N, total_tokens, dims->num_v_heads);

@@ -49,6 +49,15 @@ struct SpecArgs {
   int32_t T;
 };
 
+struct CopyArgs {
+  const gdn_state_ref* refs;  // [P], device
+  const int32_t* src;         // [n], device
+  const int32_t* dst;         // [n], device
+  int32_t P, n;
+};
+constexpr int kCopyThreads = 256;
+constexpr uint64_t kCopyChunk = 64 * 1024;  // bytes of a slot per workgroup
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -75,6 +84,7 @@ hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStre
 hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s);
 hipError_t launch_spec(const SpecArgs& a, int state_dt, int D, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyArgs& a, uint64_t max_slot_bytes, hipStream_t s);
 
 // Dynamic LDS of the speculative-decode kernel; launches need <= kSpecMaxLds.
 size_t spec_lds_bytes(int D, int T);

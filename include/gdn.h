@@ -221,6 +221,35 @@ gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckp
 gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* slot_map,
                                const int32_t* num_rejected, const gdn_ring* ring, void* stream);
 
+/* One state tensor for gdn_copy_state_blocks: slot i occupies bytes
+ * [base + i * slot_bytes, base + (i + 1) * slot_bytes).  `base` is a device
+ * address kept as an unsigned 64-bit value (vLLM PR #48109 page, the XPU
+ * state-pointer fix: device addresses may exceed 2^63, so a signed 64-bit
+ * table loses or wraps them). */
+typedef struct {
+  uint64_t base;
+  uint64_t slot_bytes;
+  uint64_t num_slots;
+} gdn_state_ref;
+
+/* State-block copy for prefix caching (vLLM PR #48109 page, implementation
+ * section: the state-copy kernel of --mamba-cache-mode align, driven by
+ * tables of state base addresses).  For every job j < n and every tensor
+ * p < P: slot src_slots[j] of refs[p] is copied byte for byte over slot
+ * dst_slots[j] of refs[p].
+ *   refs            device array of P gdn_state_ref, 8-byte aligned
+ *   max_slot_bytes  host value >= every refs[p].slot_bytes (sizes the grid;
+ *                   at most 2^31 * 64 KiB)
+ *   src_slots, dst_slots  device int32 [n]
+ * A job whose source or destination is outside [0, num_slots) of a tensor
+ * is skipped for that tensor.  A slot must not be both a source and a
+ * destination in one call, and destinations must be distinct (not checked).
+ * Any base, slot size and alignment is accepted (16-byte-aligned ones copy
+ * with vector accesses).  P <= 65535 and n <= 65535. */
+gdn_status gdn_copy_state_blocks(const gdn_state_ref* refs, int32_t P, uint64_t max_slot_bytes,
+                                 const int32_t* src_slots, const int32_t* dst_slots, int32_t n,
+                                 void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 

@@ -24,6 +24,11 @@ Sources (cited by section; see the design doc for the full reading list):
               of the latest state-building inputs, folded into S0 every L
               steps; other steps compute outputs from S0 and the ring without
               materialising the state; the read-out vector q is not cached).
+  [PR48109]   vLLM PR #48109 summary page (prhub.com.cn), the XPU state
+              pointer fix: its implementation section (the state-block copy
+              kernel behind --mamba-cache-mode align, fed by tables of state
+              base addresses) and risk section (the addresses need all 64
+              bits).
   [GDN]       The gated delta rule as published by Yang, Kautz and
               Hatamizadeh ("Gated Delta Networks: Improving Mamba2 with Delta
               Rule", 2024): S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T
@@ -58,6 +63,7 @@ __all__ = [
     "round_to_format", "to_storage", "widen", "dtype_of", "softplus", "sigmoid", "gates",
     "decay_update", "readout", "gdn_token", "ref_gdn", "decode_step", "chunk_prefill",
     "Ring", "new_ring", "replay_decode", "replay_flush", "replay_rollback", "spec_decode",
+    "copy_state_blocks",
 ]
 
 # ---------------------------------------------------------------------------
@@ -451,3 +457,29 @@ def spec_decode(pool, src_slots, dst_slots, q, k, v, a, b, A_log, dt_bias, scale
                 if _slot_ok(dst, num_slots):
                     pool[dst, h] = to_storage(S, sdt)
     return pool, o
+
+
+# ---------------------------------------------------------------------------
+# state-block copy for prefix caching ([PR48109] implementation section: the
+# state-copy kernel of --mamba-cache-mode align copies whole state blocks of
+# every state tensor named by its pointer table)
+# ---------------------------------------------------------------------------
+def copy_state_blocks(tensors, src_slots, dst_slots):
+    """Copy slot src_slots[j] over slot dst_slots[j] in every tensor, byte for byte.
+
+    tensors: list of arrays [num_slots, ...] (any dtype, slots may differ per
+    tensor).  A job whose source or destination is outside a tensor's slots
+    is skipped for that tensor.  Sources are read from the tensors as they
+    were before the call.  Returns new arrays.
+    """
+    out = []
+    for t in tensors:
+        before = np.array(t, copy=True)
+        after = np.array(t, copy=True)
+        n = before.shape[0]
+        for s, d in zip(src_slots, dst_slots):
+            s, d = int(s), int(d)
+            if _slot_ok(s, n) and _slot_ok(d, n):
+                after[d] = before[s]
+        out.append(after)
+    return out

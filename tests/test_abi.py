@@ -203,3 +203,33 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         bd.lib()
+
+
+def test_state_refs_keep_every_address_bit():
+    """Addresses at and above 2^63 pack as unsigned 64-bit values, bit for bit."""
+    import struct
+    addrs = [0, (1 << 63) - 8, 1 << 63, (1 << 64) - 8]
+    raw = gdn.state_refs_bytes([(a, 2 << 20, 1024) for a in addrs])
+    assert len(raw) == 24 * len(addrs) == len(addrs) * ctypes.sizeof(bd.gdn_state_ref)
+    for i, a in enumerate(addrs):
+        assert struct.unpack_from("<QQQ", raw, 24 * i) == (a, 2 << 20, 1024)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(P=-1), gdn.GDN_EINVAL),
+    (dict(P=65536), gdn.GDN_EINVAL),
+    (dict(n=-1), gdn.GDN_EINVAL),
+    (dict(refs=None), gdn.GDN_EINVAL),
+    (dict(refs=FAKE + 4), gdn.GDN_EINVAL),
+    (dict(src=None), gdn.GDN_EINVAL),
+    (dict(dst=FAKE + 1), gdn.GDN_EINVAL),
+    (dict(max_bytes=0), gdn.GDN_EINVAL),
+    (dict(max_bytes=(1 << 31) * 65536 + 1), gdn.GDN_EINVAL),
+    (dict(n=0), gdn.GDN_OK),
+    (dict(P=0), gdn.GDN_OK),
+])
+def test_copy_state_blocks_validation(L, case, expect):
+    c = dict(refs=FAKE, P=4, max_bytes=1 << 21, src=FAKE, dst=FAKE, n=8)
+    c.update(case)
+    st = L.gdn_copy_state_blocks(c["refs"], c["P"], c["max_bytes"], c["src"], c["dst"], c["n"], None)
+    assert st == expect, gdn.gdn_last_error()

@@ -438,3 +438,24 @@ def test_spec_decode_chain_equals_sequential_decode():
         for bi in range(2):
             np.testing.assert_allclose(O.widen(pool2[dst[bi, t]]), O.widen(ref[src[bi]]), rtol=1e-6, atol=1e-7)
     assert np.array_equal(pool2[:2], pool[:2]) and np.array_equal(pool2[10:], pool[10:])
+
+
+def test_copy_state_blocks_worked_example():
+    """Whole slots move byte for byte; out-of-range jobs are skipped per tensor; sources are the
+    pre-call contents (a chain 0 -> 1, 1 -> 2 moves the old slot 1, not the new one)."""
+    a = np.arange(4 * 3, dtype=np.int32).reshape(4, 3)          # slots 0..3
+    b = np.arange(2 * 2, dtype=np.uint16).reshape(2, 2) + 100   # slots 0..1 only
+    out_a, out_b = O.copy_state_blocks([a, b], [0, 1, 3], [1, 2, 0])
+    assert out_a.tolist() == [[9, 10, 11], [0, 1, 2], [3, 4, 5], [9, 10, 11]]
+    # in b, only the job 0 -> 1 is in range (slots 2 and 3 do not exist)
+    assert out_b.tolist() == [[100, 101], [100, 101]]
+    # inputs are not modified
+    assert a.tolist()[1] == [3, 4, 5] and b.tolist()[1] == [102, 103]
+
+
+def test_copy_state_blocks_keeps_bit_patterns():
+    """NaN payloads and signed zeros survive the copy (it is a byte copy, not a value copy)."""
+    x = np.array([[np.nan, -0.0], [1.0, 2.0]], np.float32)
+    x.view(np.uint32)[0, 0] = 0x7FC0DEAD
+    (y,) = O.copy_state_blocks([x], [0], [1])
+    assert np.array_equal(y.view(np.uint32)[1], x.view(np.uint32)[0])
