@@ -56,10 +56,15 @@ def replay_entry_bytes(ib=2, Hk=HK, Hv=HV, d=D):
     return (Hk * d + Hv * d) * ib + 2 * Hv * 4
 
 
-def replay_step_bytes(B, sdt, n_before, T, L, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
-    """Algorithmic bytes of one replay step of T tokens when every sequence holds n_before entries."""
+def replay_step_bytes(B, sdt, n_before, T, L, ib=2, ob=2, Hk=HK, Hv=HV, d=D, copy_dt=None):
+    """Algorithmic bytes of one replay step of T tokens when every sequence holds n_before entries.
+    With copy_dt (dual-precision checkpoint) outputs read the copy and a fold also writes it."""
     fold = n_before + T > L
-    state = B * Hv * d * d * SB[sdt] * (2 if fold else 1)
+    tile = B * Hv * d * d
+    if copy_dt is None:
+        state = tile * SB[sdt] * (2 if fold else 1)
+    else:
+        state = tile * SB[copy_dt] + (tile * (2 * SB[sdt] + SB[copy_dt]) if fold else 0)
     entries = B * n_before * replay_entry_bytes(ib, Hk, Hv, d)       # committed entries read
     appended = B * T * replay_entry_bytes(ib, Hk, Hv, d)             # new entries written
     inputs = B * T * (2 * Hk * d + Hv * d + 2 * Hv) * ib + 2 * Hv * 4 + B * 4 + 2 * B * 4
@@ -183,13 +188,19 @@ def bench_decode(torch, gdn, gen, B, sdt, steps, warmup, cid=1):
     return res
 
 
-def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
-    """Aligned rings (every sequence starts empty): 1 untimed cycle, then `cycles` timed cycles."""
+def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None):
+    """Aligned rings (every sequence starts empty): 1 untimed cycle, then `cycles` timed cycles.
+    copy_dt selects the dual-precision checkpoint (sdt is then the f32 master)."""
     dev = "cuda"
     steps_per_cycle = L // T if T > 1 else L
     slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
     ckpt = make_pool(torch, gen, cid, slot_map, sdt, dev)
     ring = gdn.new_ring(NUM_SLOTS, HV, L, D, D, torch.bfloat16, dev)
+    copy = None
+    if copy_dt is not None:
+        copy = torch.empty((NUM_SLOTS, HV, D, D), dtype={"bf16": torch.bfloat16, "f16": torch.float16}[copy_dt],
+                           device=dev)
+        gdn.gdn_replay_flush(ckpt, torch.from_numpy(slot_map).to(dev), ring, HK, read_copy=copy)
     A_log, dt_bias = gen.head_params(cid, HV)
     A_d, dt_d = gen.to_torch(A_log, dev), gen.to_torch(dt_bias, dev)
     sm = torch.from_numpy(slot_map).to(dev)
@@ -205,13 +216,13 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
 
     def fn(i):
         q, k, v, a, b = ins[i % n_in]
-        gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out, workspace=ws)
+        gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out, workspace=ws, read_copy=copy)
 
     t = timed_launches(torch, fn, n, warm)
     # byte model follows the (deterministic) per-slot count of the aligned schedule
     cnt, nbytes = 0, 0
     for i in range(warm + n):
-        b_i = replay_step_bytes(B, sdt, cnt, T, L)
+        b_i = replay_step_bytes(B, sdt, cnt, T, L, copy_dt=copy_dt)
         if cnt + T > L:
             cnt = 0
         cnt += T
@@ -219,15 +230,17 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4):
             nbytes += b_i
     ms = t["span_ms"] / n
     res = {
-        "B": B, "ckpt": sdt, "L": L, "T": T, "ms_per_step": round(ms, 5),
+        "B": B, "ckpt": sdt if copy_dt is None else f"{sdt} master + {copy_dt} read copy", "L": L, "T": T,
+        "ms_per_step": round(ms, 5),
         "mean_launch_us": round(t["mean_launch_ms"] * 1e3, 2),
         "GB_per_s": round(nbytes / n / (ms * 1e-3) / 1e9, 1), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "bytes_per_step_avg": nbytes // n,
         "vs_decode_bytes": round(nbytes / n / (T * decode_bytes(B, sdt)), 3),
     }
     src = ["gdn_replay.hip", "gdn_device.h"]
-    res["roofline"] = roofline_bw(nbytes / n, t["mean_launch_ms"], traffic_for(f"replay_{sdt}_B{B}_T{T}", src))
-    del ckpt, ring, ins, ws
+    key = f"replay_{sdt}_B{B}_T{T}" if copy_dt is None else f"replay_dual_{copy_dt}_B{B}_T{T}"
+    res["roofline"] = roofline_bw(nbytes / n, t["mean_launch_ms"], traffic_for(key, src))
+    del ckpt, ring, ins, ws, copy
     torch.cuda.empty_cache()
     return res
 
@@ -384,7 +397,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | "
+    ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | replay_dual_<dt>_T<t> | "
                                                     "spec_<dt>_T<t> | prefill_<dt> | blockcopy | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -409,6 +422,9 @@ def main():
             if kind == "decode":
                 r = bench_decode(torch, gdn, gen, int(rest[1][1:]) if len(rest) > 1 else 256, rest[0], args.steps,
                                  args.warmup)
+            elif kind == "replay" and rest[0] == "dual":
+                r = bench_replay(torch, gdn, gen, 512, "f32", int(rest[2][1:]) if len(rest) > 2 else 1, 2,
+                                 copy_dt=rest[1])
             elif kind == "replay":
                 r = bench_replay(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 1, 2)
             elif kind == "spec":
@@ -436,6 +452,8 @@ def main():
         for dt, T, cyc in (("f32", 1, 4), ("bf16", 1, 4), ("f32", 5, 8)):
             log(f"row: replay B=512 {dt} checkpoint T={T}")
             rows[f"replay_{dt}_B512_T{T}"] = bench_replay(torch, gdn, gen, 512, dt, T, cyc)
+        log("row: replay B=512 fp32 master + bf16 read copy T=1")
+        rows["replay_dual_bf16_B512_T1"] = bench_replay(torch, gdn, gen, 512, "f32", 1, 4, copy_dt="bf16")
         for dt in ("f32", "bf16"):
             log(f"row: speculative window B=512 T=5 {dt} state, one state per position")
             rows[f"spec_{dt}_B512_T5"] = bench_spec(torch, gdn, gen, 512, dt, 5, 16)

@@ -22,7 +22,8 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
 EXPORTS = (
     "gdn_decode_step", "gdn_spec_decode", "gdn_copy_state_blocks", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
     "gdn_replay_decode",
-    "gdn_replay_flush", "gdn_replay_rollback", "gdn_status_string", "gdn_last_error",
+    "gdn_replay_flush", "gdn_replay_rollback", "gdn_replay_decode_dual", "gdn_replay_flush_dual",
+    "gdn_status_string", "gdn_last_error",
 )
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "gdn_replay_workspace_bytes": (SZ, [pd, I32, I32]),
         "gdn_replay_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P, SZ, P]),
         "gdn_replay_flush": (INT, [pd, I32, pp, P, pr, P]),
+        "gdn_replay_decode_dual": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, pp, P, pr, P, INT, P, SZ, P]),
+        "gdn_replay_flush_dual": (INT, [pd, I32, pp, pp, P, pr, P]),
         "gdn_replay_rollback": (INT, [pd, I32, P, P, pr, P]),
         "gdn_status_string": (ctypes.c_char_p, [INT]),
         "gdn_last_error": (ctypes.c_char_p, []),
@@ -272,8 +275,9 @@ def gdn_replay_workspace_bytes(Hk, Hv, dk, dv, B, T) -> int:
 
 
 def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring, out=None, out_dtype=None,
-                      workspace=None, scale=None, stream=None):
-    """Replay step of T tokens; q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, b [B, T, Hv]."""
+                      workspace=None, scale=None, stream=None, read_copy=None):
+    """Replay step of T tokens; q, k [B, T, Hk, dk]; v [B, T, Hv, dv]; a, b [B, T, Hv].
+    With `read_copy` (a bf16/f16 pool beside the f32 `ckpt`), the dual-precision variant runs."""
     torch = _torch()
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
@@ -286,20 +290,29 @@ def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dims = _dims(Hk, Hv, dk, dv, scale)
     rs = ring.c_struct()
-    _check(lib().gdn_replay_decode(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
-                                   ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(ckpt)),
-                                   _ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype), ws_ptr,
-                                   ws_bytes, _stream(stream)))
+    head = (ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
+            ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(ckpt)))
+    tail = (_ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype), ws_ptr, ws_bytes, _stream(stream))
+    if read_copy is None:
+        _check(lib().gdn_replay_decode(*head, *tail))
+    else:
+        _check(lib().gdn_replay_decode_dual(*head, ctypes.byref(_pool(read_copy)), *tail))
     return out
 
 
-def gdn_replay_flush(ckpt, slot_map, ring: Ring, Hk, stream=None):
-    """Fold every committed ring entry of the mapped slots into their checkpoints."""
+def gdn_replay_flush(ckpt, slot_map, ring: Ring, Hk, stream=None, read_copy=None):
+    """Fold every committed ring entry of the mapped slots into their checkpoints (with `read_copy`:
+    the dual-precision flush, which also refreshes the copy of every mapped slot)."""
     Hv, dk, dv = ckpt.shape[1], ckpt.shape[2], ckpt.shape[3]
     dims = _dims(Hk, Hv, dk, dv, None)
     rs = ring.c_struct()
-    _check(lib().gdn_replay_flush(ctypes.byref(dims), int(slot_map.shape[0]), ctypes.byref(_pool(ckpt)),
-                                  _ptr(slot_map), ctypes.byref(rs), _stream(stream)))
+    if read_copy is None:
+        _check(lib().gdn_replay_flush(ctypes.byref(dims), int(slot_map.shape[0]), ctypes.byref(_pool(ckpt)),
+                                      _ptr(slot_map), ctypes.byref(rs), _stream(stream)))
+    else:
+        _check(lib().gdn_replay_flush_dual(ctypes.byref(dims), int(slot_map.shape[0]), ctypes.byref(_pool(ckpt)),
+                                           ctypes.byref(_pool(read_copy)), _ptr(slot_map), ctypes.byref(rs),
+                                           _stream(stream)))
 
 
 def gdn_replay_rollback(slot_map, num_rejected, ring: Ring, Hk, dk, stream=None):

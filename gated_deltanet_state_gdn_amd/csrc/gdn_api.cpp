@@ -8,6 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "gdn.h"
 #include "gdn_launch.h"
@@ -118,6 +121,47 @@ gdn::RingArgs ring_args(const gdn_ring* r) {
 }
 
 }  // namespace
+
+namespace gdn {
+
+hipError_t device_cus(int* cus) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    it = cache.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *cus = it->second;
+  return hipSuccess;
+}
+
+hipError_t resident_blocks(const void* kernel, int block, size_t lds, int* per_cu) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_tuple(dev, kernel, block, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds);
+    if (e != hipSuccess) return e;
+    it = cache.emplace(key, n > 0 ? n : 1).first;
+  }
+  *per_cu = it->second;
+  return hipSuccess;
+}
+
+}  // namespace gdn
 
 extern "C" {
 
@@ -233,10 +277,23 @@ size_t gdn_replay_workspace_bytes(const gdn_dims* dims, int32_t B, int32_t T) {
   return gdn::replay_workspace_bytes(B, dims->num_v_heads, T, dims->dv);
 }
 
-gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
-                             const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
-                             const int32_t* slot_map, const gdn_ring* ring, void* out, gdn_dtype out_dtype,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// A dual-precision checkpoint: an fp32 master plus a 16-bit read copy of the same slots.
+gdn_status check_dual(const gdn_pool* master, const gdn_pool* copy) {
+  GDN_REQUIRE(master->dtype == GDN_F32, GDN_EINVAL, "the dual-precision master checkpoint must be f32");
+  GDN_TRY(check_pool(copy, "read copy"));
+  GDN_REQUIRE(copy->dtype == GDN_BF16 || copy->dtype == GDN_F16, GDN_EINVAL, "the read copy must be bf16 or f16");
+  GDN_REQUIRE(copy->num_slots == master->num_slots, GDN_EINVAL, "read copy holds %lld slots, the master %lld",
+              (long long)copy->num_slots, (long long)master->num_slots);
+  GDN_REQUIRE(copy->base != master->base, GDN_EINVAL, "the read copy aliases the master");
+  return ok();
+}
+
+gdn_status replay_decode_impl(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                              const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
+                              const gdn_pool* read_copy, const int32_t* slot_map, const gdn_ring* ring, void* out,
+                              gdn_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   GDN_TRY(check_dims(dims));
   GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
   GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
@@ -247,10 +304,10 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
   GDN_TRY(check_io(q, k, v, in_dtype, out, out_dtype));
   GDN_TRY(check_gates(gates, in_dtype));
   GDN_TRY(check_pool(ckpt, "checkpoint"));
+  if (read_copy != nullptr) GDN_TRY(check_dual(ckpt, read_copy));
   GDN_TRY(check_ring(ring, in_dtype));
   GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
               (long long)ring->num_slots, (long long)ckpt->num_slots);
-  GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
   GDN_REQUIRE(gdn::replay_lds_total(dims->dk, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
               "ring length L=%d with window T=%d at dk=%d exceeds the 64 KiB LDS staging budget", ring->L, T,
               dims->dk);
@@ -266,17 +323,22 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
                         (int32_t)out_dtype, eff_scale(dims)};
   a.ring = ring_args(ring);
   a.T = T;
+  if (read_copy != nullptr) {
+    a.read_pool = read_copy->base;
+    a.read_dt = (int32_t)read_copy->dtype;
+  }
   return launched(gdn::launch_replay(a, ckpt->dtype, dims->dk, static_cast<float*>(workspace),
                                      static_cast<hipStream_t>(stream)));
 }
 
-gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt, const int32_t* slot_map,
-                            const gdn_ring* ring, void* stream) {
+gdn_status replay_flush_impl(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt, const gdn_pool* read_copy,
+                             const int32_t* slot_map, const gdn_ring* ring, void* stream) {
   GDN_TRY(check_dims(dims));
   GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
   GDN_REQUIRE((int64_t)B * dims->num_v_heads <= INT32_MAX, GDN_EINVAL, "B * Hv exceeds the grid limit");
   if (B == 0) return ok();  // nothing is read or written
   GDN_TRY(check_pool(ckpt, "checkpoint"));
+  if (read_copy != nullptr) GDN_TRY(check_dual(ckpt, read_copy));
   GDN_TRY(check_ring(ring, -1));
   GDN_REQUIRE(ring->num_slots == ckpt->num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
               (long long)ring->num_slots, (long long)ckpt->num_slots);
@@ -294,7 +356,43 @@ gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckp
   a.d.scale = eff_scale(dims);
   a.ring = ring_args(ring);
   a.T = 0;
+  if (read_copy != nullptr) {
+    a.read_pool = read_copy->base;
+    a.read_dt = (int32_t)read_copy->dtype;
+  }
   return launched(gdn::launch_replay_flush(a, ckpt->dtype, dims->dk, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                             const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
+                             const int32_t* slot_map, const gdn_ring* ring, void* out, gdn_dtype out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return replay_decode_impl(dims, B, T, q, k, v, in_dtype, gates, ckpt, nullptr, slot_map, ring, out, out_dtype,
+                            workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_replay_decode_dual(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                                  const void* v, gdn_dtype in_dtype, const gdn_gates* gates,
+                                  const gdn_pool* master, const gdn_pool* read_copy, const int32_t* slot_map,
+                                  const gdn_ring* ring, void* out, gdn_dtype out_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (B > 0) GDN_REQUIRE(read_copy != nullptr, GDN_EINVAL, "read copy is NULL");
+  return replay_decode_impl(dims, B, T, q, k, v, in_dtype, gates, master, read_copy, slot_map, ring, out,
+                            out_dtype, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt, const int32_t* slot_map,
+                            const gdn_ring* ring, void* stream) {
+  return replay_flush_impl(dims, B, ckpt, nullptr, slot_map, ring, stream);
+}
+
+gdn_status gdn_replay_flush_dual(const gdn_dims* dims, int32_t B, const gdn_pool* master,
+                                 const gdn_pool* read_copy, const int32_t* slot_map, const gdn_ring* ring,
+                                 void* stream) {
+  if (B > 0) GDN_REQUIRE(read_copy != nullptr, GDN_EINVAL, "read copy is NULL");
+  return replay_flush_impl(dims, B, master, read_copy, slot_map, ring, stream);
 }
 
 gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* slot_map, const int32_t* num_rejected,

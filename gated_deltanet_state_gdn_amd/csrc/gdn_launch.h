@@ -41,6 +41,8 @@ struct ReplayArgs {
   RingArgs ring;
   int32_t T;     // 1..L; 0 selects the flush-only kernel
   const int32_t* num_rejected;
+  void* read_pool;  // dual-precision mode: the 16-bit read copy of the fp32 checkpoint (else null)
+  int32_t read_dt;
 };
 
 struct SpecArgs {
@@ -79,6 +81,8 @@ struct PrefillArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeArgs& a, int state_dt, int D, hipStream_t s);
+// state_dt: dtype of the checkpoint pool a.d.pool; with a.read_pool set the
+// checkpoint is the fp32 master and outputs read the read_dt copy.
 hipError_t launch_replay(const ReplayArgs& a, int state_dt, int D, float* ws, hipStream_t s);
 hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStream_t s);
 hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
@@ -89,6 +93,12 @@ hipError_t launch_copy_blocks(const CopyArgs& a, uint64_t max_slot_bytes, hipStr
 // Dynamic LDS of the speculative-decode kernel; launches need <= kSpecMaxLds.
 size_t spec_lds_bytes(int D, int T);
 constexpr size_t kSpecMaxLds = 49152;
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus);
+// Workgroups of `kernel` resident on one compute unit at this block size and
+// dynamic LDS (cached per device, kernel, block and LDS size).
+hipError_t resident_blocks(const void* kernel, int block, size_t lds, int* per_cu);
 
 // Largest LDS footprint of the replay kernels for this shape; launches need <= 64 KiB.
 size_t replay_lds_total(int D, int L, int T);

@@ -37,6 +37,11 @@
 #ifndef GDN_REPLAY_WAVES_16
 #define GDN_REPLAY_WAVES_16 2
 #endif
+// waves per workgroup of the prep kernel (one unit per workgroup; 2 measured
+// best on MI355X: 1 leaves phases serial, 4 halves the units in flight)
+#ifndef GDN_REPLAY_PREP_WAVES
+#define GDN_REPLAY_PREP_WAVES 2
+#endif
 
 namespace gdn {
 
@@ -70,11 +75,20 @@ __device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t unit) {
 }
 
 // ---------------------------------------------------------------- fold
-// Also the flush (T == 0: fold whenever the ring is not empty).
-template <int SDT, int D, bool NT, int EB>
-__global__ void __launch_bounds__((ReplayGeom<SDT, D>::NW * 64))
+// Persistent: workgroup w owns units w, w + G, w + 2G, ... (G the grid size,
+// sized to the resident workgroups), checks 64 of them at a time, one per lane
+// of wave 0, and folds those that need it one after another with the whole
+// workgroup, so a step without folds costs one small check per unit.  A unit folds when count + T > L; the
+// flush (T == 0) folds every non-empty ring.  CDT >= 0 selects the
+// dual-precision checkpoint: the fp32 result is also written, rounded once,
+// to the CDT read copy (the flush then refreshes the copy of every unit).
+template <int SDT, int D>
+using FoldGeom = TileGeom<SDT, D, 4>;  // fp32 working tile: four waves for every state dtype
+
+template <int SDT, int D, bool NT, int EB, int CDT>
+__global__ void __launch_bounds__((FoldGeom<SDT, D>::NW * 64))
 gdn_replay_fold_kernel(const ReplayArgs P) {
-  using G = ReplayGeom<SDT, D>;
+  using G = FoldGeom<SDT, D>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
   constexpr int NTH = NW * 64;
   constexpr int LDE = D + 1;
@@ -84,89 +98,126 @@ gdn_replay_fold_kernel(const ReplayArgs P) {
 
   extern __shared__ float s_dyn[];
   __shared__ float s_red[2][NW][D];
+  __shared__ int s_list[64];
+  __shared__ int s_n;
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
   const int T = P.T, L = R.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / p.Hv;
-  const int h = blockIdx.x - b * p.Hv;
-  const int slot = p.slot_map[b];
-  if (slot < 0 || (int64_t)slot >= p.num_slots) return;
-  const int64_t unit = (int64_t)slot * p.Hv + h;
-  const RingPos rp = ring_pos(R, unit);
-  const int st = rp.st, cnt = rp.cnt;
-  const bool fold = (T > 0) ? (cnt + T > L) : (cnt > 0);
-  if (!fold) return;
-
-  ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D);
+  const int units = p.B * p.Hv;
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
-  float s[PASSES][VEC];
-#pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) IO::widen(IO::load_raw(tile + (r0 + pp * NW * RPW) * D + c0), s[pp]);
-
   float* e_k = s_dyn;           // [L][LDE]
   float* e_v = e_k + L * LDE;   // [L][LDE]
   float* e_a = e_v + L * LDE;   // [L] exp(g)
   float* e_b = e_a + L;         // [L] beta
-  const int64_t ring_e = unit * L;
-  for (int t = tid; t < cnt; t += NTH) {
-    const int j = (st + t) % L;
-    e_a[t] = expf(R.g[ring_e + j]);
-    e_b[t] = R.beta[ring_e + j];
-  }
-  for (int r0s = 0; r0s < cnt; r0s += kStageRows) {
-    Stager sk, sv;
-    auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
-    const int nr = min(kStageRows, cnt - r0s);
-    sk.issue(R.k, nr, ring_row);
-    sv.issue(R.v, nr, ring_row);
-    sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
-    sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
-  }
-  __syncthreads();
 
-  for (int i = 0; i < cnt; ++i) {
-    const float* ki = e_k + i * LDE;
-    float kvp[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) kvp[e] = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) {
-      const float kr = ki[r0 + pp * NW * RPW];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) kvp[e] = fmaf(s[pp][e], kr, kvp[e]);
-    }
-    float* red = s_red[i & 1][0];  // double-buffered: one barrier per entry
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) kvp[e] = xor_sum_from<LPR>(kvp[e]);
-    if (lane < LPR) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) red[wave * D + c0 + e] = kvp[e];
+  const int grid_n = gridDim.x;
+  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
+    if (wave == 0) {
+      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
+      const int x = xl < units ? (int)xl : units;
+      bool need = false;
+      if (x < units) {
+        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+        const int slot = p.slot_map[b];
+        if (slot >= 0 && (int64_t)slot < p.num_slots) {
+          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+        }
+      }
+      const uint64_t mask = __ballot(need);
+      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
+      if (lane == 0) s_n = __popcll(mask);
     }
     __syncthreads();
-    const float al = e_a[i], be = e_b[i];
-    float delta[VEC];
+    const int n_fold = s_n;
+    for (int f = 0; f < n_fold; ++f) {
+      const int x = s_list[f];
+      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+      const RingPos rp = ring_pos(R, unit);
+      const int st = rp.st, cnt = rp.cnt;
+
+      // the lane offset is made opaque per unit so that the per-pass addresses
+      // are not hoisted out of the unit loop (they would hold registers)
+      int lane_off = r0 * D + c0;
+      asm volatile("" : "+v"(lane_off));
+      ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
+      float s[PASSES][VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float kv = 0.f;
+      for (int pp = 0; pp < PASSES; ++pp) IO::widen(IO::load_raw(tile + pp * NW * RPW * D), s[pp]);
+
+      const int64_t ring_e = unit * L;
+      for (int t = tid; t < cnt; t += NTH) {
+        const int j = (st + t) % L;
+        e_a[t] = expf(R.g[ring_e + j]);
+        e_b[t] = R.beta[ring_e + j];
+      }
+      for (int r0s = 0; r0s < cnt; r0s += kStageRows) {
+        Stager sk, sv;
+        auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
+        const int nr = min(kStageRows, cnt - r0s);
+        sk.issue(R.k, nr, ring_row);
+        sv.issue(R.v, nr, ring_row);
+        sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
+        sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
+      }
+      __syncthreads();
+
+      for (int i = 0; i < cnt; ++i) {
+        const float* ki = e_k + i * LDE;
+        float kvp[VEC];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) kv += red[w * D + c0 + e];
-      delta[e] = be * (e_v[i * LDE + c0 + e] - al * kv);
+        for (int e = 0; e < VEC; ++e) kvp[e] = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+          const float kr = ki[r0 + pp * NW * RPW];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) kvp[e] = fmaf(s[pp][e], kr, kvp[e]);
+        }
+        float* red = s_red[i & 1][0];  // double-buffered: one barrier per entry
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kvp[e] = xor_sum_from<LPR>(kvp[e]);
+        if (lane < LPR) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) red[wave * D + c0 + e] = kvp[e];
+        }
+        __syncthreads();
+        const float al = e_a[i], be = e_b[i];
+        float delta[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float kv = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) kv += red[w * D + c0 + e];
+          delta[e] = be * (e_v[i * LDE + c0 + e] - al * kv);
+        }
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+          const float kr = ki[r0 + pp * NW * RPW];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr * delta[e]);
+        }
+      }
+      if (cnt > 0) {
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * NW * RPW * D, s[pp]);
+      }
+      if constexpr (CDT >= 0) {
+        using CIO = TileIO<CDT, VEC, false>;
+        uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * NW * RPW * D, s[pp]);
+      }
+      if (tid == 0) {
+        R.start[unit] = (st + cnt) % L;
+        R.count[unit] = 0;
+      }
+      __syncthreads();  // LDS staging is reused by the next unit
     }
-#pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) {
-      const float kr = ki[r0 + pp * NW * RPW];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr * delta[e]);
-    }
-  }
-#pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + (r0 + pp * NW * RPW) * D + c0, s[pp]);
-  if (tid == 0) {
-    R.start[unit] = (st + cnt) % L;
-    R.count[unit] = 0;
+    __syncthreads();  // s_list is rewritten by the next check
   }
 }
 
@@ -233,66 +284,75 @@ __device__ __forceinline__ f32x4 tile_xyt(const uint32_t* X, int nx, const uint3
   return acc;
 }
 
-// Dynamic LDS of the prep kernel: packed keys and values [E][D * EB / 4 + 1]
-// words each (E = L + T), packed window queries [T][...], then floats: gates
-// (g, beta, prefix G) [E] each, Gram matrix [E][E], key / query products
-// [E][T], coefficients c and e^G c [T][E] each.
+// Dynamic LDS of the prep kernel: packed keys and values [L][D * EB / 4 + 1]
+// words each (live entries, at most L: the committed ones then the window),
+// packed window queries [T][...], then floats: beta and prefix sums of g [L]
+// each, decay-weighted key products [L][L], key / query products [L][T],
+// coefficients c and e^G c [T][L] each.
 __host__ __device__ inline size_t replay_prep_words(int D, int EB, int L, int T) {
-  const size_t E = (size_t)L + (size_t)T, row = (size_t)D * EB / 4 + 1;
-  return 2 * E * row + (size_t)T * row + 3 * E + E * E + 3 * E * T;
+  const size_t Ls = (size_t)L, Ts = (size_t)T, row = (size_t)D * EB / 4 + 1;
+  return 2 * Ls * row + Ts * row + 2 * Ls + Ls * Ls + 3 * Ls * Ts;
 }
 __host__ __device__ inline size_t replay_prep_lds_bytes(int D, int L, int T) {
   return replay_prep_words(D, 4, L, T) * sizeof(float);  // the f32-input size bounds both
 }
 
-template <int D, int EB>
-__global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P, float* __restrict__ ws) {
+// One workgroup of NWP waves per unit.  Loads are issued in two independent
+// rounds: the window rows (which need only the row index) together with the
+// slot, then the unit's whole ring block in ring order, its gates and its
+// pointers (which need only the slot); the live entries are picked out of the
+// block into LDS.  Keys and values stay packed (input dtype) in LDS and are
+// widened on use.  Phases (one barrier each): staging and gates; the Gram
+// and key / query MFMA tiles, shared over the waves; the back substitution,
+// one wave per window position; w and acc, one thread per element.
+template <int D, int EB, int NWP>
+__global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayArgs P, float* __restrict__ ws) {
+  constexpr int NTH = NWP * 64;
   constexpr int VE = 16 / EB;             // elements per 16-byte load
   constexpr int CPR = D / VE;             // 16-byte loads per row
   constexpr int LDW = D * EB / 4 + 1;     // LDS words per packed row (+1: bank spread)
-  constexpr int RB = (64 / CPR) > 0 ? 64 / CPR : 1;  // rows per wave-wide load round
+  constexpr int RB = NTH / CPR;           // rows per workgroup-wide load round
   static_assert(64 % CPR == 0, "a wave covers whole rows");
+  constexpr int NR = 2;                   // load rounds held in registers per row kind
   using Row = PackedRow<EB>;
   extern __shared__ uint32_t s_words[];
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
   const int T = P.T, L = R.L;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / p.Hv;
   const int h = blockIdx.x - b * p.Hv;
   const int hk = h / (p.Hv / p.Hk);
-  const int E = L + T;
-  uint32_t* e_k = s_words;                  // [E][LDW] live order: committed, then window
-  uint32_t* e_v = e_k + E * LDW;            // [E][LDW]
-  uint32_t* e_q = e_v + E * LDW;            // [T][LDW]
-  float* e_g = reinterpret_cast<float*>(e_q + T * LDW);  // [E]
-  float* e_b = e_g + E;                     // [E]
-  float* e_G = e_b + E;                     // [E]
-  float* s_gram = e_G + E;                  // [E][E]
-  float* s_kq = s_gram + E * E;             // [E][T]
-  float* s_c = s_kq + E * T;                // [T][E]
-  float* s_ec = s_c + T * E;                // [T][E]
+  uint32_t* e_k = s_words;                  // [L][LDW] live order: committed, then window
+  uint32_t* e_v = e_k + L * LDW;            // [L][LDW]
+  uint32_t* e_q = e_v + L * LDW;            // [T][LDW]
+  float* e_b = reinterpret_cast<float*>(e_q + T * LDW);  // [L]
+  float* e_G = e_b + L;                     // [L]
+  float* s_F = e_G + L;                     // [L][L]
+  float* s_kq = s_F + L * L;                // [L][T]
+  float* s_c = s_kq + L * T;                // [T][L]
+  float* s_ec = s_c + T * L;                // [T][L]
 
-  const int lr = lane / CPR, lc = (lane - lr * CPR) * VE;  // this lane's row offset and column in a round
+  const int lr = tid / CPR, lc = (tid - lr * CPR) * VE;  // this thread's row offset and column in a round
   const char* kin = static_cast<const char*>(p.k);
   const char* vin = static_cast<const char*>(p.v);
   const char* qin = static_cast<const char*>(p.q);
 
-  // Batches of 4 load rounds (RB rows each) through registers; `rowptr(r)`
-  // gives the global address of row r, `dst(r)` its LDS row (or null to skip).
-  auto load_batch = [&](int r0, int nrows, auto rowptr, u32x4 (&x)[4]) {
+  // NR load rounds (RB rows each) through registers; `rowptr(r)` gives the
+  // global address of row r, `dst(r)` its LDS row (or null to skip).
+  auto load_batch = [&](int r0, int nrows, auto rowptr, u32x4 (&x)[NR]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NR; ++u) {
       const int r = (r0 + u) * RB + lr;
       u32x4 z = {0u, 0u, 0u, 0u};
       if (r < nrows) z = *reinterpret_cast<const u32x4*>(rowptr(r) + lc * EB);
       x[u] = z;
     }
   };
-  auto commit_batch = [&](int r0, int nrows, auto dst, const u32x4 (&x)[4]) {
+  auto commit_batch = [&](int r0, int nrows, auto dst, const u32x4 (&x)[NR]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NR; ++u) {
       const int r = (r0 + u) * RB + lr;
       uint32_t* d = (r < nrows) ? dst(r) : nullptr;
       if (d != nullptr) {
@@ -307,13 +367,13 @@ __global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P,
 
   // ---- round 1: the slot, the first window rows and the window gate inputs
   const int slot = p.slot_map[b];
-  u32x4 wk[4], wv[4], wq[4];
+  u32x4 wk[NR], wv[NR], wq[NR];
   load_batch(0, T, win_k, wk);
   load_batch(0, T, win_v, wv);
   load_batch(0, T, win_q, wq);
   float ga = 0.f, gb = 0.f;
-  if (lane < T) {
-    const int64_t gi = ((int64_t)b * T + lane) * p.Hv + h;
+  if (tid < T) {
+    const int64_t gi = ((int64_t)b * T + tid) * p.Hv + h;
     ga = load_elem(p.a, gi, p.in_dt);
     gb = load_elem(p.b, gi, p.in_dt);
   }
@@ -326,27 +386,27 @@ __global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P,
   const char* rv = static_cast<const char*>(R.v) + ring_e * D * EB;
   auto ring_k = [&](int j) { return rk + (int64_t)j * D * EB; };
   auto ring_v = [&](int j) { return rv + (int64_t)j * D * EB; };
-  u32x4 xk[4], xv[4];
+  u32x4 xk[NR], xv[NR];
   load_batch(0, L, ring_k, xk);
   load_batch(0, L, ring_v, xv);
   float rg = 0.f, rb = 0.f;
-  if (lane < L) {
-    rg = R.g[ring_e + lane];
-    rb = R.beta[ring_e + lane];
+  if (tid < L) {
+    rg = R.g[ring_e + tid];
+    rb = R.beta[ring_e + tid];
   }
   const RingPos rp = ring_pos(R, unit);
   const int st = rp.st;
   const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
+  const int n_all = cnt + T;           // <= L
 
   // ---- commit in live order: committed entries 0..cnt-1, then the window
-  auto live_k = [&](int j) -> uint32_t* {  // ring index j -> its live row, if live
-    const int live = (j - st + L) % L;
-    return live < cnt ? e_k + live * LDW : nullptr;
+  auto live_row = [&](uint32_t* base, int j) -> uint32_t* {  // ring index j -> its live row, if live
+    const int d = j - st;
+    const int live = d < 0 ? d + L : d;
+    return live < cnt ? base + live * LDW : nullptr;
   };
-  auto live_v = [&](int j) -> uint32_t* {
-    const int live = (j - st + L) % L;
-    return live < cnt ? e_v + live * LDW : nullptr;
-  };
+  auto live_k = [&](int j) { return live_row(e_k, j); };
+  auto live_v = [&](int j) { return live_row(e_v, j); };
   auto wdst_k = [&](int t) -> uint32_t* { return e_k + (cnt + t) * LDW; };
   auto wdst_v = [&](int t) -> uint32_t* { return e_v + (cnt + t) * LDW; };
   auto wdst_q = [&](int t) -> uint32_t* { return e_q + t * LDW; };
@@ -355,7 +415,7 @@ __global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P,
   commit_batch(0, T, wdst_q, wq);
   commit_batch(0, L, live_k, xk);
   commit_batch(0, L, live_v, xv);
-  for (int r0 = 4; r0 * RB < T; r0 += 4) {  // longer windows
+  for (int r0 = NR; r0 * RB < T; r0 += NR) {  // longer windows
     load_batch(r0, T, win_k, wk);
     load_batch(r0, T, win_v, wv);
     load_batch(r0, T, win_q, wq);
@@ -363,124 +423,131 @@ __global__ void __launch_bounds__(64) gdn_replay_prep_kernel(const ReplayArgs P,
     commit_batch(r0, T, wdst_v, wv);
     commit_batch(r0, T, wdst_q, wq);
   }
-  for (int r0 = 4; r0 * RB < L; r0 += 4) {  // longer rings
+  for (int r0 = NR; r0 * RB < L; r0 += NR) {  // longer rings
     load_batch(r0, L, ring_k, xk);
     load_batch(r0, L, ring_v, xv);
     commit_batch(r0, L, live_k, xk);
     commit_batch(r0, L, live_v, xv);
   }
-  // gates in live order: committed from the ring block, the window from its inputs
-  if (lane < L) {
-    const int live = (lane - st + L) % L;
-    if (live < cnt) {
-      e_g[live] = rg;
-      e_b[live] = rb;
-    }
-  }
+  // gates and their prefix sums in live order (wave 0): lane j takes live
+  // entry j, a committed entry from ring position (st + j) % L or window
+  // position j - cnt
   float wg = 0.f, wbeta = 0.f;
-  if (lane < T) {
+  if (tid < T) {
     wg = gate_g(ga, p.A_log[h], p.dt_bias[h]);
     wbeta = sigmoid_f(gb);
-    e_g[cnt + lane] = wg;
-    e_b[cnt + lane] = wbeta;
   }
-  __syncthreads();
-
-  // ---- append the window to the ring (raw input bytes) and move the pointers
-  const int base = (st + cnt) % L;
-  {
-    const char* kin2 = static_cast<const char*>(p.k);
-    for (int x = lane; x < T * CPR; x += 64) {
-      const int t = x / CPR, c = (x - t * CPR) * VE;
-      const int64_t j = ring_e + (base + t) % L;
-      const int64_t ko = ((((int64_t)b * T + t) * p.Hk + hk) * D + c) * EB;
-      const int64_t vo = ((((int64_t)b * T + t) * p.Hv + h) * D + c) * EB;
-      *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (j * D + c) * EB) =
-          *reinterpret_cast<const u32x4*>(kin2 + ko);
-      *reinterpret_cast<u32x4*>(static_cast<char*>(R.v) + (j * D + c) * EB) =
-          *reinterpret_cast<const u32x4*>(vin + vo);
-    }
-    if (lane < T) {
-      const int64_t j = ring_e + (base + lane) % L;
-      R.g[j] = wg;
-      R.beta[j] = wbeta;
-    }
-    if (lane == 0) {
-      R.start[unit] = st;
-      R.count[unit] = cnt + T;
-    }
-  }
-
-  // ---- prefix sums of g over the live entries
-  const int n_all = cnt + T;
-  {
-    float x = (lane < n_all) ? e_g[lane] : 0.f;
+  if (wave == 0) {
+    const int from_ring = (st + lane) % L;
+    const float g_r = __shfl(rg, from_ring, 64), b_r = __shfl(rb, from_ring, 64);
+    const int from_win = (lane - cnt) & 63;
+    const float g_w = __shfl(wg, from_win, 64), b_w = __shfl(wbeta, from_win, 64);
+    const float g = lane < cnt ? g_r : (lane < n_all ? g_w : 0.f);
+    const float be = lane < cnt ? b_r : (lane < n_all ? b_w : 0.f);
+    float x = g;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
-    if (lane < n_all) e_G[lane] = x;
+    if (lane < L) {
+      e_b[lane] = be;
+      e_G[lane] = x;
+    }
   }
-  // ---- Gram matrix of the live keys and key / query products, 16 x 16 MFMA tiles
+  __syncthreads();
+
+  // ---- append the window to the ring (raw input bytes) and move the pointers
+  const int base = (st + cnt) % L;
+  for (int x = tid; x < T * CPR; x += NTH) {
+    const int t = x / CPR, c = (x - t * CPR) * VE;
+    const int64_t j = ring_e + (base + t) % L;
+    const int64_t ko = ((((int64_t)b * T + t) * p.Hk + hk) * D + c) * EB;
+    const int64_t vo = ((((int64_t)b * T + t) * p.Hv + h) * D + c) * EB;
+    *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (j * D + c) * EB) =
+        *reinterpret_cast<const u32x4*>(kin + ko);
+    *reinterpret_cast<u32x4*>(static_cast<char*>(R.v) + (j * D + c) * EB) =
+        *reinterpret_cast<const u32x4*>(vin + vo);
+  }
+  if (tid < T) {
+    const int64_t j = ring_e + (base + tid) % L;
+    R.g[j] = wg;
+    R.beta[j] = wbeta;
+  }
+  if (tid == 0) {
+    R.start[unit] = st;
+    R.count[unit] = n_all;
+  }
+
+  // ---- decay-weighted key products s_F[i][j] = e^{G_i - G_j} k_j . k_i (j < i)
+  // and key / query products s_kq[j][t] = e^{G_{cnt+t} - G_j} k_j . q_t
+  // (j <= cnt + t), 16 x 16 MFMA tiles shared over the waves; every exponent <= 0
   {
     const int nt = (n_all + 15) >> 4, qt = (T + 15) >> 4;
+    const int n_gt = nt * (nt + 1) / 2;
     const int i4 = 4 * (lane >> 4), jc = lane & 15;
-    for (int I = 0; I < nt; ++I) {
-      for (int J = I; J < nt; ++J) {
-        const f32x4 g = tile_xyt<D, EB>(e_k + 16 * I * LDW, n_all - 16 * I, e_k + 16 * J * LDW, n_all - 16 * J, LDW,
-                                        p.in_dt, lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + i4 + r, j = 16 * J + jc;
-          if (i < n_all && j < n_all) s_gram[i * E + j] = g[r];
+    for (int job = wave; job < n_gt + nt * qt; job += NWP) {
+      int I, J;
+      const bool gram = job < n_gt;
+      if (gram) {
+        I = 0;
+        int rem = job;
+        while (rem >= nt - I) {
+          rem -= nt - I;
+          ++I;
         }
+        J = I + rem;
+      } else {
+        I = (job - n_gt) / qt;
+        J = (job - n_gt) - I * qt;
       }
-      for (int J = 0; J < qt; ++J) {
-        const f32x4 g = tile_xyt<D, EB>(e_k + 16 * I * LDW, n_all - 16 * I, e_q + 16 * J * LDW, T - 16 * J, LDW,
-                                        p.in_dt, lane);
+      const uint32_t* Y = gram ? e_k + 16 * J * LDW : e_q + 16 * J * LDW;
+      const int ny = gram ? n_all - 16 * J : T - 16 * J;
+      const f32x4 g = tile_xyt<D, EB>(e_k + 16 * I * LDW, n_all - 16 * I, Y, ny, LDW, p.in_dt, lane);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + i4 + r, t = 16 * J + jc;
-          if (i < n_all && t < T) s_kq[i * T + t] = g[r];
+      for (int r = 0; r < 4; ++r) {
+        const int a = 16 * I + i4 + r, j = 16 * J + jc;
+        if (gram) {
+          if (a < j && j < n_all) s_F[j * L + a] = expf(e_G[j] - e_G[a]) * g[r];
+        } else if (a < n_all && j < T) {
+          s_kq[a * T + j] = a <= cnt + j ? expf(e_G[cnt + j] - e_G[a]) * g[r] : 0.f;
         }
       }
     }
   }
   __syncthreads();
 
-  // ---- back substitution for each window position: lane j holds the residual of live entry j
-  for (int t = 0; t < T; ++t) {
+  // ---- back substitution, one wave per window position: lane j holds the residual of live entry j
+  for (int t = wave; t < T; t += NWP) {
     const int e_last = cnt + t;
-    const float Gn = e_G[e_last];
     const int j = lane;
     const bool live = j <= e_last;
-    const float Gj = live ? e_G[j] : 0.f;
-    float r = live ? expf(Gn - Gj) * s_kq[j * T + t] : 0.f;
+    float r = live ? s_kq[j * T + t] : 0.f;
     float cj = 0.f;
     for (int i = e_last; i >= 0; --i) {
       // c_i = beta_i * residual_i, then every earlier entry drops its term
+      const float f = j < i ? s_F[i * L + j] : 0.f;
       const float ci =
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e_b[i] * r), i));
       if (j == i) cj = ci;
-      if (live && j < i) r = fmaf(-expf(e_G[i] - Gj) * s_gram[j * E + i], ci, r);
+      r = fmaf(-f, ci, r);
     }
-    if (live) {
-      s_c[t * E + j] = cj;
-      s_ec[t * E + j] = expf(Gj) * cj;
+    if (j < n_all) {
+      s_c[t * L + j] = live ? cj : 0.f;
+      s_ec[t * L + j] = live ? expf(e_G[j]) * cj : 0.f;
     }
   }
   __syncthreads();
   // ---- w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j and acc_t = sum_j c_j v_j, to the workspace
   float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
-  for (int x = lane; x < T * D; x += 64) {
+  for (int x = tid; x < T * D; x += NTH) {
     const int t = x / D, c = x - t * D;
     const int e_last = cnt + t;
     float w = expf(e_G[e_last]) * Row::get(e_q + t * LDW, c, p.in_dt);
     float acc = 0.f;
     for (int jj = 0; jj <= e_last; ++jj) {
-      w = fmaf(-s_ec[t * E + jj], Row::get(e_k + jj * LDW, c, p.in_dt), w);
-      acc = fmaf(s_c[t * E + jj], Row::get(e_v + jj * LDW, c, p.in_dt), acc);
+      w = fmaf(-s_ec[t * L + jj], Row::get(e_k + jj * LDW, c, p.in_dt), w);
+      acc = fmaf(s_c[t * L + jj], Row::get(e_v + jj * LDW, c, p.in_dt), acc);
     }
     wsu[(2 * t) * D + c] = w;
     wsu[(2 * t + 1) * D + c] = acc;
@@ -586,39 +653,82 @@ __global__ void gdn_replay_rollback_kernel(const ReplayArgs P) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int SDT, int D, int EB>
+template <int SDT, int D, int EB, int CDT>
 static hipError_t launch_fold(const ReplayArgs& a, hipStream_t s) {
-  using G = ReplayGeom<SDT, D>;
+  using G = FoldGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
-  const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   const size_t lds = replay_fold_lds_bytes(D, a.ring.L);
-  hipLaunchKernelGGL((gdn_replay_fold_kernel<SDT, D, NT, EB>), dim3(grid), dim3(G::NW * 64), lds, s, a);
+  const auto kern = &gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>;
+  int per_cu = 0, cus = 0;
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), G::NW * 64, lds, &per_cu);
+  if (e == hipSuccess) e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)a.d.B * a.d.Hv;
+  const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+  const unsigned grid = (unsigned)(units < fill ? units : fill);
+  hipLaunchKernelGGL((gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>), dim3(grid), dim3(G::NW * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int SDT, int D, int EB>
+static hipError_t launch_fold_any(const ReplayArgs& a, hipStream_t s) {
+  if constexpr (SDT == GDN_F32) {
+    if (a.read_pool != nullptr)
+      return a.read_dt == GDN_BF16 ? launch_fold<SDT, D, EB, GDN_BF16>(a, s) : launch_fold<SDT, D, EB, GDN_F16>(a, s);
+  }
+  return launch_fold<SDT, D, EB, -1>(a, s);
+}
+
+template <int SDT, int D, bool NT, int TB>
+static void launch_stream(const ReplayArgs& a, unsigned grid, size_t lds, float* ws, hipStream_t s) {
+  using G = ReplayGeom<SDT, D>;
+  hipLaunchKernelGGL((gdn_replay_stream_kernel<SDT, D, NT, TB>), dim3(grid), dim3(G::NW * 64), lds, s, a, ws);
+}
+
+// Outputs read the checkpoint itself, or its 16-bit read copy (dual precision).
+template <int D>
+static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
+  const size_t lds = (size_t)a.T * D * sizeof(float);
+  const bool one = a.T <= 1;
+  switch (read_dt) {
+    case GDN_F32:
+      one ? launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, 1>(a, grid, lds, ws, s)
+          : launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, kStreamTB>(a, grid, lds, ws, s);
+      break;
+    case GDN_BF16:
+      one ? launch_stream<GDN_BF16, D, false, 1>(a, grid, lds, ws, s)
+          : launch_stream<GDN_BF16, D, false, kStreamTB>(a, grid, lds, ws, s);
+      break;
+    case GDN_F16:
+      one ? launch_stream<GDN_F16, D, false, 1>(a, grid, lds, ws, s)
+          : launch_stream<GDN_F16, D, false, kStreamTB>(a, grid, lds, ws, s);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <int SDT, int D>
 static hipError_t launch_replay_t(const ReplayArgs& a, float* ws, hipStream_t s) {
-  using G = ReplayGeom<SDT, D>;
-  constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
   const bool f32_in = a.d.in_dt == GDN_F32;
-  hipError_t e = f32_in ? launch_fold<SDT, D, 4>(a, s) : launch_fold<SDT, D, 2>(a, s);
+  hipError_t e = f32_in ? launch_fold_any<SDT, D, 4>(a, s) : launch_fold_any<SDT, D, 2>(a, s);
   if (e != hipSuccess || a.T == 0) return e;
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
+  constexpr int NWP = GDN_REPLAY_PREP_WAVES;
   if (f32_in)
-    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 4>), dim3(grid), dim3(64),
+    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 4, NWP>), dim3(grid), dim3(NWP * 64),
                        replay_prep_words(D, 4, a.ring.L, a.T) * sizeof(float), s, a, ws);
   else
-    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 2>), dim3(grid), dim3(64),
+    hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 2, NWP>), dim3(grid), dim3(NWP * 64),
                        replay_prep_words(D, 2, a.ring.L, a.T) * sizeof(float), s, a, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds_w = (size_t)a.T * D * sizeof(float);
-  if (a.T <= 1)
-    hipLaunchKernelGGL((gdn_replay_stream_kernel<SDT, D, NT, 1>), dim3(grid), dim3(G::NW * 64), lds_w, s, a, ws);
-  else
-    hipLaunchKernelGGL((gdn_replay_stream_kernel<SDT, D, NT, kStreamTB>), dim3(grid), dim3(G::NW * 64), lds_w, s, a,
-                       ws);
-  return hipGetLastError();
+  if (a.read_pool == nullptr) return launch_stream_any<D>(a, SDT, ws, s);
+  ReplayArgs r = a;
+  r.d.pool = a.read_pool;
+  return launch_stream_any<D>(r, a.read_dt, ws, s);
 }
 
 template <int SDT>

@@ -215,6 +215,28 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
 gdn_status gdn_replay_flush(const gdn_dims* dims, int32_t B, const gdn_pool* ckpt,
                             const int32_t* slot_map, const gdn_ring* ring, void* stream);
 
+/* Dual-precision checkpoint variants (AREX ReplaySSM article, "cache inputs,
+ * not state" section, its closing paragraph on precision: the scheme it cites
+ * recurses on a high-precision checkpoint and serves reads from a
+ * low-precision copy).  `master` is the f32 checkpoint pool that every fold reads and
+ * writes; `read_copy` is a bf16 or f16 pool of the same slots and shape that
+ * holds master rounded once.  Each fold (count + T > L) writes the folded
+ * state to master and, rounded, to read_copy; window outputs read read_copy
+ * (half the bytes of an f32 checkpoint) and the ring.  Everything else is as
+ * gdn_replay_decode / gdn_replay_flush.  gdn_replay_flush_dual also refreshes
+ * read_copy from master for every mapped slot, whether or not its ring is
+ * empty: call it once to initialise read_copy before the first step.
+ * read_copy must not alias master. */
+gdn_status gdn_replay_decode_dual(const gdn_dims* dims, int32_t B, int32_t T, const void* q,
+                                  const void* k, const void* v, gdn_dtype in_dtype,
+                                  const gdn_gates* gates, const gdn_pool* master,
+                                  const gdn_pool* read_copy, const int32_t* slot_map,
+                                  const gdn_ring* ring, void* out, gdn_dtype out_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+gdn_status gdn_replay_flush_dual(const gdn_dims* dims, int32_t B, const gdn_pool* master,
+                                 const gdn_pool* read_copy, const int32_t* slot_map,
+                                 const gdn_ring* ring, void* stream);
+
 /* Drop the last num_rejected[b] live entries of row b's slot, for every value
  * head: count <- max(count - r, 0) (the pointer move that replaces a state
  * rollback).  num_rejected: device int32 [B], each >= 0. */

@@ -63,7 +63,7 @@ __all__ = [
     "round_to_format", "to_storage", "widen", "dtype_of", "softplus", "sigmoid", "gates",
     "decay_update", "readout", "gdn_token", "ref_gdn", "decode_step", "chunk_prefill",
     "Ring", "new_ring", "replay_decode", "replay_flush", "replay_rollback", "spec_decode",
-    "copy_state_blocks",
+    "copy_state_blocks", "replay_decode_dual", "replay_flush_dual",
 ]
 
 # ---------------------------------------------------------------------------
@@ -404,6 +404,74 @@ def replay_flush(ckpt, ring, slot_map):
             for h in range(Hv):
                 _fold(ckpt, ring, int(slot), h, sdt)
     return ckpt, ring
+
+
+def _refresh_copy(master, copy, slot, h):
+    """The read copy holds the master rounded once to the copy's format."""
+    copy[slot, h] = to_storage(widen(master[slot, h]), dtype_of(copy))
+
+
+def replay_decode_dual(master, copy, ring, slot_map, q, k, v, a, b, A_log, dt_bias, scale=None, heads=None):
+    """Replay step on a dual-precision checkpoint ([ReplaySSM] "cache inputs, not state", the
+    closing remarks on precision: recursion on a high-precision checkpoint, reads from a
+    low-precision copy).
+
+    master: f32 checkpoint pool; copy: bf16/f16 pool of the same shape.  As replay_decode, except
+    that a fold reads and writes master and then refreshes copy from it, and the window outputs
+    replay from copy.  Returns (master, copy, ring, o).
+    """
+    master = np.array(master, copy=True)
+    copy = np.array(copy, copy=True)
+    if dtype_of(master) != "f32":
+        raise ValueError("the master checkpoint is f32")
+    ring = ring.copy()
+    num_slots, Hv, dk, dv = master.shape
+    B, T, Hk = q.shape[0], q.shape[1], q.shape[2]
+    ratio = Hv // Hk
+    L = ring.L
+    if not 1 <= T <= L:
+        raise ValueError("window longer than the ring")
+    s = _scale(dk, scale)
+    qf = widen(q)
+    g, beta = gates(a, b, A_log, dt_bias)
+    o = np.zeros((B, T, Hv, dv))
+    for bi in range(B):
+        slot = int(slot_map[bi])
+        if not _slot_ok(slot, num_slots):
+            continue
+        for h in (range(Hv) if heads is None else heads):
+            hk = h // ratio
+            if int(ring.count[slot, h]) + T > L:
+                _fold(master, ring, slot, h, "f32")
+                _refresh_copy(master, copy, slot, h)
+            st, cnt = int(ring.start[slot, h]), int(ring.count[slot, h])
+            for t in range(T):
+                j = (st + cnt + t) % L
+                ring.k[slot, h, j] = k[bi, t, hk]
+                ring.v[slot, h, j] = v[bi, t, h]
+                ring.g[slot, h, j] = np.float32(g[bi, t, h])
+                ring.beta[slot, h, j] = np.float32(beta[bi, t, h])
+            ring.count[slot, h] = cnt + T
+            S0 = widen(copy[slot, h])
+            for t in range(T):
+                St = _replay_state(S0, ring, slot, h, cnt + t + 1)
+                o[bi, t, h] = readout(St, qf[bi, t, hk], s)
+    return master, copy, ring, o
+
+
+def replay_flush_dual(master, copy, ring, slot_map):
+    """Fold every committed entry of the mapped slots into master and refresh copy from master
+    (also for empty rings, which is how a copy is first filled)."""
+    master = np.array(master, copy=True)
+    copy = np.array(copy, copy=True)
+    ring = ring.copy()
+    num_slots, Hv = master.shape[:2]
+    for slot in slot_map:
+        if _slot_ok(slot, num_slots):
+            for h in range(Hv):
+                _fold(master, ring, int(slot), h, "f32")
+                _refresh_copy(master, copy, int(slot), h)
+    return master, copy, ring
 
 
 def replay_rollback(ring, slot_map, num_rejected):

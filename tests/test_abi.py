@@ -233,3 +233,23 @@ def test_copy_state_blocks_validation(L, case, expect):
     c.update(case)
     st = L.gdn_copy_state_blocks(c["refs"], c["P"], c["max_bytes"], c["src"], c["dst"], c["n"], None)
     assert st == expect, gdn.gdn_last_error()
+
+
+def test_replay_dual_validation(L):
+    dims = _dims()
+    master, copy = _pool(), _pool(base=FAKE + 4096, dtype=gdn.GDN_BF16)
+    ring = _ring()
+
+    def dec(B=4, m=master, c=copy):
+        return L.gdn_replay_decode_dual(ctypes.byref(dims), B, 1, FAKE, FAKE, FAKE, gdn.GDN_BF16,
+                                        ctypes.byref(_gates()), ctypes.byref(m), ctypes.byref(c) if c else None,
+                                        FAKE, ctypes.byref(ring), FAKE, gdn.GDN_F32, FAKE, 1 << 30, None)
+
+    assert dec(c=None) == gdn.GDN_EINVAL
+    assert dec(m=_pool(dtype=gdn.GDN_BF16)) == gdn.GDN_EINVAL                 # master must be f32
+    assert dec(c=_pool(base=FAKE + 4096, dtype=gdn.GDN_F32)) == gdn.GDN_EINVAL  # copy must be 16-bit
+    assert dec(c=_pool(base=FAKE + 4096, dtype=gdn.GDN_BF16, n=9)) == gdn.GDN_EINVAL
+    assert dec(c=_pool(base=FAKE, dtype=gdn.GDN_BF16)) == gdn.GDN_EINVAL      # aliases the master
+    assert dec(B=0) == gdn.GDN_OK
+    st = L.gdn_replay_flush_dual(ctypes.byref(dims), 4, ctypes.byref(master), None, FAKE, ctypes.byref(ring), None)
+    assert st == gdn.GDN_EINVAL

@@ -22,10 +22,14 @@ def _gpu():
 
 
 class ReplayCase:
-    def __init__(self, cid, B, Hk, Hv, D, L, sdt, num_slots, sample=None, in_dt="bf16"):
+    """copy_dt selects the dual-precision checkpoint: sdt must be f32 (the master) and the read
+    copy of dtype copy_dt starts as poison, filled by an initial dual flush."""
+
+    def __init__(self, cid, B, Hk, Hv, D, L, sdt, num_slots, sample=None, in_dt="bf16", copy_dt=None):
         import torch
         import gated_deltanet_state_gdn_amd as gdn
         self.cid, self.B, self.Hk, self.Hv, self.D, self.L, self.sdt = cid, B, Hk, Hv, D, L, sdt
+        self.copy_dt = copy_dt
         self.num_slots, self.in_dt = num_slots, in_dt
         self.slot_map = gen.slot_permutation(cid, num_slots)[:B]
         self.ckpt_d, states = poisoned_pool(num_slots, Hv, D, D, sdt, [int(s) for s in self.slot_map], cid)
@@ -39,22 +43,34 @@ class ReplayCase:
         self.A_log, self.dt_bias = gen.head_params(cid, Hv)
         self.A_d, self.dt_d = dev(self.A_log), dev(self.dt_bias)
         self.slot_d = torch.from_numpy(self.slot_map).to(DEV)
+        self.copy_d = self.ref_copy = None
+        if copy_dt is not None:
+            assert sdt == "f32"
+            self.copy_d, _ = poisoned_pool(num_slots, Hv, D, D, copy_dt, [], cid)
+            self.ref_copy = np.zeros(self.ref_ckpt.shape, {"bf16": np.uint16, "f16": np.float16}[copy_dt])
+            self.flush()
 
     def step(self, step, T, a_shift=0.0):
         import torch
         import gated_deltanet_state_gdn_amd as gdn
         inp = gen.token_inputs(self.cid, step, (self.B, T), self.Hk, self.Hv, self.D, self.D, self.in_dt, a_shift)
-        say(f"replay cid={self.cid} B={self.B} D={self.D} L={self.L} T={T} ckpt={self.sdt} step={step}")
+        say(f"replay cid={self.cid} B={self.B} D={self.D} L={self.L} T={T} ckpt={self.sdt} "
+            f"copy={self.copy_dt} step={step}")
         out = gdn.gdn_replay_decode(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]),
-                                    self.A_d, self.dt_d, self.ckpt_d, self.slot_d, self.ring_d)
+                                    self.A_d, self.dt_d, self.ckpt_d, self.slot_d, self.ring_d,
+                                    read_copy=self.copy_d)
         torch.cuda.synchronize()
         sub = {k: v[self.rows] for k, v in inp.items()}
-        self.ref_ckpt, self.ref_ring, o_ref = O.replay_decode(self.ref_ckpt, self.ref_ring, self.ref_map, sub["q"],
-                                                              sub["k"], sub["v"], sub["a"], sub["b"], self.A_log,
-                                                              self.dt_bias)
+        args = (self.ref_map, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], self.A_log, self.dt_bias)
+        if self.copy_dt is None:
+            self.ref_ckpt, self.ref_ring, o_ref = O.replay_decode(self.ref_ckpt, self.ref_ring, *args)
+        else:
+            self.ref_ckpt, self.ref_copy, self.ref_ring, o_ref = O.replay_decode_dual(
+                self.ref_ckpt, self.ref_copy, self.ref_ring, *args)
         o = host(out)
         assert np.all(np.isfinite(o)), "non-finite output"
-        assert_close(o[self.rows], o_ref, "f32" if self.sdt == "f32" else "bf16", f"o step {step}")
+        tol = "f32" if self.sdt == "f32" and self.copy_dt is None else "bf16"
+        assert_close(o[self.rows], o_ref, tol, f"o step {step}")
         return inp
 
     def rollback(self, step, r):
@@ -68,16 +84,22 @@ class ReplayCase:
     def flush(self):
         import torch
         import gated_deltanet_state_gdn_amd as gdn
-        say(f"replay flush cid={self.cid}")
-        gdn.gdn_replay_flush(self.ckpt_d, self.slot_d, self.ring_d, self.Hk)
+        say(f"replay flush cid={self.cid} copy={self.copy_dt}")
+        gdn.gdn_replay_flush(self.ckpt_d, self.slot_d, self.ring_d, self.Hk, read_copy=self.copy_d)
         torch.cuda.synchronize()
-        self.ref_ckpt, self.ref_ring = O.replay_flush(self.ref_ckpt, self.ref_ring, self.ref_map)
+        if self.copy_dt is None:
+            self.ref_ckpt, self.ref_ring = O.replay_flush(self.ref_ckpt, self.ref_ring, self.ref_map)
+        else:
+            self.ref_ckpt, self.ref_copy, self.ref_ring = O.replay_flush_dual(self.ref_ckpt, self.ref_copy,
+                                                                               self.ref_ring, self.ref_map)
 
     def check_state(self, what):
         import torch
         slots = torch.as_tensor(self.slot_map[self.rows].astype(np.int64), device=DEV)
         ck = host(self.ckpt_d[slots])
         assert_close(ck, self.ref_ckpt, self.sdt, f"{what}: checkpoint")
+        if self.copy_dt is not None:
+            assert_close(host(self.copy_d[slots]), self.ref_copy, self.copy_dt, f"{what}: read copy")
         st, cnt = host(self.ring_d.start[slots]), host(self.ring_d.count[slots])
         assert np.array_equal(st, self.ref_ring.start), f"{what}: ring start"
         assert np.array_equal(cnt, self.ref_ring.count), f"{what}: ring count"
@@ -191,3 +213,29 @@ def test_replay_padded_rows():
     assert cnt[int(c.slot_map[1])].tolist() == [2, 2]
     assert cnt.sum() == 4
     assert np.array_equal(host(c.ckpt_d).view(np.uint32), before.view(np.uint32))  # no fold, nothing written
+
+
+@pytest.mark.parametrize("copy_dt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [16, 128])
+def test_replay_dual_precision_checkpoint(copy_dt, D):
+    """fp32 master + 16-bit read copy: T = 1 on L = 4 over three folds, then a window of 3 with
+    rollback, then a flush; master, copy, ring and outputs checked every step."""
+    c = ReplayCase(60 + D, 5, 1, 2, D, 4, "f32", 8, copy_dt=copy_dt)
+    c.check_state("initial flush")
+    for step in range(13):
+        c.step(step, 1, a_shift=-2.0)
+        c.check_state(f"step {step}")
+    c.step(13, 3, a_shift=-2.0)
+    c.check_state("window")
+    c.rollback(13, gen.rejected_counts(60, 13, c.B, 2))
+    c.flush()
+    c.check_state("flush")
+
+
+def test_replay_dual_full_size_sampled():
+    """B = 512, 32 value heads, 128 x 128 fp32 master with a bf16 read copy, L = 16, over a fold."""
+    c = ReplayCase(4, 512, 16, 32, 128, 16, "f32", 1024, sample=[0, 255, 511], copy_dt="bf16")
+    for step in range(18):
+        c.step(step, 1)
+        if step in (15, 16, 17):
+            c.check_state(f"step {step}")

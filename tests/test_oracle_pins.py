@@ -459,3 +459,37 @@ def test_copy_state_blocks_keeps_bit_patterns():
     x.view(np.uint32)[0, 0] = 0x7FC0DEAD
     (y,) = O.copy_state_blocks([x], [0], [1])
     assert np.array_equal(y.view(np.uint32)[1], x.view(np.uint32)[0])
+
+
+def test_replay_dual_master_tracks_f32_checkpoint_and_reads_the_copy():
+    """Dual-precision checkpoint over 17 steps of L = 4 (4 folds):
+    - the master follows the plain f32-checkpoint replay bit for bit (the copy never feeds back);
+    - after every step the copy equals the master rounded once to bf16 (numpy-independent
+      rounding checked against torch's bfloat16 cast);
+    - on steps without a fold the outputs equal a plain replay whose checkpoint is the copy;
+    - outputs stay within bf16 reach of the f32-checkpoint outputs."""
+    import torch
+    A_log, dt_bias, master, ring = _replay_setup(4, "f32")
+    ref_ckpt, ref_ring = master, ring
+    slots = [1, 2]
+    copy = np.zeros(master.shape, np.uint16)
+    master, copy, ring = O.replay_flush_dual(master, copy, ring, slots)
+    for step in range(17):
+        inp = gen.token_inputs(24, step, (2, 1), 1, 2, 8, 8, "bf16", a_shift=-4.0)
+        args = (slots, inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], A_log, dt_bias)
+        folds = int(ring.count[slots[0], 0]) + 1 > ring.L
+        _, _, o_copy = O.replay_decode(copy, ring, *args)
+        master, copy, ring, o = O.replay_decode_dual(master, copy, ring, *args)
+        ref_ckpt, ref_ring, o_ref = O.replay_decode(ref_ckpt, ref_ring, *args)
+        assert np.array_equal(master, ref_ckpt)
+        t = torch.from_numpy(master[slots].astype(np.float32)).to(torch.bfloat16)
+        assert np.array_equal(copy[slots], t.view(torch.int16).numpy().view(np.uint16))
+        if not folds:
+            np.testing.assert_array_equal(o, o_copy)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=2e-2)
+    # a dual flush folds what is left and refreshes the copy; on an empty ring it only refreshes
+    master, copy, ring = O.replay_flush_dual(master, copy, ring, slots)
+    assert np.all(ring.count[slots] == 0)
+    blank = np.zeros_like(copy)
+    master2, copy2, _ = O.replay_flush_dual(master, blank, ring, slots)
+    assert np.array_equal(master2, master) and np.array_equal(copy2[slots], copy[slots])
