@@ -32,14 +32,14 @@ import numpy as np
 __all__ = [
     "DTYPES", "TID", "rng", "store", "to_torch", "from_torch", "head_params",
     "token_inputs", "pool_slots", "slot_permutation", "seq_lengths_cu",
-    "rejected_counts", "split_lengths", "DecodeShape", "CONFIGS",
+    "rejected_counts", "split_lengths", "DecodeShape", "CONFIGS", "m2_params", "m2_inputs", "M2_LAYER",
 ]
 
 DTYPES = ("f32", "bf16", "f16")
 
 # tensor ids of the per-tensor seeds
 TID = dict(q=1, k=2, v=3, a=4, b=5, A_log=6, dt_bias=7, pool=8, slot_perm=9,
-           rejected=10, ring=11, prefill=12, counts=13)
+           rejected=10, ring=11, prefill=12, counts=13, x=14, Bm=15, Cm=16, dt=17, Dskip=18)
 
 
 def rng(config_id: int, tensor: str, index: int = 0) -> np.random.Generator:
@@ -141,6 +141,32 @@ def split_lengths(lengths, frac=0.55):
     """First call gets floor(frac * len) tokens of each sequence, the second the rest."""
     first = [int(math.floor(frac * n)) for n in lengths]
     return first, [n - f for n, f in zip(lengths, first)]
+
+
+def m2_params(config_id: int, H: int):
+    """Mamba2 head parameters, float32 [H]: A_log = log U(1, 16) (A in [-16, -1]); dt_bias the
+    inverse softplus of a log-uniform step in [1e-3, 1e-1]; skip D ~ U(0.5, 1.5)."""
+    A_log = np.log(rng(config_id, "A_log").uniform(1.0, 16.0, size=H)).astype(np.float32)
+    dt0 = np.exp(rng(config_id, "dt_bias").uniform(math.log(1e-3), math.log(1e-1), size=H))
+    dt_bias = np.log(np.expm1(dt0)).astype(np.float32)
+    Dskip = rng(config_id, "Dskip").uniform(0.5, 1.5, size=H).astype(np.float32)
+    return A_log, dt_bias, Dskip
+
+
+def m2_inputs(config_id: int, step: int, lead: tuple, H: int, G: int, d: int, n: int,
+              in_dtype: str = "bf16", dt_shift: float = 0.0) -> dict:
+    """Mamba2 per-token inputs: x [*lead, H, d] ~ N(0, 1); Bm, Cm [*lead, G, n] ~ N(0, 1/n);
+    dt [*lead, H] ~ N(dt_shift, 0.5^2) (raw, before softplus with dt_bias)."""
+    lead = tuple(int(v) for v in lead)
+    x = _normal(rng(config_id, "x", step), lead + (H, d))
+    Bm = _normal(rng(config_id, "Bm", step), lead + (G, n), n ** -0.5)
+    Cm = _normal(rng(config_id, "Cm", step), lead + (G, n), n ** -0.5)
+    dt = _normal(rng(config_id, "dt", step), lead + (H,), 0.5) + np.float32(dt_shift)
+    return {name: store(v, in_dtype) for name, v in dict(x=x, Bm=Bm, Cm=Cm, dt=dt.astype(np.float32)).items()}
+
+
+# Mamba2 layer of the ReplaySSM workload: 128 heads of headdim 64, dstate 128, 8 groups
+M2_LAYER = dict(H=128, G=8, d=64, n=128)
 
 
 def rejected_counts(config_id: int, step: int, B: int, max_r: int) -> np.ndarray:
