@@ -325,6 +325,85 @@ def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
     return res
 
 
+def m2_state_bytes(sdt, H, d, n):
+    return H * d * n * SB[sdt]
+
+
+def m2_decode_bytes(B, sdt, H, G, d, n, ib=2, ob=2):
+    """Algorithmic bytes of one Mamba2 decode step: state read + write, x, B, C, dt, outputs."""
+    return (2 * B * m2_state_bytes(sdt, H, d, n) + B * (H * d + 2 * G * n + H) * ib + 3 * H * 4 + B * 4
+            + B * H * d * ob)
+
+
+def m2_replay_step_bytes(B, sdt, n_before, T, L, H, G, d, n, ib=2, ob=2):
+    """Algorithmic bytes of one Mamba2 replay step of T tokens with n_before committed entries."""
+    fold = n_before + T > L
+    state = B * m2_state_bytes(sdt, H, d, n) * (2 if fold else 1)
+    entry = (H * d + G * n) * ib + 2 * H * 4  # x per head, B per group, g and dt' per head
+    live = 0 if fold else n_before
+    read_fold = n_before * entry if fold else 0
+    return (state + B * (live * entry + read_fold) + B * T * entry
+            + B * T * (H * d + 2 * G * n + H) * ib + 3 * H * 4 + 3 * B * 4 + B * T * H * d * ob)
+
+
+def bench_mamba2(torch, gdn, gen, B, sdt, mode, T=1, L=16, cycles=2, steps=16, cid=5):
+    """Mamba2 layer (gen.M2_LAYER): standard decode (mode "decode") or replay (mode "replay")."""
+    import numpy as np
+    dev = "cuda"
+    lay = gen.M2_LAYER
+    H, G, d, n = lay["H"], lay["G"], lay["d"], lay["n"]
+    num_slots = 2 * B
+    slot_map = gen.slot_permutation(cid, num_slots)[:B]
+    pool = torch.zeros((num_slots, H, d, n), dtype={"f32": torch.float32, "bf16": torch.bfloat16,
+                                                     "f16": torch.float16}[sdt], device=dev)
+    for i in range(0, B, 32):
+        sl = slot_map[i:i + 32]
+        pool[torch.as_tensor(sl.astype(np.int64), device=dev)] = gen.to_torch(gen.pool_slots(cid, sl, H, d, n, sdt),
+                                                                              dev)
+    A_log, dt_bias, Dk = gen.m2_params(cid, H)
+    Pm = [gen.to_torch(t, dev) for t in (A_log, dt_bias, Dk)]
+    sm = torch.from_numpy(slot_map).to(dev)
+    lead = (B,) if mode == "decode" else (B, T)
+    ins = []
+    for s in range(4):
+        inp = gen.m2_inputs(cid, s, lead, H, G, d, n, "bf16")
+        ins.append([gen.to_torch(inp[x], dev) for x in ("x", "Bm", "Cm", "dt")])
+    out = torch.empty(lead + (H, d), dtype=torch.bfloat16, device=dev)
+    if mode == "decode":
+        def fn(i):
+            x, Bm, Cm, dt = ins[i % 4]
+            gdn.gdn_mamba2_decode_step(x, Bm, Cm, dt, *Pm, pool, sm, out=out)
+        t = timed_launches(torch, fn, steps, 3)
+        n_steps, nbytes = steps, steps * m2_decode_bytes(B, sdt, H, G, d, n)
+        src = ["gdn_mamba2.hip", "gdn_device.h"]
+    else:
+        ring = gdn.new_m2_ring(num_slots, H, G, L, d, n, torch.bfloat16, dev)
+        per_cycle = L // T if T > 1 else L
+
+        def fn(i):
+            x, Bm, Cm, dt = ins[i % 4]
+            gdn.gdn_mamba2_replay_decode(x, Bm, Cm, dt, *Pm, pool, sm, ring, out=out)
+        t = timed_launches(torch, fn, cycles * per_cycle, per_cycle)
+        n_steps, nbytes, cnt = cycles * per_cycle, 0, 0
+        for i in range((cycles + 1) * per_cycle):
+            b_i = m2_replay_step_bytes(B, sdt, cnt, T, L, H, G, d, n)
+            cnt = (0 if cnt + T > L else cnt) + T
+            if i >= per_cycle:
+                nbytes += b_i
+        src = ["gdn_mamba2.hip", "gdn_device.h"]
+        del ring
+    ms = t["span_ms"] / n_steps
+    res = {"B": B, "state": sdt, "mode": mode, "T": T if mode != "decode" else 1, "L": L if mode != "decode" else None,
+           "layer": f"H={H} G={G} headdim={d} dstate={n}", "ms_per_step": round(ms, 5),
+           "GB_per_s": round(nbytes / n_steps / (ms * 1e-3) / 1e9, 1),
+           "tokens_per_s": round(B * (T if mode != "decode" else 1) / (ms * 1e-3), 1),
+           "bytes_per_step_avg": nbytes // n_steps}
+    res["roofline"] = roofline_bw(nbytes / n_steps, t["mean_launch_ms"], traffic_for(f"m2_{mode}_{sdt}_B{B}", src))
+    del pool, ins, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_copy_blocks(torch, gdn, reps=8, P=16, slots=64, jobs=32):
     """Prefix-caching state-block copy: `jobs` slot copies in each of P layer-state tensors of
     [slots, 32, 128, 128] fp32 (2 MiB slots)."""
@@ -398,7 +477,7 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | replay_dual_<dt>_T<t> | "
-                                                    "spec_<dt>_T<t> | prefill_<dt> | blockcopy | copy")
+                                                    "spec_<dt>_T<t> | mamba2_<decode|replay>_<dt>[_T<t>] | prefill_<dt> | blockcopy | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -434,6 +513,8 @@ def main():
                 r = bench_prefill(torch, gdn, gen, rest[0], max(args.steps // 8, 2))
             elif kind == "copy":
                 r = bench_copy(torch)
+            elif kind == "mamba2":
+                r = bench_mamba2(torch, gdn, gen, 512, rest[1], rest[0], T=int(rest[2][1:]) if len(rest) > 2 else 1)
             elif kind == "blockcopy":
                 r = bench_copy_blocks(torch, gdn)
             else:
@@ -457,6 +538,9 @@ def main():
         for dt in ("f32", "bf16"):
             log(f"row: speculative window B=512 T=5 {dt} state, one state per position")
             rows[f"spec_{dt}_B512_T5"] = bench_spec(torch, gdn, gen, 512, dt, 5, 16)
+        for mode in ("decode", "replay"):
+            log(f"row: Mamba2 {mode} B=512 fp32 state")
+            rows[f"mamba2_{mode}_f32_B512"] = bench_mamba2(torch, gdn, gen, 512, "f32", mode)
         log("row: state-block copy, 32 jobs x 16 tensors of 2 MiB slots")
         rows["state_block_copy"] = bench_copy_blocks(torch, gdn)
         for dt in ("f32", "bf16"):

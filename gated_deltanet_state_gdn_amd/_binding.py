@@ -23,12 +23,29 @@ EXPORTS = (
     "gdn_decode_step", "gdn_spec_decode", "gdn_copy_state_blocks", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
     "gdn_replay_decode",
     "gdn_replay_flush", "gdn_replay_rollback", "gdn_replay_decode_dual", "gdn_replay_flush_dual",
+    "gdn_mamba2_decode_step", "gdn_mamba2_replay_decode", "gdn_mamba2_replay_flush", "gdn_mamba2_replay_rollback",
     "gdn_status_string", "gdn_last_error",
 )
 
 
 class gdn_state_ref(ctypes.Structure):
     _fields_ = [("base", ctypes.c_uint64), ("slot_bytes", ctypes.c_uint64), ("num_slots", ctypes.c_uint64)]
+
+
+class gdn_m2_dims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("num_groups", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32)]
+
+
+class gdn_m2_params(ctypes.Structure):
+    _fields_ = [("dt", ctypes.c_void_p), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("D", ctypes.c_void_p)]
+
+
+class gdn_m2_ring(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("g", ctypes.c_void_p), ("dtp", ctypes.c_void_p),
+                ("start", ctypes.c_void_p), ("count", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
+                ("L", ctypes.c_int32), ("dtype", ctypes.c_int)]
 
 
 class gdn_dims(ctypes.Structure):
@@ -71,6 +88,7 @@ def lib() -> ctypes.CDLL:
     P, I32, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     pd, pg, pp, pr = (ctypes.POINTER(gdn_dims), ctypes.POINTER(gdn_gates), ctypes.POINTER(gdn_pool),
                       ctypes.POINTER(gdn_ring))
+    pm, pmp, pmr = ctypes.POINTER(gdn_m2_dims), ctypes.POINTER(gdn_m2_params), ctypes.POINTER(gdn_m2_ring)
     sig = {
         "gdn_decode_step": (INT, [pd, I32, P, P, P, INT, pg, pp, P, P, INT, P]),
         "gdn_spec_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, P, P, INT, P]),
@@ -83,6 +101,10 @@ def lib() -> ctypes.CDLL:
         "gdn_replay_decode_dual": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, pp, P, pr, P, INT, P, SZ, P]),
         "gdn_replay_flush_dual": (INT, [pd, I32, pp, pp, P, pr, P]),
         "gdn_replay_rollback": (INT, [pd, I32, P, P, pr, P]),
+        "gdn_mamba2_decode_step": (INT, [pm, I32, P, P, P, INT, pmp, pp, P, P, INT, P]),
+        "gdn_mamba2_replay_decode": (INT, [pm, I32, I32, P, P, P, INT, pmp, pp, P, pmr, P, INT, P]),
+        "gdn_mamba2_replay_flush": (INT, [pm, I32, pp, P, pmr, P]),
+        "gdn_mamba2_replay_rollback": (INT, [pm, I32, P, P, pmr, P]),
         "gdn_status_string": (ctypes.c_char_p, [INT]),
         "gdn_last_error": (ctypes.c_char_p, []),
     }
@@ -330,3 +352,84 @@ def gdn_status_string(status: int) -> str:
 
 def gdn_last_error() -> str:
     return lib().gdn_last_error().decode()
+
+
+# ------------------------------------------------------------------ Mamba2
+@dataclass
+class M2Ring:
+    """Mamba2 ReplaySSM ring (layout of gdn_m2_ring); pointers are per slot."""
+    x: object      # [num_slots, H, L, d]
+    Bm: object     # [num_slots, G, L, n]
+    g: object      # [num_slots, H, L] float32
+    dtp: object    # [num_slots, H, L] float32
+    start: object  # [num_slots] int32
+    count: object  # [num_slots] int32
+
+    @property
+    def L(self) -> int:
+        return int(self.g.shape[2])
+
+    def c_struct(self) -> gdn_m2_ring:
+        return gdn_m2_ring(_ptr(self.x), _ptr(self.Bm), _ptr(self.g), _ptr(self.dtp), _ptr(self.start),
+                           _ptr(self.count), int(self.g.shape[0]), self.L, dtype_code(self.x.dtype))
+
+
+def new_m2_ring(num_slots, H, G, L, d, n, dtype, device) -> M2Ring:
+    torch = _torch()
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+    return M2Ring(x=z((num_slots, H, L, d), dtype), Bm=z((num_slots, G, L, n), dtype),
+                  g=z((num_slots, H, L), torch.float32), dtp=z((num_slots, H, L), torch.float32),
+                  start=z((num_slots,), torch.int32), count=z((num_slots,), torch.int32))
+
+
+def _m2_params(dt, A_log, dt_bias, D):
+    return gdn_m2_params(_ptr(dt), _ptr(A_log), _ptr(dt_bias), _ptr(D))
+
+
+def gdn_mamba2_decode_step(x, Bm, Cm, dt, A_log, dt_bias, D, pool, slot_map, out=None, out_dtype=None, stream=None):
+    """One Mamba2 decode step; x [B, H, d]; Bm, Cm [B, G, n]; dt [B, H]; pool [slots, H, d, n]."""
+    torch = _torch()
+    B, H, d = x.shape
+    G, n = Bm.shape[1], Bm.shape[2]
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype or torch.float32, device=x.device)
+    dims = gdn_m2_dims(H, G, d, n)
+    _check(lib().gdn_mamba2_decode_step(ctypes.byref(dims), B, _ptr(x), _ptr(Bm), _ptr(Cm), dtype_code(x.dtype),
+                                        ctypes.byref(_m2_params(dt, A_log, dt_bias, D)), ctypes.byref(_pool(pool)),
+                                        _ptr(slot_map), _ptr(out), dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def gdn_mamba2_replay_decode(x, Bm, Cm, dt, A_log, dt_bias, D, ckpt, slot_map, ring: M2Ring, out=None,
+                             out_dtype=None, stream=None):
+    """Mamba2 replay step of T tokens; x [B, T, H, d]; Bm, Cm [B, T, G, n]; dt [B, T, H]."""
+    torch = _torch()
+    B, T, H, d = x.shape
+    G, n = Bm.shape[2], Bm.shape[3]
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=out_dtype or torch.float32, device=x.device)
+    dims = gdn_m2_dims(H, G, d, n)
+    rs = ring.c_struct()
+    _check(lib().gdn_mamba2_replay_decode(ctypes.byref(dims), B, T, _ptr(x), _ptr(Bm), _ptr(Cm), dtype_code(x.dtype),
+                                          ctypes.byref(_m2_params(dt, A_log, dt_bias, D)),
+                                          ctypes.byref(_pool(ckpt)), _ptr(slot_map), ctypes.byref(rs), _ptr(out),
+                                          dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def gdn_mamba2_replay_flush(ckpt, slot_map, ring: M2Ring, stream=None):
+    """Fold every committed entry of the mapped slots into their checkpoints."""
+    H, d, n = ckpt.shape[1], ckpt.shape[2], ckpt.shape[3]
+    dims = gdn_m2_dims(H, int(ring.Bm.shape[1]), d, n)
+    rs = ring.c_struct()
+    _check(lib().gdn_mamba2_replay_flush(ctypes.byref(dims), int(slot_map.shape[0]), ctypes.byref(_pool(ckpt)),
+                                         _ptr(slot_map), ctypes.byref(rs), _stream(stream)))
+
+
+def gdn_mamba2_replay_rollback(slot_map, num_rejected, ring: M2Ring, stream=None):
+    """count <- max(count - num_rejected[b], 0) for row b's slot."""
+    H, G = int(ring.x.shape[1]), int(ring.Bm.shape[1])
+    dims = gdn_m2_dims(H, G, int(ring.x.shape[3]), int(ring.Bm.shape[3]))
+    rs = ring.c_struct()
+    _check(lib().gdn_mamba2_replay_rollback(ctypes.byref(dims), int(slot_map.shape[0]), _ptr(slot_map),
+                                            _ptr(num_rejected), ctypes.byref(rs), _stream(stream)))

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_spec.hip", "gdn_copy.hip", "gdn_replay.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_spec.hip", "gdn_copy.hip", "gdn_mamba2.hip", "gdn_replay.hip", "gdn_prefill.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

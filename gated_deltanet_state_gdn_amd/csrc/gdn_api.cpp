@@ -416,3 +416,160 @@ gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* s
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ Mamba2
+namespace {
+
+gdn_status check_m2_dims(const gdn_m2_dims* d) {
+  GDN_REQUIRE(d != nullptr, GDN_EINVAL, "dims is NULL");
+  GDN_REQUIRE(d->num_heads >= 1 && d->num_groups >= 1, GDN_EINVAL, "head and group counts must be >= 1");
+  GDN_REQUIRE(d->num_heads % d->num_groups == 0, GDN_EINVAL, "H=%d is not a multiple of G=%d", d->num_heads,
+              d->num_groups);
+  const auto ok_dim = [](int x) { return x == 16 || x == 64 || x == 128; };
+  GDN_REQUIRE(d->headdim >= 1 && d->dstate >= 1, GDN_EINVAL, "headdim and dstate must be >= 1");
+  GDN_REQUIRE(ok_dim(d->headdim) && ok_dim(d->dstate), GDN_EUNSUPPORTED,
+              "headdim=%d dstate=%d: compiled for {16, 64, 128} each", d->headdim, d->dstate);
+  return GDN_OK;
+}
+
+gdn_status check_m2_io(const void* x, const void* Bm, const void* Cm, const gdn_m2_params* pr, int in_dt,
+                       const void* y, int out_dt) {
+  GDN_REQUIRE(x && Bm && Cm, GDN_EINVAL, "x, Bm or Cm is NULL");
+  GDN_REQUIRE(y != nullptr, GDN_EINVAL, "y is NULL");
+  const size_t eb = dtype_bytes(in_dt);
+  GDN_REQUIRE(aligned(x, eb) && aligned(Bm, eb) && aligned(Cm, eb), GDN_EINVAL, "x, Bm or Cm misaligned");
+  GDN_REQUIRE(aligned(y, dtype_bytes(out_dt)), GDN_EINVAL, "y misaligned for out_dtype");
+  GDN_REQUIRE(pr != nullptr, GDN_EINVAL, "params is NULL");
+  GDN_REQUIRE(pr->dt && pr->A_log && pr->dt_bias && pr->D, GDN_EINVAL, "a parameter pointer is NULL");
+  GDN_REQUIRE(aligned(pr->dt, eb) && aligned(pr->A_log, 4) && aligned(pr->dt_bias, 4) && aligned(pr->D, 4),
+              GDN_EINVAL, "a parameter pointer is misaligned");
+  return GDN_OK;
+}
+
+gdn_status check_m2_ring(const gdn_m2_ring* r, int in_dt, int64_t num_slots) {
+  GDN_REQUIRE(r != nullptr, GDN_EINVAL, "ring is NULL");
+  GDN_REQUIRE(r->x && r->Bm && r->g && r->dtp && r->start && r->count, GDN_EINVAL, "a ring pointer is NULL");
+  GDN_REQUIRE(r->num_slots == num_slots, GDN_EINVAL, "ring holds %lld slots, the checkpoint pool %lld",
+              (long long)r->num_slots, (long long)num_slots);
+  GDN_REQUIRE(r->L >= 1, GDN_EINVAL, "ring length L=%d must be >= 1", r->L);
+  GDN_REQUIRE(r->L <= 64, GDN_EUNSUPPORTED, "ring length L=%d: at most 64 is supported", r->L);
+  GDN_REQUIRE(valid_dtype(r->dtype), GDN_EINVAL, "ring dtype %d is not a gdn_dtype", (int)r->dtype);
+  if (in_dt >= 0)
+    GDN_REQUIRE((int)r->dtype == in_dt, GDN_EINVAL, "ring dtype %d differs from in_dtype %d", (int)r->dtype, in_dt);
+  const size_t eb = dtype_bytes(r->dtype);
+  GDN_REQUIRE(aligned(r->x, eb) && aligned(r->Bm, eb) && aligned(r->g, 4) && aligned(r->dtp, 4) &&
+                  aligned(r->start, 4) && aligned(r->count, 4),
+              GDN_EINVAL, "a ring pointer is misaligned");
+  return GDN_OK;
+}
+
+gdn::M2Args m2_args(const gdn_m2_dims* d, int32_t B, int32_t T, const void* x, const void* Bm, const void* Cm,
+                    int in_dt, const gdn_m2_params* pr, const gdn_pool* pool, const int32_t* slot_map, void* y,
+                    int out_dt) {
+  gdn::M2Args a{};
+  a.x = x;
+  a.Bm = Bm;
+  a.Cm = Cm;
+  if (pr != nullptr) {
+    a.dt = pr->dt;
+    a.A_log = pr->A_log;
+    a.dt_bias = pr->dt_bias;
+    a.Dskip = pr->D;
+  }
+  a.pool = pool->base;
+  a.slot_map = slot_map;
+  a.y = y;
+  a.num_slots = pool->num_slots;
+  a.B = B;
+  a.H = d->num_heads;
+  a.G = d->num_groups;
+  a.in_dt = in_dt;
+  a.out_dt = out_dt;
+  a.T = T;
+  return a;
+}
+
+void m2_ring_args(gdn::M2Args& a, const gdn_m2_ring* r) {
+  a.L = r->L;
+  a.rx = r->x;
+  a.rB = r->Bm;
+  a.rg = r->g;
+  a.rdtp = r->dtp;
+  a.start = r->start;
+  a.count = r->count;
+}
+
+}  // namespace
+
+gdn_status gdn_mamba2_decode_step(const gdn_m2_dims* dims, int32_t B, const void* x, const void* Bm,
+                                  const void* Cm, gdn_dtype in_dtype, const gdn_m2_params* params,
+                                  const gdn_pool* state, const int32_t* slot_map, void* y, gdn_dtype out_dtype,
+                                  void* stream) {
+  GDN_TRY(check_m2_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_heads <= INT32_MAX, GDN_EINVAL, "B * H exceeds the grid limit");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_m2_io(x, Bm, Cm, params, in_dtype, y, out_dtype));
+  GDN_TRY(check_pool(state, "state"));
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::M2Args a = m2_args(dims, B, 1, x, Bm, Cm, in_dtype, params, state, slot_map, y, out_dtype);
+  return launched(gdn::launch_m2_decode(a, state->dtype, dims->headdim, dims->dstate, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_mamba2_replay_decode(const gdn_m2_dims* dims, int32_t B, int32_t T, const void* x, const void* Bm,
+                                    const void* Cm, gdn_dtype in_dtype, const gdn_m2_params* params,
+                                    const gdn_pool* ckpt, const int32_t* slot_map, const gdn_m2_ring* ring, void* y,
+                                    gdn_dtype out_dtype, void* stream) {
+  GDN_TRY(check_m2_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_heads <= INT32_MAX, GDN_EINVAL, "B * H exceeds the grid limit");
+  GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  GDN_REQUIRE(ring != nullptr, GDN_EINVAL, "ring is NULL");
+  GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
+  if (B == 0) return ok();  // nothing is read or written
+  GDN_TRY(check_m2_io(x, Bm, Cm, params, in_dtype, y, out_dtype));
+  GDN_TRY(check_pool(ckpt, "checkpoint"));
+  GDN_TRY(check_m2_ring(ring, in_dtype, ckpt->num_slots));
+  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+              "ring length L=%d with window T=%d exceeds the 64 KiB staging budget", ring->L, T);
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::M2Args a = m2_args(dims, B, T, x, Bm, Cm, in_dtype, params, ckpt, slot_map, y, out_dtype);
+  m2_ring_args(a, ring);
+  return launched(gdn::launch_m2_replay(a, ckpt->dtype, dims->headdim, dims->dstate, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_mamba2_replay_flush(const gdn_m2_dims* dims, int32_t B, const gdn_pool* ckpt, const int32_t* slot_map,
+                                   const gdn_m2_ring* ring, void* stream) {
+  GDN_TRY(check_m2_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE((int64_t)B * dims->num_heads <= INT32_MAX, GDN_EINVAL, "B * H exceeds the grid limit");
+  if (B == 0) return ok();
+  GDN_TRY(check_pool(ckpt, "checkpoint"));
+  GDN_TRY(check_m2_ring(ring, -1, ckpt->num_slots));
+  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, 0) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+              "ring length L=%d exceeds the 64 KiB staging budget", ring->L);
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  gdn::M2Args a = m2_args(dims, B, 0, nullptr, nullptr, nullptr, (int)ring->dtype, nullptr, ckpt, slot_map, nullptr,
+                          GDN_F32);
+  m2_ring_args(a, ring);
+  return launched(gdn::launch_m2_replay(a, ckpt->dtype, dims->headdim, dims->dstate, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_mamba2_replay_rollback(const gdn_m2_dims* dims, int32_t B, const int32_t* slot_map,
+                                      const int32_t* num_rejected, const gdn_m2_ring* ring, void* stream) {
+  GDN_TRY(check_m2_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  if (B == 0) return ok();
+  GDN_REQUIRE(ring != nullptr, GDN_EINVAL, "ring is NULL");
+  GDN_TRY(check_m2_ring(ring, -1, ring->num_slots));
+  GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
+  GDN_REQUIRE(num_rejected != nullptr && aligned(num_rejected, 4), GDN_EINVAL, "num_rejected is NULL or misaligned");
+  gdn::M2Args a{};
+  a.slot_map = slot_map;
+  a.num_slots = ring->num_slots;
+  a.B = B;
+  a.num_rejected = num_rejected;
+  m2_ring_args(a, ring);
+  return launched(gdn::launch_m2_rollback(a, static_cast<hipStream_t>(stream)));
+}

@@ -60,6 +60,29 @@ struct CopyArgs {
 constexpr int kCopyThreads = 256;
 constexpr uint64_t kCopyChunk = 64 * 1024;  // bytes of a slot per workgroup
 
+struct M2Args {
+  const void* x;      // [B, T, H, P] (decode: T = 1)
+  const void* Bm;     // [B, T, G, N]
+  const void* Cm;     // [B, T, G, N]
+  const void* dt;     // [B, T, H]
+  const float* A_log;
+  const float* dt_bias;
+  const float* Dskip;
+  void* pool;         // [num_slots, H, P, N]
+  const int32_t* slot_map;
+  void* y;            // [B, T, H, P]
+  int64_t num_slots;
+  int32_t B, H, G, in_dt, out_dt;
+  int32_t T, L;       // replay window and ring length
+  void* rx;           // ring x [num_slots, H, L, P]
+  void* rB;           // ring B [num_slots, G, L, N]
+  float* rg;          // ring g [num_slots, H, L]
+  float* rdtp;        // ring dt' [num_slots, H, L]
+  int32_t* start;     // [num_slots]
+  int32_t* count;     // [num_slots]
+  const int32_t* num_rejected;
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -89,6 +112,11 @@ hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s);
 hipError_t launch_spec(const SpecArgs& a, int state_dt, int D, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, uint64_t max_slot_bytes, hipStream_t s);
+hipError_t launch_m2_decode(const M2Args& a, int state_dt, int P, int N, hipStream_t s);
+// fold, step (T > 0) and pointer advance; T == 0 is the flush
+hipError_t launch_m2_replay(const M2Args& a, int state_dt, int P, int N, hipStream_t s);
+hipError_t launch_m2_rollback(const M2Args& a, hipStream_t s);
+size_t m2_lds_bytes(int P, int N, int L, int T);
 
 // Dynamic LDS of the speculative-decode kernel; launches need <= kSpecMaxLds.
 size_t spec_lds_bytes(int D, int T);

@@ -272,6 +272,80 @@ gdn_status gdn_copy_state_blocks(const gdn_state_ref* refs, int32_t P, uint64_t 
                                  const int32_t* src_slots, const int32_t* dst_slots, int32_t n,
                                  void* stream);
 
+/* ------------------------------------------------------------------ Mamba2
+ * The second SSM variant of the ReplaySSM article (AREX ReplaySSM article:
+ * "bottleneck", "cache inputs, not state" and "numbers" sections; the
+ * recurrence is Dao and Gu's selective state-space update).  Per head h of
+ * group h / (H / G), with dt' = softplus(dt + dt_bias[h]) and
+ * g = -exp(A_log[h]) dt':
+ *     S <- exp(g) S + dt' x B^T        (S is headdim x dstate, dstate fastest)
+ *     y  = S C + D[h] x
+ * FP32 math; the state is rounded once per write-back. */
+typedef struct {
+  int32_t num_heads;  /* H */
+  int32_t num_groups; /* G, divides H */
+  int32_t headdim;    /* d: 16, 64 or 128 */
+  int32_t dstate;     /* n: 16, 64 or 128 */
+} gdn_m2_dims;
+
+/* dt: [rows, H] in the call's in_dtype (the raw step before softplus);
+ * A_log, dt_bias, D: float32 [H]. */
+typedef struct {
+  const void* dt;
+  const float* A_log;
+  const float* dt_bias;
+  const float* D;
+} gdn_m2_params;
+
+/* Mamba2 ReplaySSM ring, caller-allocated:
+ *   x     [num_slots, H, L, d]  copies of the head inputs, in `dtype`
+ *   Bm    [num_slots, G, L, n]  copies of the group B vectors, in `dtype`
+ *   g     [num_slots, H, L]     float32 log-decays
+ *   dtp   [num_slots, H, L]     float32 steps dt'
+ *   start, count [num_slots]    int32, shared by the slot's heads
+ * C is never stored.  Before first use start and count must be zero. */
+typedef struct {
+  void* x;
+  void* Bm;
+  float* g;
+  float* dtp;
+  int32_t* start;
+  int32_t* count;
+  int64_t num_slots;
+  int32_t L;       /* 1 <= L <= 64 */
+  gdn_dtype dtype; /* must equal the calls' in_dtype */
+} gdn_m2_ring;
+
+/* One token for B sequences: x [B, H, d], Bm and Cm [B, G, n], dt [B, H];
+ * state pool [num_slots, H, d, n]; y [B, H, d]. */
+gdn_status gdn_mamba2_decode_step(const gdn_m2_dims* dims, int32_t B, const void* x, const void* Bm,
+                                  const void* Cm, gdn_dtype in_dtype, const gdn_m2_params* params,
+                                  const gdn_pool* state, const int32_t* slot_map, void* y,
+                                  gdn_dtype out_dtype, void* stream);
+
+/* Replay step of T tokens: x [B, T, H, d], Bm and Cm [B, T, G, n], dt
+ * [B, T, H]; y [B, T, H, d].  Per slot: if count + T > L, every committed
+ * entry is first folded into each head's checkpoint (one rounding) and the
+ * ring emptied; then the window is appended at (start + count + t) mod L and
+ * count += T; window position t outputs y computed from the checkpoint
+ * advanced over the first count_before + t + 1 live entries (without writing
+ * it).  Dynamic shared memory must fit 64 KiB:
+ * 4 (L (d + n + 3) + T (d + 2 n + L)) bytes, else GDN_EUNSUPPORTED. */
+gdn_status gdn_mamba2_replay_decode(const gdn_m2_dims* dims, int32_t B, int32_t T, const void* x,
+                                    const void* Bm, const void* Cm, gdn_dtype in_dtype,
+                                    const gdn_m2_params* params, const gdn_pool* ckpt,
+                                    const int32_t* slot_map, const gdn_m2_ring* ring, void* y,
+                                    gdn_dtype out_dtype, void* stream);
+
+/* Fold every committed entry of the mapped slots into their checkpoints. */
+gdn_status gdn_mamba2_replay_flush(const gdn_m2_dims* dims, int32_t B, const gdn_pool* ckpt,
+                                   const int32_t* slot_map, const gdn_m2_ring* ring, void* stream);
+
+/* count <- max(count - num_rejected[b], 0) for row b's slot (device int32 [B]). */
+gdn_status gdn_mamba2_replay_rollback(const gdn_m2_dims* dims, int32_t B, const int32_t* slot_map,
+                                      const int32_t* num_rejected, const gdn_m2_ring* ring,
+                                      void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status status);
 
