@@ -457,7 +457,7 @@ gdn_status check_m2_ring(const gdn_m2_ring* r, int in_dt, int64_t num_slots) {
   if (in_dt >= 0)
     GDN_REQUIRE((int)r->dtype == in_dt, GDN_EINVAL, "ring dtype %d differs from in_dtype %d", (int)r->dtype, in_dt);
   const size_t eb = dtype_bytes(r->dtype);
-  GDN_REQUIRE(aligned(r->x, eb) && aligned(r->Bm, eb) && aligned(r->g, 4) && aligned(r->dtp, 4) &&
+  GDN_REQUIRE(aligned(r->x, 16) && aligned(r->Bm, eb) && aligned(r->g, 4) && aligned(r->dtp, 4) &&
                   aligned(r->start, 4) && aligned(r->count, 4),
               GDN_EINVAL, "a ring pointer is misaligned");
   return GDN_OK;
@@ -525,14 +525,17 @@ gdn_status gdn_mamba2_replay_decode(const gdn_m2_dims* dims, int32_t B, int32_t 
   GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
   GDN_REQUIRE((int64_t)B * dims->num_heads <= INT32_MAX, GDN_EINVAL, "B * H exceeds the grid limit");
   GDN_TRY(check_dtypes(in_dtype, out_dtype));
+  GDN_REQUIRE(aligned(x, 16), GDN_EINVAL, "x must be 16-byte aligned (it is read four elements at a time)");
   GDN_REQUIRE(ring != nullptr, GDN_EINVAL, "ring is NULL");
   GDN_REQUIRE(T >= 1 && T <= ring->L, GDN_EINVAL, "window T=%d must satisfy 1 <= T <= L=%d", T, ring->L);
   if (B == 0) return ok();  // nothing is read or written
   GDN_TRY(check_m2_io(x, Bm, Cm, params, in_dtype, y, out_dtype));
   GDN_TRY(check_pool(ckpt, "checkpoint"));
   GDN_TRY(check_m2_ring(ring, in_dtype, ckpt->num_slots));
-  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, T) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
-              "ring length L=%d with window T=%d exceeds the 64 KiB staging budget", ring->L, T);
+  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, T, dims->num_heads / dims->num_groups) <=
+                  gdn::kMaxLds,
+              GDN_EUNSUPPORTED, "ring length L=%d with window T=%d and %d heads per group exceeds the 64 KiB staging "
+              "budget", ring->L, T, dims->num_heads / dims->num_groups);
   GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
   gdn::M2Args a = m2_args(dims, B, T, x, Bm, Cm, in_dtype, params, ckpt, slot_map, y, out_dtype);
   m2_ring_args(a, ring);
@@ -547,7 +550,7 @@ gdn_status gdn_mamba2_replay_flush(const gdn_m2_dims* dims, int32_t B, const gdn
   if (B == 0) return ok();
   GDN_TRY(check_pool(ckpt, "checkpoint"));
   GDN_TRY(check_m2_ring(ring, -1, ckpt->num_slots));
-  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, 0) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
+  GDN_REQUIRE(gdn::m2_lds_bytes(dims->headdim, dims->dstate, ring->L, 0, 1) <= gdn::kMaxLds, GDN_EUNSUPPORTED,
               "ring length L=%d exceeds the 64 KiB staging budget", ring->L);
   GDN_REQUIRE(slot_map != nullptr && aligned(slot_map, 4), GDN_EINVAL, "slot_map is NULL or misaligned");
   gdn::M2Args a = m2_args(dims, B, 0, nullptr, nullptr, nullptr, (int)ring->dtype, nullptr, ckpt, slot_map, nullptr,

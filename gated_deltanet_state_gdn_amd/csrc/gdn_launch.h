@@ -116,7 +116,7 @@ hipError_t launch_m2_decode(const M2Args& a, int state_dt, int P, int N, hipStre
 // fold, step (T > 0) and pointer advance; T == 0 is the flush
 hipError_t launch_m2_replay(const M2Args& a, int state_dt, int P, int N, hipStream_t s);
 hipError_t launch_m2_rollback(const M2Args& a, hipStream_t s);
-size_t m2_lds_bytes(int P, int N, int L, int T);
+size_t m2_lds_bytes(int P, int N, int L, int T, int heads_per_group);
 
 // Dynamic LDS of the speculative-decode kernel; launches need <= kSpecMaxLds.
 size_t spec_lds_bytes(int D, int T);

@@ -203,20 +203,27 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_fold_kernel(
       }
       __syncthreads();
       const float decay = s_decay;
+      float sv[PASSES][VEC];
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) {
-        const int r = r0 + pp * NW * RPW;
-        float s[VEC];
-        IO::widen(raw[pp], s);
+        IO::widen(raw[pp], sv[pp]);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s[e] *= decay;
-        for (int j = 0; j < cnt; ++j) {
-          const float cx = ew[j] * ex[j * P + r];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) s[e] = fmaf(cx, eB[j * N + c0 + e], s[e]);
-        }
-        IO::store(tile + pp * NW * RPW * N, s);
+        for (int e = 0; e < VEC; ++e) sv[pp][e] *= decay;
       }
+      for (int j = 0; j < cnt; ++j) {  // rank-cnt update, B_j's columns held in registers
+        const float wj = ew[j];
+        float bj[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bj[e] = eB[j * N + c0 + e];
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+          const float cx = wj * ex[j * P + r0 + pp * NW * RPW];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sv[pp][e] = fmaf(cx, bj[e], sv[pp][e]);
+        }
+      }
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * NW * RPW * N, sv[pp]);
       __syncthreads();  // LDS staging is reused by the next unit
     }
     __syncthreads();  // s_list is rewritten by the next check
@@ -224,13 +231,37 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_fold_kernel(
 }
 
 // ---------------------------------------------------------------- step
-// One workgroup per (sequence, head): outputs of the T window positions from
-// the checkpoint and the ring, and the window appended to the ring (x, g, dt'
-// per head; B once per group, by the group's first head).
-// Dynamic LDS (floats): ring block x [L][P] and B [L][N] (ring order), window
-// x [T][P], B [T][N], C [T][N], prefix sums G [L], dt' [L], weights [T][L].
-__host__ __device__ inline size_t m2_step_floats(int P, int N, int L, int T) {
-  return (size_t)L * P + (size_t)L * N + (size_t)T * P + 2 * (size_t)T * N + 2 * (size_t)L + (size_t)T * L;
+// One workgroup per (sequence, group): the B . C products are shared by the
+// group's heads, so they are formed once; then the heads' checkpoint tiles
+// stream through VGPRs one after another (the next tile's loads in flight
+// while the current one is reduced).  Phase A stages the group's live B rows
+// and the window's B and C, appends the window to the ring (B once per group;
+// x, g and dt' per head), forms per head the prefix sums G of g and the weights
+// w_tj = e^{G_e - G_j} dt'_j (B_j . C_t), and the ring part of every output,
+// acc_t = sum_j w_tj x_j + D x_t.  Phase B adds e^{G_e} S0 C_t per head.
+// Dynamic LDS (floats): ring B [L][N] (ring order), window B and C [T][N]
+// each, dots [T][L], prefix sums and dt' [HPG][L] each, weights [HPG][T][L],
+// decays [HPG][T], acc [HPG][T][P].
+__host__ __device__ inline size_t m2_step_floats(int P, int N, int L, int T, int HPG) {
+  return (size_t)L * N + 2 * (size_t)T * N + (size_t)T * L + 2 * (size_t)HPG * L + (size_t)HPG * T * L +
+         (size_t)HPG * T + (size_t)HPG * T * P;
+}
+
+// Four consecutive input elements (16-byte aligned for f32, 8 for 16-bit) as floats.
+__device__ __forceinline__ void load4(const void* p, int64_t i, int dt, float (&f)[4]) {
+  if (dt == GDN_F32) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = v[e];
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t lo = w[e] & 0xffffu, hi = w[e] >> 16;
+      f[2 * e] = dt == GDN_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
+      f[2 * e + 1] = dt == GDN_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+    }
+  }
 }
 
 template <int SDT, int P, int N, bool NT>
@@ -241,64 +272,60 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
   using IO = TileIO<SDT, VEC, NT>;
   using ST = typename StateElem<SDT>::T;
   extern __shared__ float s_dyn[];
-  const int L = a.L, T = a.T;
+  const int L = a.L, T = a.T, HPG = a.H / a.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
-  const int gr = h / (a.H / a.G);
-  const bool leader = (h % (a.H / a.G)) == 0;
+  const int b = blockIdx.x / a.G, gr = blockIdx.x - (blockIdx.x / a.G) * a.G;
+  const int h0 = gr * HPG;
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
   const int slot = a.slot_map[b];
   if (slot < 0 || (int64_t)slot >= a.num_slots) {  // padded row
-    for (int i = tid; i < T * P; i += NTH) {
-      const int t = i / P, c = i - t * P;
-      store_elem(a.y, (((int64_t)b * T + t) * a.H + h) * P + c, 0.f, a.out_dt);
+    for (int i = tid; i < T * HPG * P; i += NTH) {
+      const int t = i / (HPG * P), rem = i - t * HPG * P;
+      store_elem(a.y, (((int64_t)b * T + t) * a.H + h0) * P + rem, 0.f, a.out_dt);
     }
     return;
   }
-  const ST* tile = static_cast<const ST*>(a.pool) + ((int64_t)slot * a.H + h) * (int64_t)(P * N);
-  typename IO::Raw raw[PASSES];
+  const ST* tiles = static_cast<const ST*>(a.pool) + ((int64_t)slot * a.H + h0) * (int64_t)(P * N);
+  typename IO::Raw cur[PASSES];
 #pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * N + c0);
+  for (int pp = 0; pp < PASSES; ++pp) cur[pp] = IO::load_raw(tiles + (r0 + pp * NW * RPW) * N + c0);
 
-  float* rx = s_dyn;              // [L][P] ring order
-  float* rB = rx + L * P;         // [L][N]
-  float* wx = rB + L * N;         // [T][P]
-  float* wB = wx + T * P;         // [T][N]
-  float* wC = wB + T * N;         // [T][N]
-  float* eG = wC + T * N;         // [L] prefix sums of g, live order
-  float* ed = eG + L;             // [L] dt', live order
-  float* ew = ed + L;             // [T][L] weights e^{G_e - G_j} dt'_j (B_j . C_t)
+  float* rB = s_dyn;               // [L][N] ring order
+  float* wB = rB + L * N;          // [T][N]
+  float* wC = wB + T * N;          // [T][N]
+  float* dots = wC + T * N;        // [T][L] B_j . C_t, live order
+  float* eG = dots + T * L;        // [HPG][L]
+  float* ed = eG + HPG * L;        // [HPG][L]
+  float* ew = ed + HPG * L;        // [HPG][T][L]
+  float* edec = ew + HPG * T * L;  // [HPG][T] e^{G_e}
+  float* acc = edec + HPG * T;     // [HPG][T][P]
 
   const M2Pos pos = m2_pos(a, slot);
   const int st = pos.st, cnt = pos.cnt, n_all = cnt + T;  // n_all <= L
-  const int64_t rh = ((int64_t)slot * a.H + h) * L, rgp = ((int64_t)slot * a.G + gr) * L;
-  for (int i = tid; i < cnt * P; i += NTH) {
-    const int e = i / P, c = i - e * P;
-    const int j = (st + e) % L;
-    rx[j * P + c] = load_elem(a.rx, (rh + j) * P + c, a.in_dt);
-  }
+  const int64_t rgp = ((int64_t)slot * a.G + gr) * L;
+  // ---- phase A: group rows, appends, gates
   for (int i = tid; i < cnt * N; i += NTH) {
     const int e = i / N, c = i - e * N;
     const int j = (st + e) % L;
     rB[j * N + c] = load_elem(a.rB, (rgp + j) * N + c, a.in_dt);
-  }
-  for (int i = tid; i < T * P; i += NTH) {
-    const int t = i / P, c = i - t * P;
-    const int64_t src = (((int64_t)b * T + t) * a.H + h) * P + c;
-    wx[i] = load_elem(a.x, src, a.in_dt);
-    copy_elem(a.rx, (rh + (st + cnt + t) % L) * P + c, a.x, src, a.in_dt);  // append x
   }
   for (int i = tid; i < T * N; i += NTH) {
     const int t = i / N, c = i - t * N;
     const int64_t src = (((int64_t)b * T + t) * a.G + gr) * N + c;
     wB[i] = load_elem(a.Bm, src, a.in_dt);
     wC[i] = load_elem(a.Cm, src, a.in_dt);
-    if (leader) copy_elem(a.rB, (rgp + (st + cnt + t) % L) * N + c, a.Bm, src, a.in_dt);  // append B
+    copy_elem(a.rB, (rgp + (st + cnt + t) % L) * N + c, a.Bm, src, a.in_dt);  // append B
   }
-  if (wave == 0) {
-    // lane j takes live entry j: committed from ring position (st + j) % L, or window position j - cnt
-    const int j = lane;
+  for (int i = tid; i < HPG * T * P; i += NTH) {  // append x
+    const int hi = i / (T * P), rem = i - hi * T * P, t = rem / P, c = rem - t * P;
+    const int64_t rh = ((int64_t)slot * a.H + h0 + hi) * L;
+    copy_elem(a.rx, (rh + (st + cnt + t) % L) * P + c, a.x, (((int64_t)b * T + t) * a.H + h0 + hi) * P + c,
+              a.in_dt);
+  }
+  for (int hi = wave; hi < HPG; hi += NW) {  // per head: lane j takes live entry j
+    const int h = h0 + hi, j = lane;
+    const int64_t rh = ((int64_t)slot * a.H + h) * L;
     float gj = 0.f, dj = 0.f;
     if (j < cnt) {
       gj = a.rg[rh + (st + j) % L];
@@ -307,64 +334,92 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
       const int t = j - cnt;
       dj = softplus_f(load_elem(a.dt, ((int64_t)b * T + t) * a.H + h, a.in_dt) + a.dt_bias[h]);
       gj = -expf(a.A_log[h]) * dj;
-      const int64_t dst = rh + (st + cnt + t) % L;  // append g and dt'
-      a.rg[dst] = gj;
-      a.rdtp[dst] = dj;
+      a.rg[rh + (st + cnt + t) % L] = gj;  // append g and dt'
+      a.rdtp[rh + (st + cnt + t) % L] = dj;
     }
-    float G_ = gj;
+    float Gs = gj;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(G_, off, 64);
-      if (j >= off) G_ += y;
+      const float y = __shfl_up(Gs, off, 64);
+      if (j >= off) Gs += y;
     }
     if (j < L) {
-      eG[j] = G_;
-      ed[j] = dj;
+      eG[hi * L + j] = Gs;
+      ed[hi * L + j] = dj;
     }
   }
   __syncthreads();
-  // weights: one thread per (t, j <= cnt + t)
-  for (int i = tid; i < T * L; i += NTH) {
-    const int t = i / L, j = i - t * L;
-    const int e_last = cnt + t;
-    float w = 0.f;
-    if (j <= e_last) {
-      const float* Bj = j < cnt ? rB + ((st + j) % L) * N : wB + (j - cnt) * N;
-      const float* Ct = wC + t * N;
-      float dot = 0.f;
-      for (int c = 0; c < N; ++c) dot = fmaf(Bj[c], Ct[c], dot);
-      w = expf(eG[e_last] - eG[j]) * ed[j] * dot;
-    }
-    ew[i] = w;
+  for (int item = wave; item < T * L; item += NW) {  // B_j . C_t, one wave per pair, lanes over n
+    const int t = item / L, j = item - t * L;
+    if (j > cnt + t) continue;
+    const float* Bj = j < cnt ? rB + ((st + j) % L) * N : wB + (j - cnt) * N;
+    const float* Ct = wC + t * N;
+    float d = 0.f;
+    for (int c = lane; c < N; c += 64) d = fmaf(Bj[c], Ct[c], d);
+    d = wave_sum(d);
+    if (lane == 0) dots[item] = d;
   }
   __syncthreads();
-  // outputs: y_t[r] = e^{G_e} (S0 C_t)[r] + sum_j w_tj x_j[r] + D x_t[r]
-  const float Dh = a.Dskip[h];
-  for (int t = 0; t < T; ++t) {
+  for (int i = tid; i < HPG * T * L; i += NTH) {  // weights per head
+    const int hi = i / (T * L), rem = i - hi * T * L, t = rem / L, j = rem - t * L;
     const int e_last = cnt + t;
-    const float decay = expf(eG[e_last]);
-    float Cc[VEC];
+    ew[i] = j <= e_last ? expf(eG[hi * L + e_last] - eG[hi * L + j]) * ed[hi * L + j] * dots[t * L + j] : 0.f;
+    if (j == 0) edec[hi * T + t] = expf(eG[hi * L + e_last]);
+  }
+  __syncthreads();
+  // acc[hi][t][r..r+3] = sum_j w x_j + D x_t, four rows per thread, x read from the ring and the window
+  for (int i = tid; i < HPG * T * (P / 4); i += NTH) {
+    const int hi = i / (T * (P / 4)), rem = i - hi * T * (P / 4), t = rem / (P / 4), r = (rem - t * (P / 4)) * 4;
+    const int h = h0 + hi;
+    const int64_t rh = ((int64_t)slot * a.H + h) * L;
+    const int64_t xw = ((int64_t)b * T * a.H + h) * P + r;  // window x of position 0
+    float v[4], xt[4];
+    load4(a.x, xw + (int64_t)t * a.H * P, a.in_dt, xt);
+    const float Dh = a.Dskip[h];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) Cc[e] = wC[t * N + c0 + e];
+    for (int e = 0; e < 4; ++e) v[e] = Dh * xt[e];
+    const float* w = ew + (hi * T + t) * L;
+    for (int j = 0; j <= cnt + t; ++j) {
+      float xj[4];
+      if (j < cnt)
+        load4(a.rx, (rh + (st + j) % L) * P + r, a.in_dt, xj);
+      else
+        load4(a.x, xw + (int64_t)(j - cnt) * a.H * P, a.in_dt, xj);
 #pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) {
-      const int r = r0 + pp * NW * RPW;
-      float s[VEC];
-      IO::widen(raw[pp], s);
-      float part = 0.f;
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(w[j], xj[e], v[e]);
+    }
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) part = fmaf(s[e], Cc[e], part);
-      part = row_sum<LPR>(part);
-      if ((lane % LPR) == 0) {
-        float yv = decay * part;
-        for (int j = 0; j <= e_last; ++j) {
-          const float xj = j < cnt ? rx[((st + j) % L) * P + r] : wx[(j - cnt) * P + r];
-          yv = fmaf(ew[t * L + j], xj, yv);
-        }
-        yv = fmaf(Dh, wx[t * P + r], yv);
-        store_elem(a.y, (((int64_t)b * T + t) * a.H + h) * P + r, yv, a.out_dt);
+    for (int e = 0; e < 4; ++e) acc[(hi * T + t) * P + r + e] = v[e];
+  }
+  __syncthreads();
+  // ---- phase B: the heads' tiles in turn, the next one's loads in flight
+  for (int hi = 0; hi < HPG; ++hi) {
+    typename IO::Raw nxt[PASSES];
+    const int hn = hi + 1 < HPG ? hi + 1 : hi;  // the last head re-reads itself (keeps the load count fixed)
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp)
+      nxt[pp] = IO::load_raw(tiles + (int64_t)hn * (P * N) + (r0 + pp * NW * RPW) * N + c0);
+    for (int t = 0; t < T; ++t) {
+      float Cc[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Cc[e] = wC[t * N + c0 + e];
+      const float decay = edec[hi * T + t];
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) {
+        const int r = r0 + pp * NW * RPW;
+        float sv[VEC];
+        IO::widen(cur[pp], sv);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) part = fmaf(sv[e], Cc[e], part);
+        part = row_sum<LPR>(part);
+        if ((lane % LPR) == 0)
+          store_elem(a.y, (((int64_t)b * T + t) * a.H + h0 + hi) * P + r, fmaf(decay, part, acc[(hi * T + t) * P + r]),
+                     a.out_dt);
       }
     }
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) cur[pp] = nxt[pp];
   }
 }
 
@@ -409,8 +464,8 @@ static hipError_t m2_launch_t(const M2Args& a, int what, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.T > 0) {
-    hipLaunchKernelGGL((gdn_m2_step_kernel<SDT, P, N, NT>), dim3(units), dim3(G::NW * 64),
-                       m2_step_floats(P, N, a.L, a.T) * sizeof(float), s, a);
+    hipLaunchKernelGGL((gdn_m2_step_kernel<SDT, P, N, NT>), dim3((unsigned)((int64_t)a.B * a.G)), dim3(G::NW * 64),
+                       m2_step_floats(P, N, a.L, a.T, a.H / a.G) * sizeof(float), s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -460,8 +515,8 @@ hipError_t launch_m2_rollback(const M2Args& a, hipStream_t s) {
   hipLaunchKernelGGL(gdn_m2_advance_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, s, a, 2);
   return hipGetLastError();
 }
-size_t m2_lds_bytes(int P, int N, int L, int T) {
-  const size_t step = T > 0 ? m2_step_floats(P, N, L, T) * sizeof(float) : 0;
+size_t m2_lds_bytes(int P, int N, int L, int T, int HPG) {
+  const size_t step = T > 0 ? m2_step_floats(P, N, L, T, HPG) * sizeof(float) : 0;
   const size_t fold = (size_t)L * (P + N + 1) * sizeof(float) + 64 * 4 + 8;
   return step > fold ? step : fold;
 }

@@ -329,8 +329,9 @@ gdn_status gdn_mamba2_decode_step(const gdn_m2_dims* dims, int32_t B, const void
  * ring emptied; then the window is appended at (start + count + t) mod L and
  * count += T; window position t outputs y computed from the checkpoint
  * advanced over the first count_before + t + 1 live entries (without writing
- * it).  Dynamic shared memory must fit 64 KiB:
- * 4 (L (d + n + 3) + T (d + 2 n + L)) bytes, else GDN_EUNSUPPORTED. */
+ * it).  x and the ring's x must be 16-byte aligned.  With HPG = H / G heads
+ * per group, 4 (L n + 2 T n + T L + HPG (2 L + T L + T + T d)) bytes of
+ * staging must fit 64 KiB, else GDN_EUNSUPPORTED. */
 gdn_status gdn_mamba2_replay_decode(const gdn_m2_dims* dims, int32_t B, int32_t T, const void* x,
                                     const void* Bm, const void* Cm, gdn_dtype in_dtype,
                                     const gdn_m2_params* params, const gdn_pool* ckpt,
