@@ -277,4 +277,64 @@ struct TileGeom {
   static_assert(LPR * VEC == D && LPR * RPW == 64 && PASSES * RPW * NW == D, "tile geometry");
 };
 
+// ------------------------------------------------------------------ packed rows on MFMA
+// Rows of keys / queries kept packed in LDS in their input dtype (row stride
+// ldw words) and widened on use.
+template <int EB>
+struct PackedRow {
+  // element c of a packed row (EB = 4: f32 words; EB = 2: bf16 / f16 pairs)
+  __device__ __forceinline__ static float get(const uint32_t* row, int c, int dt) {
+    if constexpr (EB == 4) {
+      return __uint_as_float(row[c]);
+    } else {
+      const uint32_t w = row[c >> 1];
+      const uint32_t h16 = (c & 1) ? (w >> 16) : (w & 0xffffu);
+      return dt == GDN_BF16 ? bf16_bits_to_f32(h16) : f16_bits_to_f32(h16);
+    }
+  }
+};
+
+// One 16 x 16 tile of X Y^T over D columns on MFMA, X and Y packed rows in
+// LDS (row stride ldw words); rows at or beyond nx / ny read as zero.  Lane l
+// supplies X[l % 16][k-block l / 16] and Y[l % 16][same block]; element r of
+// the result is (4 (l / 16) + r, l % 16).  16-bit rows use the gfx950
+// 16x16x32 bf16 / f16 instructions (products of two 16-bit values are exact in
+// FP32), f32 rows the 16x16x4 f32 one.
+template <int D, int EB>
+__device__ __forceinline__ f32x4 tile_xyt(const uint32_t* X, int nx, const uint32_t* Y, int ny, int ldw, int dt,
+                                          int lane) {
+  const int i = lane & 15, kb = lane >> 4;
+  const bool xv = i < nx, yv = i < ny;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (EB == 2) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int s = 0; s < (D + 31) / 32; ++s) {
+      const int w0 = 16 * s + 4 * kb;  // word of element 32 s + 8 kb; words past D / 2 read as zero
+      const bool kv = w0 < D / 2;
+      u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (xv && kv) a[w] = X[i * ldw + w0 + w];
+        if (yv && kv) b[w] = Y[i * ldw + w0 + w];
+      }
+      if (dt == GDN_BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                     0, 0, 0);
+    }
+  } else {
+#pragma unroll 8
+    for (int s = 0; s < D / 4; ++s) {
+      const float a = xv ? __uint_as_float(X[i * ldw + 4 * s + kb]) : 0.f;
+      const float b = yv ? __uint_as_float(Y[i * ldw + 4 * s + kb]) : 0.f;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 }  // namespace gdn

@@ -69,8 +69,10 @@ __device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
 // ---------------------------------------------------------------- kernel 1
 template <int D, int EB>
 __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
-  constexpr int LDK = D + 4, LDT = kC + 4;
-  __shared__ float s_k[kC][LDK], s_q[kC][LDK];
+  constexpr int LDT = kC + 4;
+  constexpr int LDW = D * EB / 4 + 1;  // words per packed key / query row (+1: bank spread)
+  constexpr int VE = 16 / EB, CPR = D / VE;
+  __shared__ uint32_t s_k[kC * LDW], s_q[kC * LDW];
   __shared__ float s_A[kC][LDT], s_T[kC][LDT];
   __shared__ float s_M[4][16][20];
   __shared__ float s_g[kC], s_beta[kC], s_gam[kC];
@@ -94,13 +96,34 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   const int len = min(kC, seq_hi - t0);
   const int hk = h / (p.Hv / p.Hk);
 
+  // keys and queries stay packed in their input dtype; rows >= len are never
+  // read (the tile products treat them as zero)
   {
-    RowStager<D, kC, 256, EB> sk, sq;
-    auto row = [&](int t) { return ((int64_t)(t0 + t) * p.Hk + hk) * D; };
-    sk.issue(p.k, len, row);
-    sq.issue(p.q, len, row);
-    sk.commit(&s_k[0][0], LDK, p.in_dt);
-    sq.commit(&s_q[0][0], LDK, p.in_dt);
+    constexpr int IT = (kC * CPR + 255) / 256;
+    u32x4 xk[IT], xq[IT];
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+      const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
+      u32x4 zk = {0u, 0u, 0u, 0u}, zq = zk;
+      if (x < kC * CPR && r < len) {
+        const int64_t off = (((int64_t)(t0 + r) * p.Hk + hk) * D + cc * VE) * EB;
+        zk = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
+        zq = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
+      }
+      xk[u] = zk;
+      xq[u] = zq;
+    }
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+      const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
+      if (x < kC * CPR && r < len) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          s_k[r * LDW + cc * 4 + w] = xk[u][w];
+          s_q[r * LDW + cc * 4 + w] = xq[u][w];
+        }
+      }
+    }
   }
   if (tid < kC) {
     float g = 0.f, be = 0.f;
@@ -131,14 +154,9 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   for (int job = wave; job < 32; job += 4) {
     const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (J <= I) {
-      if (isP)
-        acc = mma16<D>(acc, [&](int i, int k) { return s_q[16 * I + i][k]; },
-                       [&](int k, int j) { return s_k[16 * J + j][k]; }, lane);
-      else
-        acc = mma16<D>(acc, [&](int i, int k) { return s_k[16 * I + i][k]; },
-                       [&](int k, int j) { return s_k[16 * J + j][k]; }, lane);
-    }
+    if (J <= I)  // X Y^T on MFMA (16-bit rows: the exact bf16 / f16 products, fp32 accumulation)
+      acc = tile_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, len - 16 * I, s_k + 16 * J * LDW, len - 16 * J, LDW,
+                            p.in_dt, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * I + acc_row(lane, r), s = 16 * J + acc_col(lane);
@@ -202,15 +220,28 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
 }
 
 // ---------------------------------------------------------------- kernel 2
+// dv columns per state-kernel workgroup (a multiple of 16)
+#ifndef GDN_PREFILL_BV
+#define GDN_PREFILL_BV 32
+#endif
+
+// waves of a state-kernel workgroup: its LDS allows one workgroup per CU, so
+// the waves are what hides latency (measured on MI355X: 4 waves 2.19 ms, 8
+// waves 1.53 ms, 16 waves 1.30 ms for the 4-sequence workload)
+#ifndef GDN_PREFILL_STATE_WAVES
+#define GDN_PREFILL_STATE_WAVES 16
+#endif
+constexpr int kStateThreads = 64 * GDN_PREFILL_STATE_WAVES;
+
 template <int D>
 struct PrefillGeom {
-  static constexpr int BV = D < 32 ? D : 32;  // dv columns per workgroup
+  static constexpr int BV = D < GDN_PREFILL_BV ? D : GDN_PREFILL_BV;  // dv columns per workgroup
   static constexpr int NB = D / BV;
   static constexpr int NJ = BV / 16;
 };
 
 template <int SDT, int D, int EB>
-__global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArgs p, const float* __restrict__ ws) {
+__global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const PrefillArgs p, const float* __restrict__ ws) {
   using G = PrefillGeom<D>;
   constexpr int BV = G::BV, NB = G::NB, NJ = G::NJ;
   constexpr int LDK = D + 4, LDV = BV + 4, LDT = kC + 4;
@@ -239,7 +270,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
   const int col0 = blk * BV;
   const int slot = p.slot_map[n];
   if (slot < 0 || (int64_t)slot >= p.num_slots) {  // padded sequence: zero outputs
-    for (int i = tid; i < len * BV; i += 256) {
+    for (int i = tid; i < len * BV; i += kStateThreads) {
       const int t = i / BV, j = i - t * BV;
       store_elem(p.out, ((int64_t)(seq_lo + t) * p.Hv + h) * D + col0 + j, 0.f, p.out_dt);
     }
@@ -247,7 +278,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
   }
   using ST = typename StateElem<SDT>::T;
   ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot * p.Hv + h) * (int64_t)(D * D);
-  for (int i = tid; i < D * BV; i += 256) {
+  for (int i = tid; i < D * BV; i += kStateThreads) {
     const int r = i / BV, j = i - r * BV;
     s_S[r][j] = load_elem(tile, (int64_t)r * D + col0 + j, SDT);
   }
@@ -260,10 +291,10 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
 
   // chunk inputs are staged through registers: the loads of chunk c + 1 are
   // issued right after chunk c reaches LDS and complete under its GEMMs
-  RowStager<D, kC, 256, EB> stk, stq;
-  RowStager<BV, kC, 256, EB> stv;
-  RowStager<kC, kC, 256, 4> stT, stP;
-  RowStager<kC, 2, 256, 4> stg;
+  RowStager<D, kC, kStateThreads, EB> stk, stq;
+  RowStager<BV, kC, kStateThreads, EB> stv;
+  RowStager<kC, kC, kStateThreads, 4> stT, stP;
+  RowStager<kC, 2, kStateThreads, 4> stg;
   auto issue = [&](int c) {
     const int t0 = seq_lo + c * kC;
     const int L = min(kC, seq_hi - t0);
@@ -297,7 +328,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
     }
 
     // X = [K; Q] S
-    for (int job = wave; job < 8 * NJ; job += 4) {
+    for (int job = wave; job < 8 * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if (I < 4)
@@ -311,13 +342,13 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
     }
     __syncthreads();
     // R = diag(beta) (V - diag(e^gamma) K S)   (overwrites Q)
-    for (int i = tid; i < kC * BV; i += 256) {
+    for (int i = tid; i < kC * BV; i += kStateThreads) {
       const int t = i / BV, j = i - t * BV;
       s_R[t * LDV + j] = s_beta[t] * (s_v[t][j] - s_eg[t] * s_X[t][j]);
     }
     __syncthreads();
     // U = T R
-    for (int job = wave; job < 4 * NJ; job += 4) {
+    for (int job = wave; job < 4 * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       acc = mma16<kC>(acc, [&](int i, int k) { return s_T[16 * I + i][k]; },
@@ -328,7 +359,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
     __syncthreads();
     // O = scale (diag(e^gamma) Q S + P U)  and  S <- e^{gamma_C} S + (diag(dec) K)^T U
     const float egC = s_egC;
-    for (int job = wave; job < (4 + D / 16) * NJ; job += 4) {
+    for (int job = wave; job < (4 + D / 16) * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc;
       if (I < 4) {
@@ -358,7 +389,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_state_kernel(const PrefillArg
     }
     __syncthreads();
   }
-  for (int i = tid; i < D * BV; i += 256) {
+  for (int i = tid; i < D * BV; i += kStateThreads) {
     const int r = i / BV, j = i - r * BV;
     store_elem(tile, (int64_t)r * D + col0 + j, s_S[r][j], SDT);
   }
@@ -374,13 +405,13 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws
   const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
   switch (state_dt) {
     case GDN_F32:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
       break;
     case GDN_BF16:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
       break;
     case GDN_F16:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(256), 0, s, a, ws);
+      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
       break;
     default: return hipErrorInvalidValue;
   }
