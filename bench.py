@@ -420,7 +420,7 @@ def bench_copy_blocks(torch, gdn, reps=8, P=16, slots=64, jobs=32):
     ms = t["span_ms"] / reps
     res = {"P": P, "jobs": jobs, "slot_MiB": slot_bytes / 2 ** 20, "ms_per_call": round(ms, 4),
            "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes,
-           "roofline": roofline_bw(nbytes, t["mean_launch_ms"], None)}
+           "roofline": roofline_bw(nbytes, t["mean_launch_ms"], traffic_for("blockcopy", ["gdn_copy.hip", "gdn_device.h"]))}
     del tensors
     torch.cuda.empty_cache()
     return res
@@ -450,7 +450,7 @@ def cpu_baseline(gen, seconds=12.0):
     B, cid = 256, 1
     slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
     A_log, dt_bias = gen.head_params(cid, HV)
-    rows, done, elapsed, step = 16, 0, 0.0, 0
+    rows, done, elapsed, step = 64, 0, 0.0, 0
     pool = gen.pool_slots(cid, slot_map[:rows], HV, D, D, "f32")
     local = list(range(rows))
     while elapsed < seconds and step < 64:
