@@ -33,7 +33,7 @@
 namespace gdn {
 
 constexpr int kC = 64;                        // chunk length
-constexpr int kWsFloats = 2 * kC * kC + 2 * kC;  // T, P, gamma, beta per (chunk slot, head)
+constexpr int kWsFloats = 2 * kC * kC + 4 * kC;  // T, P, gamma, beta, e^gamma, e^{gamma_C - gamma} per (chunk slot, head)
 
 // Chunk slot of chunk c of sequence n: n + floor(cu[n] / C) + c.  It is unique
 // and below N + ceil(total / C) (floor((x+l)/C) >= floor(x/C) + ceil(l/C) - 1).
@@ -216,6 +216,8 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   if (tid < kC) {
     wsp[2 * kC * kC + tid] = s_gam[tid];
     wsp[2 * kC * kC + kC + tid] = s_beta[tid];
+    wsp[2 * kC * kC + 2 * kC + tid] = expf(s_gam[tid]);
+    wsp[2 * kC * kC + 3 * kC + tid] = expf(s_gam[kC - 1] - s_gam[tid]);
   }
 }
 
@@ -395,6 +397,325 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
   }
 }
 
+// ---------------------------------------------------------------- kernel 2, 16-bit inputs
+// The same sequential chunk loop for bf16 / f16 inputs, with every MFMA operand
+// read from LDS as 16-byte runs along the contraction index.  In a block of 32
+// k values, lane (i, kk) of v_mfma_f32_16x16x4_f32 takes k = 32 b + 8 kk + s in
+// the s-th of eight consecutive instructions: that is a permutation of the
+// block's k, applied alike to both operands, so each lane fetches its eight A
+// values and its eight B values with one or two ds_read_b128 each.  Operands
+// are kept k-contiguous: K and Q rows packed 16-bit, T and P rows fp32, and
+// the B sides transposed (S^T, V^T -> R^T, U^T, and K^T for the state update,
+// built from the K loads with one lane exchange).  Every row stride is 4 times
+// an odd number of 32-bit words, so the 16 rows of a tile start in distinct
+// banks.  16 waves: P1 forms [K S] on waves 0-7 (epilogue: R^T in place of
+// V^T) and [Q S] on waves 8-15 (kept in registers), P2 U = T R on waves 0-7,
+// P3 the outputs on waves 8-15 and the state update on every wave.
+constexpr int kS16Threads = 1024;
+
+template <int IDT>
+__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (IDT == GDN_BF16) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      f[2 * i] = f16_bits_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// acc += A (16 x 32 block b) B: a[8] and b[8] hold this lane's eight k values
+__device__ __forceinline__ f32x4 mfma8(f32x4 acc, const float* a, const float* b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+  return acc;
+}
+
+template <int SDT, int D, int IDT>
+__global__ void __launch_bounds__(kS16Threads) gdn_prefill_state16_kernel(const PrefillArgs p, const float* __restrict__ ws) {
+  constexpr int BV = 32, NB = D / BV, NT = kS16Threads;
+  static_assert(D == 64 || D == 128, "16-bit state kernel: D = 64 or 128");
+  constexpr int LKW = D / 2 + 4;  // 32-bit words per packed K / Q row
+  constexpr int LTW = kC / 2 + 4; // words per packed K^T row
+  constexpr int LTF = kC + 4;     // floats per T / P / V^T (R^T) / U^T row
+  constexpr int LSF = D + 4;      // floats per S^T row
+  __shared__ __align__(16) uint32_t s_k[kC * LKW];
+  __shared__ __align__(16) uint32_t s_q[kC * LKW];
+  __shared__ __align__(16) uint32_t s_kt[D * LTW];
+  __shared__ __align__(16) float s_T[kC * LTF];
+  __shared__ __align__(16) float s_P[kC * LTF];
+  __shared__ __align__(16) float s_St[BV * LSF];
+  __shared__ __align__(16) float s_Rt[BV * LTF];  // V^T, overwritten by R^T
+  __shared__ __align__(16) float s_Ut[BV * LTF];
+  __shared__ __align__(16) float s_g[4 * kC];     // gamma, beta, e^gamma, e^{gamma_C - gamma}
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kk = lane >> 4;
+  const int bid = blockIdx.x;  // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
+  const int x8 = bid & 7, y = bid >> 3;
+  const int blk = y % NB;
+  const int unit = (y / NB) * 8 + x8;
+  if (unit >= p.N * p.Hv) return;
+  const int n = unit / p.Hv, h = unit - n * p.Hv;
+  const int hk = h / (p.Hv / p.Hk);
+  const int seq_lo = p.cu_seqlens[n], seq_hi = p.cu_seqlens[n + 1];
+  const int len = seq_hi - seq_lo;
+  if (len <= 0) return;
+  const int col0 = blk * BV;
+  const int slot = p.slot_map[n];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) {  // padded sequence: zero outputs
+    for (int i = tid; i < len * BV; i += NT) {
+      const int t = i / BV, j = i - t * BV;
+      store_elem(p.out, ((int64_t)(seq_lo + t) * p.Hv + h) * D + col0 + j, 0.f, p.out_dt);
+    }
+    return;
+  }
+  using ST = typename StateElem<SDT>::T;
+  ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot * p.Hv + h) * (int64_t)(D * D);
+  for (int i = tid; i < D * BV; i += NT) {
+    const int r = i / BV, j = i - r * BV;
+    s_St[j * LSF + r] = load_elem(tile, (int64_t)r * D + col0 + j, SDT);
+  }
+  const int nch = (len + kC - 1) / kC;
+
+  // chunk inputs staged through registers: the loads of chunk c + 1 are issued
+  // right after chunk c reaches LDS and complete under its products.
+  //   Q: 8 elements a lane, row-major order;  K: 8 elements a lane, a wave per
+  //   8-column strip over the 64 rows (for the K^T exchange);  V: 8 columns
+  //   of one row, a wave per strip;  T, P: 4 floats a lane;  gates: 4 floats.
+  constexpr int KL = kC * D / 8;  // 16-byte loads of K (and of Q): 1024 or 512
+  static_assert(KL <= NT, "one K load per lane");
+  u32x4 rk, rq, rv;
+  f32x4 rT, rP, rg;
+  auto issue = [&](int c) {
+    const int t0 = seq_lo + c * kC;
+    const int L = min(kC, seq_hi - t0);
+    const float* wsp = ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    rk = z;
+    rq = z;
+    rv = z;
+    if (tid < KL) {
+      const int kr = tid & 63, kc = tid >> 6;
+      if (kr < L)
+        rk = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.k) +
+                                             ((int64_t)(t0 + kr) * p.Hk + hk) * D + kc * 8);
+      const int qr = tid / (D / 8), qc = tid - qr * (D / 8);
+      if (qr < L)
+        rq = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
+                                             ((int64_t)(t0 + qr) * p.Hk + hk) * D + qc * 8);
+    }
+    if (tid < kC * (BV / 8)) {
+      const int vr = tid & 63, vc = tid >> 6;
+      if (vr < L)
+        rv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.v) +
+                                             ((int64_t)(t0 + vr) * p.Hv + h) * D + col0 + vc * 8);
+    }
+    rT = ld4(wsp + 4 * tid);
+    rP = ld4(wsp + kC * kC + 4 * tid);
+    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+    rg = tid < kC ? ld4(wsp + 2 * kC * kC + 4 * tid) : zf;
+  };
+  auto commit = [&]() {
+    if (tid < KL) {
+      const int qr = tid / (D / 8), qc = tid - qr * (D / 8);
+      *reinterpret_cast<u32x4*>(s_q + qr * LKW + qc * 4) = rq;
+      const int kr = tid & 63, kc = tid >> 6;
+      *reinterpret_cast<u32x4*>(s_k + kr * LKW + kc * 4) = rk;
+      // K^T: rows kc*8 .. kc*8+7, columns kr.  Lanes 2m and 2m+1 hold rows kr and
+      // kr+1; after one exchange the even lane writes the (kr, kr+1) pairs of
+      // columns 0-3 of the strip and the odd lane those of columns 4-7.
+      const bool odd = kr & 1;
+      const uint32_t give0 = odd ? rk[0] : rk[2], give1 = odd ? rk[1] : rk[3];
+      const uint32_t own0 = odd ? rk[2] : rk[0], own1 = odd ? rk[3] : rk[1];
+      const uint32_t got0 = __shfl_xor(give0, 1, 64), got1 = __shfl_xor(give1, 1, 64);
+      uint32_t* kt = s_kt + (kc * 8 + (odd ? 4 : 0)) * LTW + (kr >> 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t ow = m < 2 ? own0 : own1, gw = m < 2 ? got0 : got1;
+        const uint32_t mine = (m & 1) ? (ow >> 16) : (ow & 0xffffu);
+        const uint32_t theirs = (m & 1) ? (gw >> 16) : (gw & 0xffffu);
+        kt[m * LTW] = odd ? (theirs | (mine << 16)) : (mine | (theirs << 16));
+      }
+    }
+    if (tid < kC * (BV / 8)) {
+      const int vr = tid & 63, vc = tid >> 6;
+      float f[8];
+      unpack8<IDT>(rv, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_Rt[(vc * 8 + e) * LTF + vr] = f[e];
+    }
+    {
+      const int r = tid >> 4, c4 = (tid & 15) * 4;
+      *reinterpret_cast<f32x4*>(s_T + r * LTF + c4) = rT;
+      *reinterpret_cast<f32x4*>(s_P + r * LTF + c4) = rP;
+    }
+    if (tid < kC) *reinterpret_cast<f32x4*>(s_g + 4 * tid) = rg;
+  };
+  const float* s_beta = s_g + kC;
+  const float* s_eg = s_g + 2 * kC;
+  const float* s_dec = s_g + 3 * kC;
+
+  issue(0);
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = seq_lo + c * kC;
+    const int L = min(kC, seq_hi - t0);
+    commit();
+    __syncthreads();
+    if (c + 1 < nch) issue(c + 1);
+
+    // ---- P1: [K S] (waves 0-7) and [Q S] (waves 8-15), tile rows 16 I.., columns 16 J..
+    const int jw = wave & 7, I = jw >> 1, J = jw & 1;
+    f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint32_t* A = (wave < 8 ? s_k : s_q) + (16 * I + li) * LKW + 4 * kk;
+      const float* Bt = s_St + (16 * J + li) * LSF + 8 * kk;
+      u32x4 aw[D / 32];
+      f32x4 bw[D / 16];
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        aw[b] = *reinterpret_cast<const u32x4*>(A + 16 * b);
+        bw[2 * b] = ld4(Bt + 32 * b);
+        bw[2 * b + 1] = ld4(Bt + 32 * b + 4);
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        float a[8], bb[8];
+        unpack8<IDT>(aw[b], a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bb[e] = bw[2 * b][e];
+          bb[4 + e] = bw[2 * b + 1][e];
+        }
+        acc = mfma8(acc, a, bb);
+      }
+      if (wave < 8) {  // R^T[j][t] = beta_t (V^T[j][t] - e^{gamma_t} (K S)[t][j]), in place
+        float* rt = s_Rt + (16 * J + li) * LTF + 16 * I + 4 * kk;
+        const f32x4 vt = ld4(rt), be = ld4(s_beta + 16 * I + 4 * kk), eg = ld4(s_eg + 16 * I + 4 * kk);
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = be[e] * (vt[e] - eg[e] * acc[e]);
+        *reinterpret_cast<f32x4*>(rt) = r;
+      } else {
+        qs = acc;
+      }
+    }
+    __syncthreads();
+    // ---- P2: U = T R on waves 0-7, stored as U^T
+    if (wave < 8) {
+      const float* A = s_T + (16 * I + li) * LTF + 8 * kk;
+      const float* Bt = s_Rt + (16 * J + li) * LTF + 8 * kk;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < kC / 32; ++b) {
+        float a[8], bb[8];
+        const f32x4 a0 = ld4(A + 32 * b), a1 = ld4(A + 32 * b + 4);
+        const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a0[e];
+          a[4 + e] = a1[e];
+          bb[e] = b0[e];
+          bb[4 + e] = b1[e];
+        }
+        acc = mfma8(acc, a, bb);
+      }
+      *reinterpret_cast<f32x4*>(s_Ut + (16 * J + li) * LTF + 16 * I + 4 * kk) = acc;
+    }
+    __syncthreads();
+    // ---- P3: O = scale (e^gamma [Q S] + P U) on waves 8-15
+    if (wave >= 8) {
+      const float* A = s_P + (16 * I + li) * LTF + 8 * kk;
+      const float* Bt = s_Ut + (16 * J + li) * LTF + 8 * kk;
+      const f32x4 eg = ld4(s_eg + 16 * I + 4 * kk);
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = eg[e] * qs[e];
+#pragma unroll
+      for (int b = 0; b < kC / 32; ++b) {
+        float a[8], bb[8];
+        const f32x4 a0 = ld4(A + 32 * b), a1 = ld4(A + 32 * b + 4);
+        const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a0[e];
+          a[4 + e] = a1[e];
+          bb[e] = b0[e];
+          bb[4 + e] = b1[e];
+        }
+        acc = mfma8(acc, a, bb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * kk + e;
+        if (t < L)
+          store_elem(p.out, ((int64_t)(t0 + t) * p.Hv + h) * D + col0 + 16 * J + li, p.scale * acc[e], p.out_dt);
+      }
+    }
+    // ---- P3: S <- e^{gamma_C} S + (diag(dec) K)^T U; tile rows 16 Is.. of S, columns 16 Js..
+    {
+      const float egC = s_eg[kC - 1];
+      for (int job = wave; job < (D / 16) * 2; job += NT / 64) {
+        const int Is = job >> 1, Js = job & 1;
+        const uint32_t* A = s_kt + (16 * Is + li) * LTW + 4 * kk;
+        const float* Bt = s_Ut + (16 * Js + li) * LTF + 8 * kk;
+        f32x4* Sp = reinterpret_cast<f32x4*>(s_St + (16 * Js + li) * LSF + 16 * Is + 4 * kk);
+        f32x4 acc = *Sp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= egC;
+        u32x4 aw[kC / 32];
+#pragma unroll
+        for (int b = 0; b < kC / 32; ++b) aw[b] = *reinterpret_cast<const u32x4*>(A + 16 * b);
+#pragma unroll
+        for (int b = 0; b < kC / 32; ++b) {
+          float a[8], bb[8];
+          unpack8<IDT>(aw[b], a);
+          const f32x4 d0 = ld4(s_dec + 32 * b + 8 * kk), d1 = ld4(s_dec + 32 * b + 8 * kk + 4);
+          const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] *= d0[e];
+            a[4 + e] *= d1[e];
+            bb[e] = b0[e];
+            bb[4 + e] = b1[e];
+          }
+          acc = mfma8(acc, a, bb);
+        }
+        // element e of lane (li, kk) is S(16 Is + 4 kk + e, 16 Js + li)
+        *Sp = acc;
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < D * BV; i += NT) {
+    const int r = i / BV, j = i - r * BV;
+    store_elem(tile, (int64_t)r * D + col0 + j, s_St[j * LSF + r], SDT);
+  }
+}
+
+template <int D, int IDT>
+static hipError_t launch_state16(const PrefillArgs& a, int state_dt, unsigned grid, float* ws, hipStream_t s) {
+  switch (state_dt) {
+    case GDN_F32:
+      hipLaunchKernelGGL((gdn_prefill_state16_kernel<GDN_F32, D, IDT>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    case GDN_BF16:
+      hipLaunchKernelGGL((gdn_prefill_state16_kernel<GDN_BF16, D, IDT>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    case GDN_F16:
+      hipLaunchKernelGGL((gdn_prefill_state16_kernel<GDN_F16, D, IDT>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int EB>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
   const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens);
@@ -402,20 +723,26 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.N * a.Hv;
-  const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
-  switch (state_dt) {
-    case GDN_F32:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
-      break;
-    case GDN_BF16:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
-      break;
-    case GDN_F16:
-      hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
-      break;
-    default: return hipErrorInvalidValue;
+  if constexpr (EB == 2 && (D == 64 || D == 128)) {  // 16-bit inputs, wide heads: the k-contiguous kernel
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / 32));
+    return a.in_dt == GDN_BF16 ? launch_state16<D, GDN_BF16>(a, state_dt, grid, ws, s)
+                               : launch_state16<D, GDN_F16>(a, state_dt, grid, ws, s);
+  } else {
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
+    switch (state_dt) {
+      case GDN_F32:
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        break;
+      case GDN_BF16:
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        break;
+      case GDN_F16:
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <int D>

@@ -179,8 +179,8 @@ def test_replay_flush_and_rollback_validation(L):
 def test_prefill_validation_and_workspace(L):
     dims = _dims()
     need = L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 64)
-    # (N + ceil(T / 64)) chunk slots x Hv x (2 * 64 * 64 + 2 * 64) floats
-    assert need == (4 + 319) * 32 * (2 * 64 * 64 + 128) * 4
+    # (N + ceil(T / 64)) chunk slots x Hv x (2 * 64 * 64 + 4 * 64) floats
+    assert need == (4 + 319) * 32 * (2 * 64 * 64 + 256) * 4
     assert L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 32) == 0
 
     def call(N=4, T=20408, chunk=64, ws=FAKE, wsb=need, cu=FAKE):

@@ -75,6 +75,14 @@ def test_prefill_ragged_lengths(sdt):
     run_prefill(70, [1, 63, 64, 65, 0, 130], 2, 4, 32, sdt, a_shift=-1.0)
 
 
+@pytest.mark.parametrize("in_dt", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_ragged_lengths_wide_heads(D, in_dt):
+    """Head dims 64 and 128 with 16-bit inputs (the k-contiguous state kernel): partial, exact and
+    empty chunks, GQA with two value heads per key head."""
+    run_prefill(74 + D, [1, 63, 64, 65, 0, 130], 2, 4, D, "f32", in_dt=in_dt, a_shift=-1.0)
+
+
 @pytest.mark.parametrize("D", [16, 64, 128])
 def test_prefill_head_dims(D):
     run_prefill(71 + D, [100, 37, 192], 1, 2, D, "f32")
