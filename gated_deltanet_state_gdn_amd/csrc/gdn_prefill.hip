@@ -398,19 +398,24 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
 }
 
 // ---------------------------------------------------------------- kernel 2, 16-bit inputs
-// The same sequential chunk loop for bf16 / f16 inputs, with every MFMA operand
-// read from LDS as 16-byte runs along the contraction index.  In a block of 32
-// k values, lane (i, kk) of v_mfma_f32_16x16x4_f32 takes k = 32 b + 8 kk + s in
-// the s-th of eight consecutive instructions: that is a permutation of the
-// block's k, applied alike to both operands, so each lane fetches its eight A
-// values and its eight B values with one or two ds_read_b128 each.  Operands
-// are kept k-contiguous: K and Q rows packed 16-bit, T and P rows fp32, and
-// the B sides transposed (S^T, V^T -> R^T, U^T, and K^T for the state update,
-// built from the K loads with one lane exchange).  Every row stride is 4 times
-// an odd number of 32-bit words, so the 16 rows of a tile start in distinct
-// banks.  16 waves: P1 forms [K S] on waves 0-7 (epilogue: R^T in place of
-// V^T) and [Q S] on waves 8-15 (kept in registers), P2 U = T R on waves 0-7,
-// P3 the outputs on waves 8-15 and the state update on every wave.
+// The same sequential chunk loop for bf16 / f16 inputs at head dims 64 and 128,
+// arranged so that the MFMA pipes see little but MFMAs:
+//  * In a block of 32 k values, lane (i, kk) of v_mfma_f32_16x16x4_f32 takes
+//    k = 32 b + 8 kk + s in the s-th of eight consecutive instructions (one
+//    permutation of the block's k for both operands), so every operand is a
+//    16-byte run along k.
+//  * The row-side operands that come from memory (K or Q rows for [K S] /
+//    [Q S], T or P rows for T R / P U) are loaded by each wave straight into
+//    registers, for chunk c + 1 as soon as chunk c has used them; they never
+//    pass through LDS.
+//  * LDS holds what the loop produces (S^T, R^T, U^T) and K^T for the state
+//    update.  K^T is double-buffered: waves 8-15, idle while waves 0-7 form
+//    U = T R, build chunk c + 1's K^T from a one-chunk-ahead register copy,
+//    with one lane exchange per row pair and an XOR swizzle of 16-byte
+//    column groups that keeps both its writes and its reads free of bank
+//    conflicts.  The gate vectors are double-buffered alongside.
+// Three barriers per chunk: after [K S] / [Q S] (R^T ready), after U = T R
+// (U^T ready), after the outputs and the state update (S^T ready).
 constexpr int kS16Threads = 1024;
 
 template <int IDT>
@@ -427,32 +432,47 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
   }
 }
 
+template <int IDT>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (IDT == GDN_BF16) return __uint_as_float(h << 16);
+  else return f16_bits_to_f32(h);
+}
+
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-// acc += A (16 x 32 block b) B: a[8] and b[8] hold this lane's eight k values
+// acc += A B over one block of 32 k: a[8] and b[8] hold this lane's eight k values
 __device__ __forceinline__ f32x4 mfma8(f32x4 acc, const float* a, const float* b) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
   return acc;
 }
 
+// One output element through a buffer resource: stores at or past the
+// resource's byte size are dropped by the hardware, so every lane issues the
+// same store whether or not its row exists (keeps vector-memory counts static).
+__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, int byte_off, float x, int dt) {
+  if (dt == GDN_F32) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, byte_off, 0, 0);
+  } else if (dt == GDN_BF16) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, byte_off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)x), r, byte_off, 0, 0);
+  }
+}
+
 template <int SDT, int D, int IDT>
 __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state16_kernel(const PrefillArgs p, const float* __restrict__ ws) {
-  constexpr int BV = 32, NB = D / BV, NT = kS16Threads;
+  constexpr int BV = 32, NB = D / BV, NT = kS16Threads, KB = D / 32;
   static_assert(D == 64 || D == 128, "16-bit state kernel: D = 64 or 128");
-  constexpr int LKW = D / 2 + 4;  // 32-bit words per packed K / Q row
-  constexpr int LTW = kC / 2 + 4; // words per packed K^T row
-  constexpr int LTF = kC + 4;     // floats per T / P / V^T (R^T) / U^T row
-  constexpr int LSF = D + 4;      // floats per S^T row
-  __shared__ __align__(16) uint32_t s_k[kC * LKW];
-  __shared__ __align__(16) uint32_t s_q[kC * LKW];
-  __shared__ __align__(16) uint32_t s_kt[D * LTW];
-  __shared__ __align__(16) float s_T[kC * LTF];
-  __shared__ __align__(16) float s_P[kC * LTF];
+  constexpr int LTW = kC / 2 + 4;  // words per K^T row: 8 column groups of 4 words (swizzled) + pad
+  constexpr int LTF = kC + 4;      // floats per R^T / U^T row
+  constexpr int LSF = D + 4;       // floats per S^T row
+  constexpr int KTL = kC * D / 8 / 512;  // K^T loads per lane of waves 8-15
+  __shared__ __align__(16) uint32_t s_kt[2][D * LTW];
   __shared__ __align__(16) float s_St[BV * LSF];
-  __shared__ __align__(16) float s_Rt[BV * LTF];  // V^T, overwritten by R^T
+  __shared__ __align__(16) float s_Rt[BV * LTF];
   __shared__ __align__(16) float s_Ut[BV * LTF];
-  __shared__ __align__(16) float s_g[4 * kC];     // gamma, beta, e^gamma, e^{gamma_C - gamma}
+  __shared__ __align__(16) float s_g[2][4 * kC];  // gamma, beta, e^gamma, e^{gamma_C - gamma}
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
@@ -482,201 +502,200 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state16_kernel(const 
     s_St[j * LSF + r] = load_elem(tile, (int64_t)r * D + col0 + j, SDT);
   }
   const int nch = (len + kC - 1) / kC;
+  auto chunk_len = [&](int c) { return min(kC, len - c * kC); };
+  auto chunk_ws = [&](int c) { return ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats; };
 
-  // chunk inputs staged through registers: the loads of chunk c + 1 are issued
-  // right after chunk c reaches LDS and complete under its products.
-  //   Q: 8 elements a lane, row-major order;  K: 8 elements a lane, a wave per
-  //   8-column strip over the 64 rows (for the K^T exchange);  V: 8 columns
-  //   of one row, a wave per strip;  T, P: 4 floats a lane;  gates: 4 floats.
-  constexpr int KL = kC * D / 8;  // 16-byte loads of K (and of Q): 1024 or 512
-  static_assert(KL <= NT, "one K load per lane");
-  u32x4 rk, rq, rv;
-  f32x4 rT, rP, rg;
-  auto issue = [&](int c) {
-    const int t0 = seq_lo + c * kC;
-    const int L = min(kC, seq_hi - t0);
-    const float* wsp = ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    rk = z;
-    rq = z;
-    rv = z;
-    if (tid < KL) {
-      const int kr = tid & 63, kc = tid >> 6;
-      if (kr < L)
-        rk = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.k) +
-                                             ((int64_t)(t0 + kr) * p.Hk + hk) * D + kc * 8);
-      const int qr = tid / (D / 8), qc = tid - qr * (D / 8);
-      if (qr < L)
-        rq = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
-                                             ((int64_t)(t0 + qr) * p.Hk + hk) * D + qc * 8);
-    }
-    if (tid < kC * (BV / 8)) {
-      const int vr = tid & 63, vc = tid >> 6;
-      if (vr < L)
-        rv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.v) +
-                                             ((int64_t)(t0 + vr) * p.Hv + h) * D + col0 + vc * 8);
-    }
-    rT = ld4(wsp + 4 * tid);
-    rP = ld4(wsp + kC * kC + 4 * tid);
-    const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-    rg = tid < kC ? ld4(wsp + 2 * kC * kC + 4 * tid) : zf;
+  // wave roles: tile (I, J) of the 64 x 32 chunk outputs; waves 0-7 hold K and T
+  // rows, waves 8-15 Q and P rows
+  const bool lo = wave < 8;
+  const int jw = wave & 7, I = jw >> 1, J = jw & 1;
+  const int arow = 16 * I + li;
+  const uint16_t* a1src = static_cast<const uint16_t*>(lo ? p.k : p.q);
+  u32x4 a1[KB];
+  f32x4 a2[4];
+  uint32_t vv[4];
+  auto load_a1 = [&](int c) {
+    const int r = min(arow, chunk_len(c) - 1);  // rows past the end are zeroed where used
+    const uint16_t* src = a1src + ((int64_t)(seq_lo + c * kC + r) * p.Hk + hk) * D + 8 * kk;
+#pragma unroll
+    for (int b = 0; b < KB; ++b) a1[b] = *reinterpret_cast<const u32x4*>(src + 32 * b);
   };
-  auto commit = [&]() {
-    if (tid < KL) {
-      const int qr = tid / (D / 8), qc = tid - qr * (D / 8);
-      *reinterpret_cast<u32x4*>(s_q + qr * LKW + qc * 4) = rq;
-      const int kr = tid & 63, kc = tid >> 6;
-      *reinterpret_cast<u32x4*>(s_k + kr * LKW + kc * 4) = rk;
-      // K^T: rows kc*8 .. kc*8+7, columns kr.  Lanes 2m and 2m+1 hold rows kr and
-      // kr+1; after one exchange the even lane writes the (kr, kr+1) pairs of
-      // columns 0-3 of the strip and the odd lane those of columns 4-7.
-      const bool odd = kr & 1;
-      const uint32_t give0 = odd ? rk[0] : rk[2], give1 = odd ? rk[1] : rk[3];
-      const uint32_t own0 = odd ? rk[2] : rk[0], own1 = odd ? rk[3] : rk[1];
-      const uint32_t got0 = __shfl_xor(give0, 1, 64), got1 = __shfl_xor(give1, 1, 64);
-      uint32_t* kt = s_kt + (kc * 8 + (odd ? 4 : 0)) * LTW + (kr >> 1);
+  auto load_a2 = [&](int c) {  // T rows (waves 0-7) or P rows (waves 8-15)
+    const float* src = chunk_ws(c) + (lo ? 0 : kC * kC) + arow * kC + 8 * kk;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      a2[2 * b] = ld4(src + 32 * b);
+      a2[2 * b + 1] = ld4(src + 32 * b + 4);
+    }
+  };
+  auto load_v = [&](int c) {  // V at the accumulator positions of the [K S] tile
+    const int L = chunk_len(c);
+    const uint16_t* src = static_cast<const uint16_t*>(p.v) + (int64_t)h * D + col0 + 16 * J + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = min(16 * I + 4 * kk + e, L - 1);
+      vv[e] = src[(int64_t)(seq_lo + c * kC + r) * p.Hv * D];
+    }
+  };
+  // K^T staging (loaded by every wave, committed by waves 8-15): lane bits 0-2 =
+  // 8-column group, 3-4 = row pair, 5 = row parity; waves w and 8 + w cover
+  // rows 8 w .. 8 w + 7
+  const int kw = wave & 7, kcg = lane & 7, krp = (lane >> 3) & 3, kodd = lane >> 5;
+  const int krow = 8 * kw + 2 * krp + kodd;
+  u32x4 ktr[KTL];
+  f32x4 gr;
+  auto load_kt = [&](int c) {
+    const int r = min(krow, chunk_len(c) - 1);
+    const uint16_t* src = static_cast<const uint16_t*>(p.k) + ((int64_t)(seq_lo + c * kC + r) * p.Hk + hk) * D + 8 * kcg;
+#pragma unroll
+    for (int u = 0; u < KTL; ++u) ktr[u] = *reinterpret_cast<const u32x4*>(src + 64 * u);
+    gr = ld4(chunk_ws(c) + 2 * kC * kC + 4 * lane);
+  };
+  auto commit_kt = [&](int c) {
+    const bool dead = krow >= chunk_len(c);
+    uint32_t* kt = s_kt[c & 1];
+#pragma unroll
+    for (int u = 0; u < KTL; ++u) {
+      u32x4 w = ktr[u];
+      if (dead) w = u32x4{0u, 0u, 0u, 0u};
+      // the even row keeps columns 0-3 of its group and takes the odd row's; the odd row columns 4-7
+      const uint32_t give0 = kodd ? w[0] : w[2], give1 = kodd ? w[1] : w[3];
+      const uint32_t own0 = kodd ? w[2] : w[0], own1 = kodd ? w[3] : w[1];
+      const uint32_t got0 = __shfl_xor(give0, 32, 64), got1 = __shfl_xor(give1, 32, 64);
+      const int d0 = 64 * u + 8 * kcg + (kodd ? 4 : 0);
+      const int col = 4 * (kw ^ kcg) + krp;  // swizzled column group (d0 >> 3 & 7 == kcg) + row pair
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t ow = m < 2 ? own0 : own1, gw = m < 2 ? got0 : got1;
         const uint32_t mine = (m & 1) ? (ow >> 16) : (ow & 0xffffu);
         const uint32_t theirs = (m & 1) ? (gw >> 16) : (gw & 0xffffu);
-        kt[m * LTW] = odd ? (theirs | (mine << 16)) : (mine | (theirs << 16));
+        kt[(d0 + m) * LTW + col] = kodd ? (theirs | (mine << 16)) : (mine | (theirs << 16));
       }
     }
-    if (tid < kC * (BV / 8)) {
-      const int vr = tid & 63, vc = tid >> 6;
-      float f[8];
-      unpack8<IDT>(rv, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_Rt[(vc * 8 + e) * LTF + vr] = f[e];
-    }
-    {
-      const int r = tid >> 4, c4 = (tid & 15) * 4;
-      *reinterpret_cast<f32x4*>(s_T + r * LTF + c4) = rT;
-      *reinterpret_cast<f32x4*>(s_P + r * LTF + c4) = rP;
-    }
-    if (tid < kC) *reinterpret_cast<f32x4*>(s_g + 4 * tid) = rg;
+    if (wave == 8) *reinterpret_cast<f32x4*>(s_g[c & 1] + 4 * lane) = gr;
   };
-  const float* s_beta = s_g + kC;
-  const float* s_eg = s_g + 2 * kC;
-  const float* s_dec = s_g + 3 * kC;
 
-  issue(0);
+  // Every wave issues the same vector-memory instructions in the same order
+  // each chunk (loads of a chunk past the last one re-read the last, K^T and
+  // V rows are loaded by all waves, output stores past the end are dropped),
+  // so the compiler's wait counts name exactly the loads each use needs and
+  // the one-chunk-ahead loads stay in flight under the products.
+  load_kt(0);
+  load_a1(0);
+  load_v(0);
+  if (!lo) commit_kt(0);
+  load_kt(min(1, nch - 1));
+  load_a2(0);
+  __syncthreads();
+
+  const int ob = p.out_dt == GDN_F32 ? 4 : 2;
   for (int c = 0; c < nch; ++c) {
     const int t0 = seq_lo + c * kC;
-    const int L = min(kC, seq_hi - t0);
-    commit();
-    __syncthreads();
-    if (c + 1 < nch) issue(c + 1);
-
-    // ---- P1: [K S] (waves 0-7) and [Q S] (waves 8-15), tile rows 16 I.., columns 16 J..
-    const int jw = wave & 7, I = jw >> 1, J = jw & 1;
-    f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+    const int L = chunk_len(c);
+    const int cn = min(c + 1, nch - 1);
+    const float* g = s_g[c & 1];
+    // ---- P1: [K S] (waves 0-7) or [Q S] (waves 8-15) for tile (I, J)
+    f32x4 qs;
     {
-      const uint32_t* A = (wave < 8 ? s_k : s_q) + (16 * I + li) * LKW + 4 * kk;
       const float* Bt = s_St + (16 * J + li) * LSF + 8 * kk;
-      u32x4 aw[D / 32];
-      f32x4 bw[D / 16];
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        aw[b] = *reinterpret_cast<const u32x4*>(A + 16 * b);
-        bw[2 * b] = ld4(Bt + 32 * b);
-        bw[2 * b + 1] = ld4(Bt + 32 * b + 4);
-      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const bool live = arow < L;
 #pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
+      for (int b = 0; b < KB; ++b) {
         float a[8], bb[8];
-        unpack8<IDT>(aw[b], a);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bb[e] = bw[2 * b][e];
-          bb[4 + e] = bw[2 * b + 1][e];
-        }
-        acc = mfma8(acc, a, bb);
-      }
-      if (wave < 8) {  // R^T[j][t] = beta_t (V^T[j][t] - e^{gamma_t} (K S)[t][j]), in place
-        float* rt = s_Rt + (16 * J + li) * LTF + 16 * I + 4 * kk;
-        const f32x4 vt = ld4(rt), be = ld4(s_beta + 16 * I + 4 * kk), eg = ld4(s_eg + 16 * I + 4 * kk);
-        f32x4 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = be[e] * (vt[e] - eg[e] * acc[e]);
-        *reinterpret_cast<f32x4*>(rt) = r;
-      } else {
-        qs = acc;
-      }
-    }
-    __syncthreads();
-    // ---- P2: U = T R on waves 0-7, stored as U^T
-    if (wave < 8) {
-      const float* A = s_T + (16 * I + li) * LTF + 8 * kk;
-      const float* Bt = s_Rt + (16 * J + li) * LTF + 8 * kk;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < kC / 32; ++b) {
-        float a[8], bb[8];
-        const f32x4 a0 = ld4(A + 32 * b), a1 = ld4(A + 32 * b + 4);
+        unpack8<IDT>(a1[b], a);
         const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = a0[e];
-          a[4 + e] = a1[e];
+          a[e] = live ? a[e] : 0.f;
+          a[4 + e] = live ? a[4 + e] : 0.f;
+          bb[e] = b0[e];
+          bb[4 + e] = b1[e];
+        }
+        acc = mfma8(acc, a, bb);
+      }
+      load_a1(cn);
+      if (lo) {  // R^T[j][t] = beta_t (V[t][j] - e^{gamma_t} (K S)[t][j])
+        const int tb = 16 * I + 4 * kk;
+        const f32x4 be = ld4(g + kC + tb), eg = ld4(g + 2 * kC + tb);
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = tb + e < L ? half_to_f32<IDT>(vv[e]) : 0.f;
+          r[e] = be[e] * (v - eg[e] * acc[e]);
+        }
+        *reinterpret_cast<f32x4*>(s_Rt + (16 * J + li) * LTF + tb) = r;
+      }
+      load_v(cn);
+      qs = acc;
+    }
+    __syncthreads();
+    // ---- P2: U = T R on waves 0-7 (stored as U^T); waves 8-15 stage chunk c + 1's K^T
+    if (lo) {
+      const float* Bt = s_Rt + (16 * J + li) * LTF + 8 * kk;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float a[8], bb[8];
+        const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a2[2 * b][e];
+          a[4 + e] = a2[2 * b + 1][e];
           bb[e] = b0[e];
           bb[4 + e] = b1[e];
         }
         acc = mfma8(acc, a, bb);
       }
       *reinterpret_cast<f32x4*>(s_Ut + (16 * J + li) * LTF + 16 * I + 4 * kk) = acc;
+    } else {
+      commit_kt(c + 1);  // past the last chunk this fills the idle buffer with unused rows
     }
+    load_kt(min(c + 2, nch - 1));
     __syncthreads();
     // ---- P3: O = scale (e^gamma [Q S] + P U) on waves 8-15
-    if (wave >= 8) {
-      const float* A = s_P + (16 * I + li) * LTF + 8 * kk;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (!lo) {
       const float* Bt = s_Ut + (16 * J + li) * LTF + 8 * kk;
-      const f32x4 eg = ld4(s_eg + 16 * I + 4 * kk);
-      f32x4 acc;
+      const f32x4 eg = ld4(g + 2 * kC + 16 * I + 4 * kk);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = eg[e] * qs[e];
+      for (int e = 0; e < 4; ++e) o[e] = eg[e] * qs[e];
 #pragma unroll
-      for (int b = 0; b < kC / 32; ++b) {
+      for (int b = 0; b < 2; ++b) {
         float a[8], bb[8];
-        const f32x4 a0 = ld4(A + 32 * b), a1 = ld4(A + 32 * b + 4);
         const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = a0[e];
-          a[4 + e] = a1[e];
+          a[e] = a2[2 * b][e];
+          a[4 + e] = a2[2 * b + 1][e];
           bb[e] = b0[e];
           bb[4 + e] = b1[e];
         }
-        acc = mfma8(acc, a, bb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + 4 * kk + e;
-        if (t < L)
-          store_elem(p.out, ((int64_t)(t0 + t) * p.Hv + h) * D + col0 + 16 * J + li, p.scale * acc[e], p.out_dt);
+        o = mfma8(o, a, bb);
       }
     }
     // ---- P3: S <- e^{gamma_C} S + (diag(dec) K)^T U; tile rows 16 Is.. of S, columns 16 Js..
     {
-      const float egC = s_eg[kC - 1];
+      const uint32_t* kt = s_kt[c & 1];
+      const float egC = g[3 * kC - 1];
       for (int job = wave; job < (D / 16) * 2; job += NT / 64) {
         const int Is = job >> 1, Js = job & 1;
-        const uint32_t* A = s_kt + (16 * Is + li) * LTW + 4 * kk;
+        const int i = 16 * Is + li;
+        const uint32_t* A = kt + i * LTW;
+        const int sw = (i >> 3) & 7;
         const float* Bt = s_Ut + (16 * Js + li) * LTF + 8 * kk;
         f32x4* Sp = reinterpret_cast<f32x4*>(s_St + (16 * Js + li) * LSF + 16 * Is + 4 * kk);
+        u32x4 aw[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) aw[b] = *reinterpret_cast<const u32x4*>(A + 4 * ((4 * b + kk) ^ sw));
         f32x4 acc = *Sp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] *= egC;
-        u32x4 aw[kC / 32];
 #pragma unroll
-        for (int b = 0; b < kC / 32; ++b) aw[b] = *reinterpret_cast<const u32x4*>(A + 16 * b);
-#pragma unroll
-        for (int b = 0; b < kC / 32; ++b) {
+        for (int b = 0; b < 2; ++b) {
           float a[8], bb[8];
           unpack8<IDT>(aw[b], a);
-          const f32x4 d0 = ld4(s_dec + 32 * b + 8 * kk), d1 = ld4(s_dec + 32 * b + 8 * kk + 4);
+          const f32x4 d0 = ld4(g + 3 * kC + 32 * b + 8 * kk), d1 = ld4(g + 3 * kC + 32 * b + 8 * kk + 4);
           const f32x4 b0 = ld4(Bt + 32 * b), b1 = ld4(Bt + 32 * b + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -687,16 +706,396 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state16_kernel(const 
           }
           acc = mfma8(acc, a, bb);
         }
-        // element e of lane (li, kk) is S(16 Is + 4 kk + e, 16 Js + li)
-        *Sp = acc;
+        *Sp = acc;  // element e of lane (li, kk) is S(16 Is + 4 kk + e, 16 Js + li)
       }
     }
+    {  // outputs of this chunk: rows t0 .. t0 + L - 1; waves 0-7 store nowhere
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<char*>(p.out) + (int64_t)t0 * p.Hv * D * ob, (short)0, L * p.Hv * D * ob, 0x00020000);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * kk + e;
+        const int off = lo ? 0x7ffffff0 : ((t * p.Hv + h) * D + col0 + 16 * J + li) * ob;
+        out_store(r, off, p.scale * o[e], p.out_dt);
+      }
+    }
+    load_a2(cn);
     __syncthreads();
   }
   for (int i = tid; i < D * BV; i += NT) {
     const int r = i / BV, j = i - r * BV;
     store_elem(tile, (int64_t)r * D + col0 + j, s_St[j * LSF + r], SDT);
   }
+}
+
+// ---------------------------------------------------------------- kernel 2, bf16 inputs
+// bf16 keys and queries are exact MFMA operands, so the three products that
+// have a key or query on one side run on v_mfma_f32_16x16x32_bf16 with the
+// fp32 side written as the sum of three bf16 terms (x = x1 + x2 + x3, each
+// the bf16 rounding of what the earlier terms leave; together they keep more
+// bits than fp32).  Each such product is three bf16 MFMAs per 32 k, against
+// eight fp32 ones, and its results match fp32 arithmetic to within fp32
+// rounding:  [K S] and [Q S] take S as three bf16 planes of S^T, the state
+// update takes K^T (diag(dec) U) with diag(dec) U as three planes.  The two
+// products with fp32 on both sides (T R and P U) stay on fp32 MFMA.  Layout,
+// staging and wave roles are those of the 16-bit kernel above.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4 a, const u32x4 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc,
+                                                 0, 0, 0);
+}
+
+// x = x1 + x2 + x3 in bf16 (round to nearest even); the differences are exact in fp32
+__device__ __forceinline__ void split3(float x, uint32_t* h) {
+  const __bf16 b1 = (__bf16)x;
+  const float r1 = x - (float)b1;
+  const __bf16 b2 = (__bf16)r1;
+  const float r2 = r1 - (float)b2;
+  const __bf16 b3 = (__bf16)r2;
+  h[0] = __builtin_bit_cast(unsigned short, b1);
+  h[1] = __builtin_bit_cast(unsigned short, b2);
+  h[2] = __builtin_bit_cast(unsigned short, b3);
+}
+
+// four consecutive fp32 values -> three planes of two packed words each
+__device__ __forceinline__ void split3x4(const f32x4 v, u32x2* planes) {
+  uint32_t h[4][3];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split3(v[e], h[e]);
+#pragma unroll
+  for (int x = 0; x < 3; ++x) planes[x] = u32x2{h[0][x] | (h[1][x] << 16), h[2][x] | (h[3][x] << 16)};
+}
+
+template <int SDT, int D>
+__global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(const PrefillArgs p, const float* __restrict__ ws) {
+  constexpr int BV = 32, NB = D / BV, NT = kS16Threads, KB = D / 32;
+  static_assert(D == 64 || D == 128, "bf16 state kernel: D = 64 or 128");
+  constexpr int LTW = kC / 2 + 4;  // words per K^T row (8 swizzled 4-word column groups + pad) and per (dec U)^T plane row
+  constexpr int LTF = kC + 4;      // floats per R^T / U^T row
+  constexpr int LSF = D + 4;       // floats per S^T row
+  constexpr int LSW = D / 2 + 4;   // words per S^T plane row
+  constexpr int KTL = kC * D / 8 / 512;
+  __shared__ __align__(16) uint32_t s_kt[2][D * LTW];
+  __shared__ __align__(16) float s_St[BV * LSF];
+  __shared__ __align__(16) uint32_t s_Sp[3][BV * LSW];
+  __shared__ __align__(16) float s_Rt[BV * LTF];
+  __shared__ __align__(16) float s_Ut[BV * LTF];
+  __shared__ __align__(16) uint32_t s_DUp[3][BV * LTW];
+  __shared__ __align__(16) float s_g[2][4 * kC];  // gamma, beta, e^gamma, e^{gamma_C - gamma}
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kk = lane >> 4;
+  const int bid = blockIdx.x;  // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
+  const int x8 = bid & 7, y = bid >> 3;
+  const int blk = y % NB;
+  const int unit = (y / NB) * 8 + x8;
+  if (unit >= p.N * p.Hv) return;
+  const int n = unit / p.Hv, h = unit - n * p.Hv;
+  const int hk = h / (p.Hv / p.Hk);
+  const int seq_lo = p.cu_seqlens[n], seq_hi = p.cu_seqlens[n + 1];
+  const int len = seq_hi - seq_lo;
+  if (len <= 0) return;
+  const int col0 = blk * BV;
+  const int slot = p.slot_map[n];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) {  // padded sequence: zero outputs
+    for (int i = tid; i < len * BV; i += NT) {
+      const int t = i / BV, j = i - t * BV;
+      store_elem(p.out, ((int64_t)(seq_lo + t) * p.Hv + h) * D + col0 + j, 0.f, p.out_dt);
+    }
+    return;
+  }
+  using ST = typename StateElem<SDT>::T;
+  ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot * p.Hv + h) * (int64_t)(D * D);
+  // S^T (fp32) and its three bf16 planes; lane quad (j, 4 rows)
+  for (int i = tid; i < BV * (D / 4); i += NT) {
+    const int j = i / (D / 4), r4 = (i - j * (D / 4)) * 4;
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = load_elem(tile, (int64_t)(r4 + e) * D + col0 + j, SDT);
+    *reinterpret_cast<f32x4*>(s_St + j * LSF + r4) = v;
+    u32x2 pl[3];
+    split3x4(v, pl);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) *reinterpret_cast<u32x2*>(s_Sp[x] + j * LSW + r4 / 2) = pl[x];
+  }
+  const int nch = (len + kC - 1) / kC;
+  auto chunk_len = [&](int c) { return min(kC, len - c * kC); };
+  auto chunk_ws = [&](int c) { return ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats; };
+
+  // Fixed wave roles, each with its own chunk loop and the same three barriers
+  // per chunk:
+  //   waves 0-3  (K role): [K S] for rows 16 w.., both column tiles; R^T; U = T R
+  //   waves 4-7  (Q role): [Q S] for rows 16 (w - 4).., both column tiles; outputs
+  //   waves 8-15 (S role): K^T and gate staging one chunk ahead; the state update
+  // Every global element a work-group reads is loaded by one lane only, one
+  // chunk ahead, and each role issues the same loads every chunk.
+  // Rows past a chunk's end read the chunk's last row instead: beta is zero
+  // there, so their [K S] rows, R rows and U rows vanish, and their outputs
+  // are dropped.
+  const int I = wave & 3;
+  const int arow = 16 * I + li;
+  // [X S] for rows 16 I.. and both 16-column tiles, S from its three planes
+  auto xs_tiles = [&](const u32x4* a1, f32x4* res) {
+    f32x4 h0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, h1[2] = {h0[0], h0[0]};
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+#pragma unroll
+      for (int J = 0; J < 2; ++J) {
+        const int bo = (16 * J + li) * LSW + 4 * kk + 16 * b;
+        h0[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[0] + bo), h0[J]);
+        h1[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[1] + bo), h1[J]);
+        h1[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[2] + bo), h1[J]);
+      }
+    }
+#pragma unroll
+    for (int J = 0; J < 2; ++J)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[J][e] = h0[J][e] + h1[J][e];
+  };
+  // rows 16 I.. of (fp32 rows in a2) x (fp32 B^T rows at bt, row stride LTF), both column tiles
+  auto f32_tiles = [&](const f32x4* a2, const float* bt, f32x4* acc) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float a[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = a2[2 * b][e];
+        a[4 + e] = a2[2 * b + 1][e];
+      }
+#pragma unroll
+      for (int J = 0; J < 2; ++J) {
+        const float* B = bt + (16 * J + li) * LTF + 8 * kk + 32 * b;
+        const f32x4 b0 = ld4(B), b1 = ld4(B + 4);
+        float bb[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bb[e] = b0[e];
+          bb[4 + e] = b1[e];
+        }
+        acc[J] = mfma8(acc[J], a, bb);
+      }
+    }
+  };
+  auto load_rows = [&](const void* src, int c, u32x4* a1) {  // K or Q rows 16 I + li
+    const int r = min(arow, chunk_len(c) - 1);
+    const uint16_t* q = static_cast<const uint16_t*>(src) + ((int64_t)(seq_lo + c * kC + r) * p.Hk + hk) * D + 8 * kk;
+#pragma unroll
+    for (int b = 0; b < KB; ++b) a1[b] = *reinterpret_cast<const u32x4*>(q + 32 * b);
+  };
+  auto load_mat = [&](int c, int which, f32x4* a2) {  // T (which 0) or P (which 1) rows 16 I + li
+    const float* q = chunk_ws(c) + which * kC * kC + arow * kC + 8 * kk;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      a2[2 * b] = ld4(q + 32 * b);
+      a2[2 * b + 1] = ld4(q + 32 * b + 4);
+    }
+  };
+
+  if (wave < 4) {
+    // ================================================================ K role
+    u32x4 a1[KB];
+    f32x4 a2[4];
+    uint32_t vv[2][4];
+    auto load_v = [&](int c) {  // V at the accumulator positions of both [K S] tiles
+      const int L = chunk_len(c);
+      const uint16_t* q = static_cast<const uint16_t*>(p.v) + (int64_t)h * D + col0 + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = (int64_t)(seq_lo + c * kC + min(16 * I + 4 * kk + e, L - 1)) * p.Hv * D;
+        vv[0][e] = q[row];
+        vv[1][e] = q[row + 16];
+      }
+    };
+    load_rows(p.k, 0, a1);
+    load_v(0);
+    load_mat(0, 0, a2);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int L = chunk_len(c), cn = min(c + 1, nch - 1);
+      const float* g = s_g[c & 1];
+      const int tb = 16 * I + 4 * kk;
+      {  // P1: [K S], then R^T[j][t] = beta_t (V[t][j] - e^{gamma_t} (K S)[t][j])
+        f32x4 ks[2];
+        xs_tiles(a1, ks);
+        const f32x4 be = ld4(g + kC + tb), eg = ld4(g + 2 * kC + tb);
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = tb + e < L ? __uint_as_float(vv[J][e] << 16) : 0.f;
+            r[e] = be[e] * (v - eg[e] * ks[J][e]);
+          }
+          *reinterpret_cast<f32x4*>(s_Rt + (16 * J + li) * LTF + tb) = r;
+        }
+        load_rows(p.k, cn, a1);
+        load_v(cn);
+      }
+      __syncthreads();
+      {  // P2: U = T R; U^T in fp32 and diag(dec) U as three bf16 planes
+        f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32_tiles(a2, s_Rt, u);
+        load_mat(cn, 0, a2);
+        const f32x4 dc = ld4(g + 3 * kC + tb);
+#pragma unroll
+        for (int J = 0; J < 2; ++J) {
+          const int jr = 16 * J + li;
+          *reinterpret_cast<f32x4*>(s_Ut + jr * LTF + tb) = u[J];
+          f32x4 du;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) du[e] = dc[e] * u[J][e];
+          u32x2 pl[3];
+          split3x4(du, pl);
+#pragma unroll
+          for (int x = 0; x < 3; ++x) *reinterpret_cast<u32x2*>(s_DUp[x] + jr * LTW + tb / 2) = pl[x];
+        }
+      }
+      __syncthreads();
+      __syncthreads();
+    }
+  } else if (wave < 8) {
+    // ================================================================ Q role
+    u32x4 a1[KB];
+    f32x4 a2[4];
+    const int ob = p.out_dt == GDN_F32 ? 4 : 2;
+    load_rows(p.q, 0, a1);
+    load_mat(0, 1, a2);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int t0 = seq_lo + c * kC;
+      const int L = chunk_len(c), cn = min(c + 1, nch - 1);
+      const float* g = s_g[c & 1];
+      f32x4 qs[2];
+      xs_tiles(a1, qs);  // P1
+      load_rows(p.q, cn, a1);
+      __syncthreads();
+      __syncthreads();
+      {  // P3: O = scale (e^gamma [Q S] + P U)
+        const f32x4 eg = ld4(g + 2 * kC + 16 * I + 4 * kk);
+        f32x4 o[2];
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[J][e] = eg[e] * qs[J][e];
+        f32_tiles(a2, s_Ut, o);
+        load_mat(cn, 1, a2);
+        // rows t0 .. t0 + L - 1 of the output; stores past the end are dropped
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char*>(p.out) + (int64_t)t0 * p.Hv * D * ob, (short)0, L * p.Hv * D * ob, 0x00020000);
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * I + 4 * kk + e;
+            out_store(r, ((t * p.Hv + h) * D + col0 + 16 * J + li) * ob, p.scale * o[J][e], p.out_dt);
+          }
+      }
+      __syncthreads();
+    }
+  } else {
+    // ================================================================ S role
+    // K^T staging: lane bits 0-2 = 8-column group, 3-4 = row pair, 5 = row
+    // parity; wave 8 + w covers rows 8 w .. 8 w + 7
+    const int kw = wave - 8, kcg = lane & 7, krp = (lane >> 3) & 3, kodd = lane >> 5;
+    const int krow = 8 * kw + 2 * krp + kodd;
+    u32x4 ktr[KTL];
+    f32x4 gr;
+    auto load_kt = [&](int c) {
+      const int r = min(krow, chunk_len(c) - 1);
+      const uint16_t* q = static_cast<const uint16_t*>(p.k) + ((int64_t)(seq_lo + c * kC + r) * p.Hk + hk) * D + 8 * kcg;
+#pragma unroll
+      for (int u = 0; u < KTL; ++u) ktr[u] = *reinterpret_cast<const u32x4*>(q + 64 * u);
+      gr = ld4(chunk_ws(c) + 2 * kC * kC + 4 * lane);
+    };
+    auto commit_kt = [&](int c) {  // chunk c's K^T and gates into buffer c & 1
+      const bool dead = krow >= chunk_len(c);
+      uint32_t* kt = s_kt[c & 1];
+#pragma unroll
+      for (int u = 0; u < KTL; ++u) {
+        u32x4 w = ktr[u];
+        if (dead) w = u32x4{0u, 0u, 0u, 0u};
+        // the even row keeps columns 0-3 of its group and takes the odd row's; the odd row columns 4-7
+        const uint32_t give0 = kodd ? w[0] : w[2], give1 = kodd ? w[1] : w[3];
+        const uint32_t own0 = kodd ? w[2] : w[0], own1 = kodd ? w[3] : w[1];
+        const uint32_t got0 = __shfl_xor(give0, 32, 64), got1 = __shfl_xor(give1, 32, 64);
+        const int d0 = 64 * u + 8 * kcg + (kodd ? 4 : 0);
+        const int col = 4 * (kw ^ kcg) + krp;  // swizzled column group (d0 >> 3 & 7 == kcg) + row pair
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t ow = m < 2 ? own0 : own1, gw = m < 2 ? got0 : got1;
+          const uint32_t mine = (m & 1) ? (ow >> 16) : (ow & 0xffffu);
+          const uint32_t theirs = (m & 1) ? (gw >> 16) : (gw & 0xffffu);
+          kt[(d0 + m) * LTW + col] = kodd ? (theirs | (mine << 16)) : (mine | (theirs << 16));
+        }
+      }
+      if (wave == 8) *reinterpret_cast<f32x4*>(s_g[c & 1] + 4 * lane) = gr;
+    };
+    load_kt(0);
+    commit_kt(0);
+    load_kt(min(1, nch - 1));
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      commit_kt(c + 1);  // past the last chunk this fills the idle buffer with unused rows
+      load_kt(min(c + 2, nch - 1));
+      __syncthreads();
+      __syncthreads();
+      {  // P3: S <- e^{gamma_C} S + K^T (diag(dec) U); tiles of rows 16 Is.., columns 16 Js..
+        const uint32_t* kt = s_kt[c & 1];
+        const float egC = s_g[c & 1][3 * kC - 1];
+#pragma unroll
+        for (int jj = 0; jj < (D / 16) * 2 / 8; ++jj) {
+          const int job = kw + 8 * jj;
+          const int Is = job >> 1, Js = job & 1;
+          const int i = 16 * Is + li, jr = 16 * Js + li;
+          const uint32_t* A = kt + i * LTW;
+          const int sw = (i >> 3) & 7;
+          f32x4* Sp = reinterpret_cast<f32x4*>(s_St + jr * LSF + 16 * Is + 4 * kk);
+          f32x4 acc0 = *Sp, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc0[e] *= egC;
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const u32x4 aw = *reinterpret_cast<const u32x4*>(A + 4 * ((4 * b + kk) ^ sw));
+            const int bo = jr * LTW + 16 * b + 4 * kk;
+            acc0 = mfma_bf16(aw, *reinterpret_cast<const u32x4*>(s_DUp[0] + bo), acc0);
+            acc1 = mfma_bf16(aw, *reinterpret_cast<const u32x4*>(s_DUp[1] + bo), acc1);
+            acc1 = mfma_bf16(aw, *reinterpret_cast<const u32x4*>(s_DUp[2] + bo), acc1);
+          }
+          f32x4 acc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = acc0[e] + acc1[e];
+          *Sp = acc;  // element e of lane (li, kk) is S(16 Is + 4 kk + e, 16 Js + li)
+          u32x2 pl[3];
+          split3x4(acc, pl);
+#pragma unroll
+          for (int x = 0; x < 3; ++x) *reinterpret_cast<u32x2*>(s_Sp[x] + jr * LSW + 8 * Is + 2 * kk) = pl[x];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < D * BV; i += NT) {
+    const int r = i / BV, j = i - r * BV;
+    store_elem(tile, (int64_t)r * D + col0 + j, s_St[j * LSF + r], SDT);
+  }
+}
+
+template <int D>
+static hipError_t launch_state_bf16(const PrefillArgs& a, int state_dt, unsigned grid, float* ws, hipStream_t s) {
+  switch (state_dt) {
+    case GDN_F32:
+      hipLaunchKernelGGL((gdn_prefill_state_bf16_kernel<GDN_F32, D>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    case GDN_BF16:
+      hipLaunchKernelGGL((gdn_prefill_state_bf16_kernel<GDN_BF16, D>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    case GDN_F16:
+      hipLaunchKernelGGL((gdn_prefill_state_bf16_kernel<GDN_F16, D>), dim3(grid), dim3(kS16Threads), 0, s, a, ws);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int D, int IDT>
@@ -725,7 +1124,7 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws
   const int64_t units = (int64_t)a.N * a.Hv;
   if constexpr (EB == 2 && (D == 64 || D == 128)) {  // 16-bit inputs, wide heads: the k-contiguous kernel
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / 32));
-    return a.in_dt == GDN_BF16 ? launch_state16<D, GDN_BF16>(a, state_dt, grid, ws, s)
+    return a.in_dt == GDN_BF16 ? launch_state_bf16<D>(a, state_dt, grid, ws, s)
                                : launch_state16<D, GDN_F16>(a, state_dt, grid, ws, s);
   } else {
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
