@@ -835,17 +835,30 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
   // are dropped.
   const int I = wave & 3;
   const int arow = 16 * I + li;
-  // [X S] for rows 16 I.. and both 16-column tiles, S from its three planes
+  // [X S] for rows 16 I.. and both 16-column tiles, S from its three planes.
+  // The six plane reads of block b + 1 are issued before the MFMAs of block b
+  // (the scheduling barrier keeps the compiler from sinking them), so LDS
+  // latency hides behind the MFMAs of the same wave.
   auto xs_tiles = [&](const u32x4* a1, f32x4* res) {
     f32x4 h0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, h1[2] = {h0[0], h0[0]};
+    u32x4 sb[2][2][3];
+    auto fetch = [&](int b, u32x4 (*dst)[3]) {
+#pragma unroll
+      for (int J = 0; J < 2; ++J)
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+          dst[J][x] = *reinterpret_cast<const u32x4*>(s_Sp[x] + (16 * J + li) * LSW + 4 * kk + 16 * b);
+    };
+    fetch(0, sb[0]);
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
+      if (b + 1 < KB) fetch(b + 1, sb[(b + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int J = 0; J < 2; ++J) {
-        const int bo = (16 * J + li) * LSW + 4 * kk + 16 * b;
-        h0[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[0] + bo), h0[J]);
-        h1[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[1] + bo), h1[J]);
-        h1[J] = mfma_bf16(a1[b], *reinterpret_cast<const u32x4*>(s_Sp[2] + bo), h1[J]);
+        h0[J] = mfma_bf16(a1[b], sb[b & 1][J][0], h0[J]);
+        h1[J] = mfma_bf16(a1[b], sb[b & 1][J][1], h1[J]);
+        h1[J] = mfma_bf16(a1[b], sb[b & 1][J][2], h1[J]);
       }
     }
 #pragma unroll
@@ -853,8 +866,19 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
 #pragma unroll
       for (int e = 0; e < 4; ++e) res[J][e] = h0[J][e] + h1[J][e];
   };
-  // rows 16 I.. of (fp32 rows in a2) x (fp32 B^T rows at bt, row stride LTF), both column tiles
+  // rows 16 I.. of (fp32 rows in a2) x (fp32 B^T rows at bt, row stride LTF), both
+  // column tiles; both blocks' B reads are issued before the MFMAs
   auto f32_tiles = [&](const f32x4* a2, const float* bt, f32x4* acc) {
+    f32x4 bv[2][2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int J = 0; J < 2; ++J) {
+        const float* B = bt + (16 * J + li) * LTF + 8 * kk + 32 * b;
+        bv[b][J][0] = ld4(B);
+        bv[b][J][1] = ld4(B + 4);
+      }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float a[8];
@@ -865,13 +889,11 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
       }
 #pragma unroll
       for (int J = 0; J < 2; ++J) {
-        const float* B = bt + (16 * J + li) * LTF + 8 * kk + 32 * b;
-        const f32x4 b0 = ld4(B), b1 = ld4(B + 4);
         float bb[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bb[e] = b0[e];
-          bb[4 + e] = b1[e];
+          bb[e] = bv[b][J][0][e];
+          bb[4 + e] = bv[b][J][1][e];
         }
         acc[J] = mfma8(acc[J], a, bb);
       }
