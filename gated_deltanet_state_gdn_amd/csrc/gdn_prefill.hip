@@ -66,13 +66,50 @@ __device__ __forceinline__ f32x4_t mma16(f32x4_t acc, const FA& A, const FB& B, 
 __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4) + r; }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
 
+// One 16 x 16 tile of X Y^T over D columns, X and Y packed rows in LDS (row
+// stride ldw words, a multiple of 4, rows past the data zeroed).  Lane l
+// supplies row l % 16 of both at the same k; 16-bit rows use the gfx950
+// 16x16x32 bf16 / f16 MFMA with one 16-byte LDS read per operand and k block,
+// fp32 rows the 16x16x4 f32 one.  Element r of the result is (4 (l / 16) + r, l % 16).
+template <int D, int EB>
+__device__ __forceinline__ f32x4_t rows_xyt(const uint32_t* X, const uint32_t* Y, int ldw, int dt, int lane) {
+  const int i = lane & 15, kb = lane >> 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (EB == 2) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int s = 0; s < (D + 31) / 32; ++s) {
+      const int w0 = 16 * s + 4 * kb;  // word of element 32 s + 8 kb
+      const bool kv = D >= 32 || w0 < D / 2;
+      const int wr = kv ? w0 : 0;
+      u32x4 a = *reinterpret_cast<const u32x4*>(X + i * ldw + wr);
+      u32x4 b = *reinterpret_cast<const u32x4*>(Y + i * ldw + wr);
+      if (!kv) a = b = u32x4{0u, 0u, 0u, 0u};
+      if (dt == GDN_BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                     0, 0, 0);
+    }
+  } else {
+#pragma unroll 8
+    for (int s = 0; s < D / 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(X[i * ldw + 4 * s + kb]),
+                                                 __uint_as_float(Y[i * ldw + 4 * s + kb]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------- kernel 1
 template <int D, int EB>
 __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
   constexpr int LDT = kC + 4;
-  constexpr int LDW = D * EB / 4 + 1;  // words per packed key / query row (+1: bank spread)
+  constexpr int LDW = D * EB / 4 + 4;  // words per packed key / query row: 16-byte rows, 4 mod 8 banks
   constexpr int VE = 16 / EB, CPR = D / VE;
-  __shared__ uint32_t s_k[kC * LDW], s_q[kC * LDW];
+  __shared__ __align__(16) uint32_t s_k[kC * LDW];
+  __shared__ __align__(16) uint32_t s_q[kC * LDW];
   __shared__ float s_A[kC][LDT], s_T[kC][LDT];
   __shared__ float s_M[4][16][20];
   __shared__ float s_g[kC], s_beta[kC], s_gam[kC];
@@ -96,8 +133,8 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   const int len = min(kC, seq_hi - t0);
   const int hk = h / (p.Hv / p.Hk);
 
-  // keys and queries stay packed in their input dtype; rows >= len are never
-  // read (the tile products treat them as zero)
+  // keys and queries stay packed in their input dtype, rows >= len zeroed; the
+  // gate inputs are loaded alongside, so the work-group waits on memory once
   {
     constexpr int IT = (kC * CPR + 255) / 256;
     u32x4 xk[IT], xq[IT];
@@ -113,27 +150,27 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       xk[u] = zk;
       xq[u] = zq;
     }
+    float ga = 0.f, gb = 0.f, al = 0.f, db = 0.f;
+    if (tid < kC) {
+      const int64_t gi = (int64_t)(t0 + min(tid, len - 1)) * p.Hv + h;
+      ga = load_elem(p.a, gi, p.in_dt);
+      gb = load_elem(p.b, gi, p.in_dt);
+      al = p.A_log[h];
+      db = p.dt_bias[h];
+    }
 #pragma unroll
     for (int u = 0; u < IT; ++u) {
       const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
-      if (x < kC * CPR && r < len) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          s_k[r * LDW + cc * 4 + w] = xk[u][w];
-          s_q[r * LDW + cc * 4 + w] = xq[u][w];
-        }
+      if (x < kC * CPR) {
+        *reinterpret_cast<u32x4*>(s_k + r * LDW + cc * 4) = xk[u];
+        *reinterpret_cast<u32x4*>(s_q + r * LDW + cc * 4) = xq[u];
       }
     }
-  }
-  if (tid < kC) {
-    float g = 0.f, be = 0.f;
-    if (tid < len) {
-      const int64_t gi = (int64_t)(t0 + tid) * p.Hv + h;
-      g = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
-      be = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+    if (tid < kC) {
+      const bool live = tid < len;
+      s_g[tid] = live ? gate_g(ga, al, db) : 0.f;
+      s_beta[tid] = live ? sigmoid_f(gb) : 0.f;
     }
-    s_g[tid] = g;
-    s_beta[tid] = be;
   }
   __syncthreads();
   if (wave == 0) {  // inclusive prefix sum of g over the chunk
@@ -155,8 +192,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
     const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (J <= I)  // X Y^T on MFMA (16-bit rows: the exact bf16 / f16 products, fp32 accumulation)
-      acc = tile_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, len - 16 * I, s_k + 16 * J * LDW, len - 16 * J, LDW,
-                            p.in_dt, lane);
+      acc = rows_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, s_k + 16 * J * LDW, LDW, p.in_dt, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * I + acc_row(lane, r), s = 16 * J + acc_col(lane);
