@@ -108,10 +108,16 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   constexpr int LDT = kC + 4;
   constexpr int LDW = D * EB / 4 + 4;  // words per packed key / query row: 16-byte rows, 4 mod 8 banks
   constexpr int VE = 16 / EB, CPR = D / VE;
-  __shared__ __align__(16) uint32_t s_k[kC * LDW];
-  __shared__ __align__(16) uint32_t s_q[kC * LDW];
-  __shared__ float s_A[kC][LDT], s_T[kC][LDT];
-  __shared__ float s_M[4][16][20];
+  // two buffers: K rows then T, Q rows then A (about 40 KB in all at D = 128,
+  // so four work-groups share a CU and cover each other's memory waits)
+  constexpr int UW = kC * LDW > kC * LDT ? kC * LDW : kC * LDT;
+  __shared__ __align__(16) uint32_t s_u0[UW];
+  __shared__ __align__(16) uint32_t s_u1[UW];
+  __shared__ float s_M[4][16][17];
+  uint32_t* const s_k = s_u0;
+  uint32_t* const s_q = s_u1;
+  float (*const s_T)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u0);
+  float (*const s_A)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u1);
   __shared__ float s_g[kC], s_beta[kC], s_gam[kC];
 
   const int cs = blockIdx.x, h = blockIdx.y;
@@ -187,8 +193,12 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   float* wsp = ws + ((int64_t)cs * p.Hv + h) * kWsFloats;
   float* ws_T = wsp;
   float* ws_P = wsp + kC * kC;
-  // A (strictly lower, to LDS) and P (causal, to the workspace): 2 x 16 tiles
-  for (int job = wave; job < 32; job += 4) {
+  // A (strictly lower) and P (causal, to the workspace): 16 tiles each, wave w
+  // takes tile rows I = w.. of both; A stays in registers until Q is no longer read
+  f32x4_t a_t[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int job = wave + 4 * k;
     const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (J <= I)  // X Y^T on MFMA (16-bit rows: the exact bf16 / f16 products, fp32 accumulation)
@@ -199,9 +209,16 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       if (isP) {
         ws_P[t * kC + s] = (s <= t) ? expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
       } else {
-        s_A[t][s] = (s < t) ? s_beta[t] * expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
+        a_t[k][r] = (s < t) ? s_beta[t] * expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
       }
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // A into the Q buffer
+    const int job = wave + 4 * k, I = (job >> 2) & 3, J = job & 3;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_A[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = a_t[k][r];
   }
   __syncthreads();
 
