@@ -317,7 +317,8 @@ def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
         "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes, "flops_per_call": flops,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf / FP32_MFMA_PEAK_TFS, 4), "traffic": None,
-                     "scope": "whole call (chunk kernel + state kernel), fp32 MFMA peak"},
+                     "scope": "whole call (chunk kernel + state kernel); fp32-accurate products, those with a key or "
+                              "query operand run as three-term bf16 splits; against the fp32 MFMA peak"},
         "workspace_MiB": round(ws.numel() / 2 ** 20, 1),
     }
     del pool, ws, out, args
