@@ -236,12 +236,12 @@ __host__ __device__ inline size_t replay_prep_lds_bytes(int D, int L, int T) {
   return replay_prep_words(D, 4, L, T) * sizeof(float);  // the f32-input size bounds both
 }
 
-// One workgroup of NWP waves per unit.  Loads are issued in two independent
-// rounds: the window rows (which need only the row index) together with the
-// slot, then the unit's whole ring block in ring order, its gates and its
-// pointers (which need only the slot); the live entries are picked out of the
-// block into LDS.  Keys and values stay packed (input dtype) in LDS and are
-// widened on use.  Phases (one barrier each): staging and gates; the Gram
+// One workgroup of NWP waves per unit.  Loads are issued in two rounds: the
+// window rows (which need only the row index) together with the slot, then
+// the unit's ring pointers and, after them, only its live ring entries and
+// their gates (many workgroups share a CU, so the extra dependent load is
+// hidden, and the ring bytes read drop to the live entries).  Keys and
+// values stay packed (input dtype) in LDS and are widened on use.  Phases (one barrier each): staging and gates; the Gram
 // and key / query MFMA tiles, shared over the waves; the back substitution,
 // one wave per window position; w and acc, one thread per element.
 template <int D, int EB, int NWP>
@@ -319,41 +319,38 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
 
-  // ---- round 2: the unit's whole ring block (ring order), its gates and pointers
+  // ---- round 2: the unit's ring pointers, then its live entries (committed,
+  // in ring order from the start pointer) and their gates
   const int64_t ring_e = unit * L;
-  const char* rk = static_cast<const char*>(R.k) + ring_e * D * EB;
-  const char* rv = static_cast<const char*>(R.v) + ring_e * D * EB;
-  auto ring_k = [&](int j) { return rk + (int64_t)j * D * EB; };
-  auto ring_v = [&](int j) { return rv + (int64_t)j * D * EB; };
-  u32x4 xk[NR], xv[NR];
-  load_batch(0, L, ring_k, xk);
-  load_batch(0, L, ring_v, xv);
-  float rg = 0.f, rb = 0.f;
-  if (tid < L) {
-    rg = R.g[ring_e + tid];
-    rb = R.beta[ring_e + tid];
-  }
   const RingPos rp = ring_pos(R, unit);
   const int st = rp.st;
   const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
   const int n_all = cnt + T;           // <= L
+  const char* rk = static_cast<const char*>(R.k) + ring_e * D * EB;
+  const char* rv = static_cast<const char*>(R.v) + ring_e * D * EB;
+  auto live_src_k = [&](int i) { return rk + (int64_t)((st + i) % L) * D * EB; };
+  auto live_src_v = [&](int i) { return rv + (int64_t)((st + i) % L) * D * EB; };
+  u32x4 xk[NR], xv[NR];
+  load_batch(0, cnt, live_src_k, xk);
+  load_batch(0, cnt, live_src_v, xv);
+  float rg = 0.f, rb = 0.f;
+  if (tid < cnt) {
+    const int64_t j = ring_e + (st + tid) % L;
+    rg = R.g[j];
+    rb = R.beta[j];
+  }
 
   // ---- commit in live order: committed entries 0..cnt-1, then the window
-  auto live_row = [&](uint32_t* base, int j) -> uint32_t* {  // ring index j -> its live row, if live
-    const int d = j - st;
-    const int live = d < 0 ? d + L : d;
-    return live < cnt ? base + live * LDW : nullptr;
-  };
-  auto live_k = [&](int j) { return live_row(e_k, j); };
-  auto live_v = [&](int j) { return live_row(e_v, j); };
+  auto live_k = [&](int i) -> uint32_t* { return e_k + i * LDW; };
+  auto live_v = [&](int i) -> uint32_t* { return e_v + i * LDW; };
   auto wdst_k = [&](int t) -> uint32_t* { return e_k + (cnt + t) * LDW; };
   auto wdst_v = [&](int t) -> uint32_t* { return e_v + (cnt + t) * LDW; };
   auto wdst_q = [&](int t) -> uint32_t* { return e_q + t * LDW; };
   commit_batch(0, T, wdst_k, wk);
   commit_batch(0, T, wdst_v, wv);
   commit_batch(0, T, wdst_q, wq);
-  commit_batch(0, L, live_k, xk);
-  commit_batch(0, L, live_v, xv);
+  commit_batch(0, cnt, live_k, xk);
+  commit_batch(0, cnt, live_v, xv);
   for (int r0 = NR; r0 * RB < T; r0 += NR) {  // longer windows
     load_batch(r0, T, win_k, wk);
     load_batch(r0, T, win_v, wv);
@@ -362,11 +359,11 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
     commit_batch(r0, T, wdst_v, wv);
     commit_batch(r0, T, wdst_q, wq);
   }
-  for (int r0 = NR; r0 * RB < L; r0 += NR) {  // longer rings
-    load_batch(r0, L, ring_k, xk);
-    load_batch(r0, L, ring_v, xv);
-    commit_batch(r0, L, live_k, xk);
-    commit_batch(r0, L, live_v, xv);
+  for (int r0 = NR; r0 * RB < cnt; r0 += NR) {  // longer rings
+    load_batch(r0, cnt, live_src_k, xk);
+    load_batch(r0, cnt, live_src_v, xv);
+    commit_batch(r0, cnt, live_k, xk);
+    commit_batch(r0, cnt, live_v, xv);
   }
   // gates and their prefix sums in live order (wave 0): lane j takes live
   // entry j, a committed entry from ring position (st + j) % L or window
@@ -377,8 +374,7 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
     wbeta = sigmoid_f(gb);
   }
   if (wave == 0) {
-    const int from_ring = (st + lane) % L;
-    const float g_r = __shfl(rg, from_ring, 64), b_r = __shfl(rb, from_ring, 64);
+    const float g_r = rg, b_r = rb;  // lane j < cnt loaded live entry j
     const int from_win = (lane - cnt) & 63;
     const float g_w = __shfl(wg, from_win, 64), b_w = __shfl(wbeta, from_win, 64);
     const float g = lane < cnt ? g_r : (lane < n_all ? g_w : 0.f);
