@@ -77,18 +77,20 @@ __device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t unit) {
 
 // ---------------------------------------------------------------- fold
 // Persistent: workgroup w owns units w, w + G, w + 2G, ... (G the grid size,
-// sized to the resident workgroups), checks 64 of them at a time, one per lane
-// of wave 0, and folds those that need it one after another with the whole
-// workgroup, so a step without folds costs one small check per unit.  A unit folds when count + T > L; the
-// flush (T == 0) folds every non-empty ring.  CDT >= 0 selects the
-// dual-precision checkpoint: the fp32 result is also written, rounded once,
-// to the CDT read copy (the flush then refreshes the copy of every unit).
+// sized to the resident workgroups), checks 64 of them at a time, one per
+// lane of wave 0, and folds those that need it one after another with the
+// whole workgroup, so a step without folds costs one small check per unit.
+// A unit folds when count + T > L; the flush (T == 0) folds every non-empty
+// ring.  CDT >= 0 selects the dual-precision checkpoint: the fp32 result is
+// also written, rounded once, to the CDT read copy (the flush then refreshes
+// the copy of every unit).  Two variants: by columns for D >= 32 (below the
+// prep section), by rows for D = 16 (here).
 template <int SDT, int D>
 using FoldGeom = TileGeom<SDT, D, 4>;  // fp32 working tile: four waves for every state dtype
 
 template <int SDT, int D, bool NT, int EB, int CDT>
 __global__ void __launch_bounds__((FoldGeom<SDT, D>::NW * 64))
-gdn_replay_fold_kernel(const ReplayArgs P) {
+gdn_replay_fold_rows_kernel(const ReplayArgs P) {
   using G = FoldGeom<SDT, D>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
   constexpr int NTH = NW * 64;
@@ -211,6 +213,155 @@ gdn_replay_fold_kernel(const ReplayArgs P) {
         uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
 #pragma unroll
         for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * NW * RPW * D, s[pp]);
+      }
+      if (tid == 0) {
+        R.start[unit] = (st + cnt) % L;
+        R.count[unit] = 0;
+      }
+      __syncthreads();  // LDS staging is reused by the next unit
+    }
+    __syncthreads();  // s_list is rewritten by the next check
+  }
+}
+
+// The fold for D >= 32, with the tile split by columns: wave w holds columns
+// w D / 4 .. (w + 1) D / 4 - 1 of every row, four per lane, so the key
+// products S^T k of its columns reduce within the wave.  The columns of S
+// are independent under the recurrence, so each wave runs all cnt steps on
+// its own with no barrier between them: two barriers per unit (staging,
+// reuse) instead of one per entry.  Keys are staged permuted so that a lane
+// reads the key rows it multiplies as one contiguous run.
+constexpr int kFoldColThreads = 256;
+
+template <int SDT, int D, bool NT, int EB, int CDT>
+__global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const ReplayArgs P) {
+  constexpr int NW = kFoldColThreads / 64, VEC = 4;
+  constexpr int CW = D / NW;      // columns per wave
+  constexpr int CG = CW / VEC;    // column groups per wave
+  constexpr int RS = 64 / CG;     // row lanes per column group
+  constexpr int PASSES = D / RS;  // rows per lane: pp * RS + rs
+  static_assert(D >= 32 && CG * RS == 64 && PASSES * RS == D, "fold geometry");
+  constexpr int NTH = kFoldColThreads;
+  using IO = TileIO<SDT, VEC, NT>;
+  using ST = typename StateElem<SDT>::T;
+
+  extern __shared__ float s_dyn[];
+  __shared__ int s_list[64];
+  __shared__ int s_n;
+
+  const DecodeArgs& p = P.d;
+  const RingArgs& R = P.ring;
+  const int T = P.T, L = R.L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int units = p.B * p.Hv;
+  const int cg = lane % CG, rs = lane / CG;
+  const int c0 = wave * CW + cg * VEC;
+  float* e_kp = s_dyn;           // [L][RS][PASSES]: element (j, row pp * RS + r) at j D + r PASSES + pp
+  float* e_v = e_kp + L * D;     // [L][D]
+  float* e_a = e_v + L * D;      // [L] exp(g)
+  float* e_b = e_a + L;          // [L] beta
+  constexpr int VE = 16 / EB, CPR = D / VE;  // ring row elements per 16-byte load, loads per row
+
+  const int grid_n = gridDim.x;
+  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
+    if (wave == 0) {
+      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
+      const int x = xl < units ? (int)xl : units;
+      bool need = false;
+      if (x < units) {
+        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+        const int slot = p.slot_map[b];
+        if (slot >= 0 && (int64_t)slot < p.num_slots) {
+          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+        }
+      }
+      const uint64_t mask = __ballot(need);
+      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
+      if (lane == 0) s_n = __popcll(mask);
+    }
+    __syncthreads();
+    const int n_fold = s_n;
+    for (int f = 0; f < n_fold; ++f) {
+      const int x = s_list[f];
+      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+      const RingPos rp = ring_pos(R, unit);
+      const int st = rp.st, cnt = rp.cnt;
+
+      // the lane offset is made opaque per unit so that the per-pass addresses
+      // are not hoisted out of the unit loop (they would hold registers)
+      int lane_off = rs * D + c0;
+      asm volatile("" : "+v"(lane_off));
+      ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
+      typename IO::Raw raw[PASSES];
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + pp * RS * D);
+
+      const int64_t ring_e = unit * L;
+      for (int t = tid; t < cnt; t += NTH) {
+        const int j = (st + t) % L;
+        e_a[t] = expf(R.g[ring_e + j]);
+        e_b[t] = R.beta[ring_e + j];
+      }
+      for (int q = tid; q < cnt * CPR; q += NTH) {  // keys (permuted) and values, widened
+        const int t = q / CPR, cc = (q - t * CPR) * VE;
+        const int64_t row = (ring_e + (st + t) % L) * D + cc;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + row * EB);
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          float kf, vf;
+          if constexpr (EB == 4) {
+            kf = __uint_as_float(kw[e]);
+            vf = __uint_as_float(vw[e]);
+          } else {
+            const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
+            const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
+            kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
+            vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+          }
+          const int r = cc + e;
+          e_kp[t * D + (r % RS) * PASSES + r / RS] = kf;
+          e_v[t * D + r] = vf;
+        }
+      }
+      float s[PASSES][VEC];
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
+      __syncthreads();
+
+      // the cnt steps S <- e^{g} S;  d = beta (v - S^T k);  S <- S + k d^T, per column
+      for (int j = 0; j < cnt; ++j) {
+        const float al = e_a[j], be = e_b[j];
+        float kr[PASSES];
+        const float* kp = e_kp + j * D + rs * PASSES;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) kr[pp] = kp[pp];
+        float xs[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xs[e] = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xs[e] = fmaf(s[pp][e], kr[pp], xs[e]);
+        float dl[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dl[e] = be * (e_v[j * D + c0 + e] - al * xor_sum_from<CG>(xs[e]));
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr[pp] * dl[e]);
+      }
+      if (cnt > 0) {
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * RS * D, s[pp]);
+      }
+      if constexpr (CDT >= 0) {
+        using CIO = TileIO<CDT, VEC, false>;
+        uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * RS * D, s[pp]);
       }
       if (tid == 0) {
         R.start[unit] = (st + cnt) % L;
@@ -593,15 +744,23 @@ static hipError_t launch_fold(const ReplayArgs& a, hipStream_t s) {
   using G = FoldGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
   const size_t lds = replay_fold_lds_bytes(D, a.ring.L);
-  const auto kern = &gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>;
+  void (*kern)(const ReplayArgs);
+  int threads;
+  if constexpr (D >= 32) {
+    kern = &gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>;
+    threads = kFoldColThreads;
+  } else {
+    kern = &gdn_replay_fold_rows_kernel<SDT, D, NT, EB, CDT>;
+    threads = G::NW * 64;
+  }
   int per_cu = 0, cus = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), G::NW * 64, lds, &per_cu);
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), threads, lds, &per_cu);
   if (e == hipSuccess) e = device_cus(&cus);
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.d.B * a.d.Hv;
   const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
   const unsigned grid = (unsigned)(units < fill ? units : fill);
-  hipLaunchKernelGGL((gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>), dim3(grid), dim3(G::NW * 64), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
