@@ -222,12 +222,38 @@ struct RowStager {
 };
 
 // ------------------------------------------------------------------ wave64 reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the lanes that differ only in bits >= log2(OFF_FROM), returned to
+// every lane, all on the VALU: bits 0-1 by DPP quad permutes, bits 2-3 by DPP
+// rotates within 16-lane rows (by 8, then by 4 over the pair sums), bits 4 and
+// 5 by the gfx950 16- and 32-lane swaps (v_permlane16/32_swap with both
+// operands x: the two results hold the two halves, so their sum is the
+// all-reduce).  No LDS-crossbar permutes.
 template <int OFF_FROM>
 __device__ __forceinline__ float xor_sum_from(float x) {
-  // Sum over the lanes that differ only in bits >= log2(OFF_FROM).
-#pragma unroll
-  for (int off = OFF_FROM; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  static_assert(OFF_FROM >= 1 && OFF_FROM <= 32 && (OFF_FROM & (OFF_FROM - 1)) == 0, "power of two lane offset");
+  if constexpr (OFF_FROM <= 1) x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  if constexpr (OFF_FROM <= 2) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if constexpr (OFF_FROM <= 8) x += dpp_mov<0x128>(x);  // row_ror:8: lane ^ 8 within a row
+  if constexpr (OFF_FROM <= 4) x += dpp_mov<0x124>(x);  // row_ror:4 over the pair sums: bits 2-3 complete
+  // Both swap results pass through an empty asm: when they are added directly
+  // this compiler takes the first result for both operands of the add.
+  if constexpr (OFF_FROM <= 16) {
+    const unsigned a = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    unsigned r0 = r[0], r1 = r[1];
+    asm volatile("" : "+v"(r0), "+v"(r1));
+    x = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+  }
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  unsigned r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
 }
 
 __device__ __forceinline__ float wave_sum(float x) { return xor_sum_from<1>(x); }
