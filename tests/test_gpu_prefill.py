@@ -152,6 +152,15 @@ def test_prefill_padded_sequence():
     del torch, states, inp
 
 
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+def test_prefill_wide_heads_16bit_states_with_padding(sdt):
+    """Head dim 128, bf16 inputs, 16-bit states (rounded once per call), ragged lengths and a
+    padded sequence: zero outputs for it, and the others against the oracle."""
+    slot_map = np.int32([3, -1, 0, 5])
+    pool, states, o, inp = run_prefill(76, [130, 40, 64, 1], 2, 4, 128, sdt, num_slots=6, slot_map=slot_map)
+    assert np.all(o[130:170] == 0)
+
+
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 def test_prefill_workload_sampled(sdt):
     """Full-size workload: 4 packed sequences of 1024, 3000, 8192, 8192 tokens, 16 key / 32 value
