@@ -25,8 +25,12 @@
 // the workspace.  Kernel 2 (sequential over chunks, one workgroup per
 // (sequence, value head, 32-column dv block); each dv column of S evolves on
 // its own given k, g and beta): the S-dependent products [K;Q] S, T R, P U and
-// K~^T U on fp32 MFMA with the state block resident in LDS, the state read
-// from its slot once and written back, rounded, once.
+// K~^T U on MFMA with the state block resident in LDS, the state read from its
+// slot once and written back, rounded, once.  Kernel 2 has three variants:
+// bf16 inputs at dk = 64 / 128 (the key- and query-side products on bf16 MFMA
+// with the fp32 side split in three bf16 terms, fixed wave roles), f16 inputs
+// at dk = 64 / 128 (the same operand layout, fp32 MFMA), and the first,
+// LDS-staged fp32 design for fp32 inputs and small head dims.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
