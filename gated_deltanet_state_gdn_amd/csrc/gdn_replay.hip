@@ -331,9 +331,22 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
       for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
       __syncthreads();
 
-      // the cnt steps S <- e^{g} S;  d = beta (v - S^T k);  S <- S + k d^T, per column
+      // the cnt steps S <- e^{g} S;  d = beta (v - S^T k);  S <- S + k d^T, per column.
+      // The tile is held as S = sc * S' with the decays in the scalar sc, so a
+      // step costs one FMA per element: S' <- S' + k (d / sc).  When sc falls
+      // below 2^-64 (an underflowed decay included) it is folded into S' before
+      // the step, so 1/sc stays finite and the tile far from fp32 range.
+      float sc = 1.f;
       for (int j = 0; j < cnt; ++j) {
-        const float al = e_a[j], be = e_b[j];
+        const float be = e_b[j];
+        sc *= e_a[j];
+        if (sc < 0x1p-64f) {  // uniform over the workgroup
+#pragma unroll
+          for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s[pp][e] *= sc;
+          sc = 1.f;
+        }
         float kr[PASSES];
         const float* kp = e_kp + j * D + rs * PASSES;
 #pragma unroll
@@ -345,13 +358,20 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
         for (int pp = 0; pp < PASSES; ++pp)
 #pragma unroll
           for (int e = 0; e < VEC; ++e) xs[e] = fmaf(s[pp][e], kr[pp], xs[e]);
+        const float inv = 1.f / sc;
         float dl[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dl[e] = be * (e_v[j * D + c0 + e] - al * xor_sum_from<CG>(xs[e]));
+        for (int e = 0; e < VEC; ++e) dl[e] = inv * be * (e_v[j * D + c0 + e] - sc * xor_sum_from<CG>(xs[e]));
 #pragma unroll
         for (int pp = 0; pp < PASSES; ++pp)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr[pp] * dl[e]);
+          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(kr[pp], dl[e], s[pp][e]);
+      }
+      if (sc != 1.f) {
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s[pp][e] *= sc;
       }
       if (cnt > 0) {
 #pragma unroll

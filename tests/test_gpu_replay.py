@@ -129,6 +129,19 @@ def test_replay_standard_decode_with_folds(sdt, D):
     c.check_state("flush")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_replay_strong_decay_folds(D):
+    """Strong decay (a + 6) on L = 16: within one fold the running decay of the tile drops far
+    below 2^-64 and is folded into it; every row checked after each fold and the flush."""
+    c = ReplayCase(61 + D, 4, 1, 2, D, 16, "f32", 6)
+    for step in range(34):
+        c.step(step, 1, a_shift=6.0)
+        if step % 16 in (0, 15):
+            c.check_state(f"step {step}")
+    c.flush()
+    c.check_state("flush")
+
+
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 def test_replay_spec_windows_with_rollback(sdt):
     """T = 3 windows on L = 8 with seeded rejections; then a flush."""
