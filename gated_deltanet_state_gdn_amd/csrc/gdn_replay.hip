@@ -660,6 +660,248 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   }
 }
 
+// ---------------------------------------------------------------- prep, one wave per unit
+// For rings of at most 16 entries, 16-bit inputs and D = 64 or 128.  Lane l
+// stands for live entry e = l % 16 (the committed entries in ring order, then
+// the window) and keeps that entry's key and value rows in registers: with
+// g = l / 16 and NS = D / 32, the 16-byte chunks NS g .. NS g + NS - 1, one
+// contiguous run per lane.  That is the operand layout of the 16x16x32 MFMA
+// with the reduction index permuted alike on both sides, so the Gram tile
+// K K^T is one MFMA chain over the key registers and K Q^T a second over the
+// window queries (lane l holds query l % 16).  Every 16-lane row runs the back
+// substitution alike (lane e ends with c_e); the terms of w and acc are then
+// summed over the 16 entries by a DPP reduce-scatter that leaves each lane
+// finished columns.  One wave and no workgroup barrier, so twice the units of
+// the two-wave kernel stay in flight; the window goes to the ring straight
+// from the registers that loaded it.
+
+// One halving step of a reduce-scatter over 16-lane rows: lanes with `up` keep
+// the upper half of x[0 .. 2H - 1], their partner (lane ^ M) the lower half;
+// each adds the half it keeps to the partner's copy of it.
+template <int M, int H, int N>
+__device__ __forceinline__ void rs_halve(float (&x)[N], bool up) {
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = up ? x[i] : x[i + H];
+    const float keep = up ? x[i + H] : x[i];
+    float got;
+    if constexpr (M == 8) got = dpp_mov<0x128>(send);                   // row_ror:8 is lane ^ 8
+    else if constexpr (M == 4) got = dpp_mov<0x1B>(dpp_mov<0x141>(send));  // half mirror, then quad reverse
+    else if constexpr (M == 2) got = dpp_mov<0x4E>(send);               // quad_perm [2, 3, 0, 1]
+    else got = dpp_mov<0xB1>(send);                                     // quad_perm [1, 0, 3, 2]
+    x[i] = keep + got;
+  }
+}
+// On return x[0] of lane e (e = lane % 16) holds the sum over its 16-lane row of element e.
+__device__ __forceinline__ void reduce_scatter16(float (&x)[16], int e) {
+  rs_halve<8, 8>(x, (e & 8) != 0);
+  rs_halve<4, 4>(x, (e & 4) != 0);
+  rs_halve<2, 2>(x, (e & 2) != 0);
+  rs_halve<1, 1>(x, (e & 1) != 0);
+}
+
+// Dynamic LDS of the one-wave prep (bytes): window queries [T][D] (16-bit),
+// decay-weighted key products [16][16] and key / query products [16][T].
+__host__ __device__ inline size_t replay_prep16_lds_bytes(int D, int T) {
+  return (size_t)T * D * 2 + 16 * 16 * sizeof(float) + 16 * (size_t)T * sizeof(float);
+}
+
+template <int D, int IDT>
+__global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayArgs P, float* __restrict__ ws) {
+  static_assert(D == 64 || D == 128, "two or four 16-byte chunks per lane");
+  static_assert(IDT == GDN_BF16 || IDT == GDN_F16, "16-bit inputs");
+  constexpr int NS = D / 32;  // chunks per lane and row
+  constexpr int RB = 2 * D;   // bytes per row
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  extern __shared__ uint32_t s_words[];
+
+  const DecodeArgs& p = P.d;
+  const RingArgs& R = P.ring;
+  const int T = P.T, L = R.L;
+  const int lane = threadIdx.x, e = lane & 15, g = lane >> 4;
+  const int b = blockIdx.x / p.Hv;
+  const int h = blockIdx.x - b * p.Hv;
+  const int hk = h / (p.Hv / p.Hk);
+  const int coff = g * NS * 16;  // byte offset of this lane's run in a row
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(s_words);                   // [T][D]
+  float* s_F = reinterpret_cast<float*>(s_words + (T * D) / 2);           // [16][16]
+  float* s_kq = s_F + 16 * 16;                                            // [16][T]
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  // ---- round 1: the slot and the window queries (lane e: query e)
+  const int slot = p.slot_map[b];
+  u32x4 qx[NS];
+  {
+    const bool qv = e < T;
+    const char* src = static_cast<const char*>(p.q) + (((int64_t)b * T + (qv ? e : 0)) * p.Hk + hk) * RB + coff;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qx[s] = qv ? *reinterpret_cast<const u32x4*>(src + 16 * s) : z4;
+  }
+  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
+  const int64_t unit = (int64_t)slot * p.Hv + h;
+  const RingPos rp = ring_pos(R, unit);
+  const int st = rp.st;
+  const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
+  const int n_all = cnt + T;           // <= L <= 16
+
+  // the queries wait in LDS (their registers are free during round 2) for the
+  // K Q^T operands and the e^{G_n} q term of w
+  if (e < T) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(s_q + e * D + 8 * (NS * g + s)) = qx[s];
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- round 2: lane e loads live entry e, a committed one from ring position
+  // (st + e) % L and a window one (position e - cnt) from the inputs; that ring
+  // position is also where a window entry is appended
+  const bool live = e < n_all, committed = e < cnt;
+  const int tw = committed ? 0 : min(e - cnt, T - 1);
+  const int64_t rj = unit * L + (st + e) % L;
+  const char* ks = committed ? static_cast<const char*>(R.k) + rj * RB
+                             : static_cast<const char*>(p.k) + (((int64_t)b * T + tw) * p.Hk + hk) * RB;
+  const char* vs = committed ? static_cast<const char*>(R.v) + rj * RB
+                             : static_cast<const char*>(p.v) + (((int64_t)b * T + tw) * p.Hv + h) * RB;
+  u32x4 kx[NS], vx[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kx[s] = live ? *reinterpret_cast<const u32x4*>(ks + coff + 16 * s) : z4;
+    vx[s] = live ? *reinterpret_cast<const u32x4*>(vs + coff + 16 * s) : z4;
+  }
+  float gl = 0.f, bl = 0.f;
+  if (live) {
+    if (committed) {
+      gl = R.g[rj];
+      bl = R.beta[rj];
+    } else {
+      const int64_t gi = ((int64_t)b * T + tw) * p.Hv + h;
+      gl = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
+      bl = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+    }
+  }
+  // ---- prefix sums G of g in live order (each 16-lane row alike)
+  float G = gl;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const float y = __shfl_up(G, off, 16);
+    if (e >= off) G += y;
+  }
+
+  // ---- append the window to the ring and move the pointers
+  if (live && !committed) {
+    char* kd = static_cast<char*>(R.k) + rj * RB + coff;
+    char* vd = static_cast<char*>(R.v) + rj * RB + coff;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      *reinterpret_cast<u32x4*>(kd + 16 * s) = kx[s];
+      *reinterpret_cast<u32x4*>(vd + 16 * s) = vx[s];
+    }
+    if (g == 0) {
+      R.g[rj] = gl;
+      R.beta[rj] = bl;
+    }
+  }
+  if (lane == 0) {
+    R.start[unit] = st;
+    R.count[unit] = n_all;
+  }
+
+  // ---- K K^T and K Q^T; element r of lane (e, g) is row 4 g + r, column e
+  f32x4 kk = {0.f, 0.f, 0.f, 0.f}, kq = kk;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qx[s] = e < T ? *reinterpret_cast<const u32x4*>(s_q + e * D + 8 * (NS * g + s)) : z4;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if constexpr (IDT == GDN_BF16) {
+      kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[s]), __builtin_bit_cast(bf16x8, kx[s]),
+                                                   kk, 0, 0, 0);
+      kq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kx[s]), __builtin_bit_cast(bf16x8, qx[s]),
+                                                   kq, 0, 0, 0);
+    } else {
+      kk = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kx[s]), __builtin_bit_cast(f16x8, kx[s]),
+                                                  kk, 0, 0, 0);
+      kq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kx[s]), __builtin_bit_cast(f16x8, qx[s]),
+                                                  kq, 0, 0, 0);
+    }
+  }
+  // decay weights (every exponent <= 0): F[i][j] = e^{G_i - G_j} k_i . k_j for
+  // j < i; kq[j][t] = e^{G_{cnt+t} - G_j} k_j . q_t for j <= cnt + t
+  {
+    const float Gt = __shfl(G, min(cnt + e, 15), 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const float Gi = __shfl(G, i, 64);
+      s_F[i * 16 + e] = e < i ? expf(Gi - G) * kk[r] : 0.f;
+      if (e < T) s_kq[i * T + e] = i <= cnt + e ? expf(Gt - Gi) * kq[r] : 0.f;
+    }
+  }
+  __syncthreads();  // a single wave: orders the LDS writes before the reads
+
+  float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
+  const float eG = expf(G);
+  for (int t = 0; t < T; ++t) {
+    // the rows stay packed: opaque per position, so their widened values are
+    // not hoisted out of the loop (they would take four times the registers)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t ku = kx[s][w], vu = vx[s][w];
+        asm volatile("" : "+v"(ku), "+v"(vu));
+        kx[s][w] = ku;
+        vx[s][w] = vu;
+      }
+    // ---- back substitution, rows alike: lane e holds the residual of entry e;
+    // c_i = beta_i r_i, then every earlier entry drops its term
+    float r = s_kq[e * T + t], c = 0.f;
+    {
+      float fcol[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) fcol[i] = s_F[i * 16 + e];
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        const float ci = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl * r), i));
+        c = e == i ? ci : c;
+        r = fmaf(-fcol[i], ci, r);
+      }
+    }
+    // ---- w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j and acc_t = sum_j c_j v_j,
+    // a half row at a time (the scheduling barriers keep the widened rows from
+    // being formed all at once, which would take four times the registers)
+    __builtin_amdgcn_sched_barrier(0);
+    const float ec = eG * c;
+    const float eGn = expf(__shfl(G, cnt + t, 64));
+#pragma unroll
+    for (int hh = 0; hh < NS / 2; ++hh) {
+      const int col = 8 * NS * g + 16 * hh + e;  // the column this lane finishes
+      float x[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[8 * s2 + 2 * w] = -ec * unpack_lo<IDT>(kx[2 * hh + s2][w]);
+          x[8 * s2 + 2 * w + 1] = -ec * unpack_hi<IDT>(kx[2 * hh + s2][w]);
+        }
+      reduce_scatter16(x, e);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t qh = s_q[t * D + col];
+      wsu[2 * t * D + col] = fmaf(eGn, IDT == GDN_BF16 ? bf16_bits_to_f32(qh) : f16_bits_to_f32(qh), x[0]);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[8 * s2 + 2 * w] = c * unpack_lo<IDT>(vx[2 * hh + s2][w]);
+          x[8 * s2 + 2 * w + 1] = c * unpack_hi<IDT>(vx[2 * hh + s2][w]);
+        }
+      reduce_scatter16(x, e);
+      __builtin_amdgcn_sched_barrier(0);
+      wsu[(2 * t + 1) * D + col] = x[0];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- stream
 template <int SDT, int D, bool NT, int TB>
 __global__ void __launch_bounds__((ReplayGeom<SDT, D>::NW * 64))
@@ -831,12 +1073,23 @@ static hipError_t launch_replay_t(const ReplayArgs& a, float* ws, hipStream_t s)
   if (e != hipSuccess || a.T == 0) return e;
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   constexpr int NWP = GDN_REPLAY_PREP_WAVES;
+  if constexpr (D == 64 || D == 128) {
+    if (!f32_in && a.ring.L <= 16) {
+      const size_t lds = replay_prep16_lds_bytes(D, a.T);
+      if (a.d.in_dt == GDN_BF16)
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_BF16>), dim3(grid), dim3(64), lds, s, a, ws);
+      else
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_F16>), dim3(grid), dim3(64), lds, s, a, ws);
+      goto prep_done;
+    }
+  }
   if (f32_in)
     hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 4, NWP>), dim3(grid), dim3(NWP * 64),
                        replay_prep_words(D, 4, a.ring.L, a.T) * sizeof(float), s, a, ws);
   else
     hipLaunchKernelGGL((gdn_replay_prep_kernel<D, 2, NWP>), dim3(grid), dim3(NWP * 64),
                        replay_prep_words(D, 2, a.ring.L, a.T) * sizeof(float), s, a, ws);
+prep_done:
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.read_pool == nullptr) return launch_stream_any<D>(a, SDT, ws, s);
