@@ -31,15 +31,13 @@
 #ifndef GDN_REPLAY_NT_F32
 #define GDN_REPLAY_NT_F32 1
 #endif
-// waves per workgroup of the stream and fold kernels
+// waves per workgroup of the stream kernel, every checkpoint dtype (for 16-bit
+// tiles two waves ran T = 5 windows 10% slower on MI355X, eight no faster)
 #ifndef GDN_REPLAY_WAVES
 #define GDN_REPLAY_WAVES 4
 #endif
-#ifndef GDN_REPLAY_WAVES_16
-#define GDN_REPLAY_WAVES_16 2
-#endif
-// waves per workgroup of the prep kernel (one unit per workgroup; 2 measured
-// best on MI355X: 1 leaves phases serial, 4 halves the units in flight)
+// waves per workgroup of the two-wave prep kernel (one unit per workgroup;
+// 1 leaves its phases serial, 4 halves the units in flight)
 #ifndef GDN_REPLAY_PREP_WAVES
 #define GDN_REPLAY_PREP_WAVES 2
 #endif
@@ -47,7 +45,7 @@
 namespace gdn {
 
 template <int SDT, int D>
-using ReplayGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_REPLAY_WAVES : GDN_REPLAY_WAVES_16>;
+using ReplayGeom = TileGeom<SDT, D, GDN_REPLAY_WAVES>;
 
 constexpr int kStageRows = 16;  // entry rows staged per batch of loads
 constexpr int kStreamTB = 4;    // window positions reduced per pass over the tile
