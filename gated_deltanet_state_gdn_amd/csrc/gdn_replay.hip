@@ -659,57 +659,37 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
 }
 
 // ---------------------------------------------------------------- prep, one wave per unit
-// For rings of at most 16 entries, 16-bit inputs and D = 64 or 128.  Lane l
-// stands for live entry e = l % 16 (the committed entries in ring order, then
-// the window) and keeps that entry's key and value rows in registers: with
-// g = l / 16 and NS = D / 32, the 16-byte chunks NS g .. NS g + NS - 1, one
-// contiguous run per lane.  That is the operand layout of the 16x16x32 MFMA
-// with the reduction index permuted alike on both sides, so the Gram tile
-// K K^T is one MFMA chain over the key registers and K Q^T a second over the
-// window queries (lane l holds query l % 16).  Every 16-lane row runs the back
-// substitution alike (lane e ends with c_e); the terms of w and acc are then
-// summed over the 16 entries by a DPP reduce-scatter that leaves each lane
-// finished columns.  One wave and no workgroup barrier, so twice the units of
-// the two-wave kernel stay in flight; the window goes to the ring straight
-// from the registers that loaded it.
+// For rings of at most 16 entries, 16-bit inputs and D = 64 or 128: one wave
+// per unit and no workgroup barrier.  For the key products lane l stands for
+// live entry e = l % 16 (the committed entries in ring order, then the window)
+// and holds that entry's key row in the operand layout of the 16x16x32 MFMA:
+// with g = l / 16 and NS = D / 32, the 16-byte chunks NS g .. NS g + NS - 1,
+// the reduction index permuted alike on both sides so that each lane reads
+// one contiguous run.  K K^T is then one MFMA chain over the key registers and
+// K Q^T a second over the window queries.  Every 16-lane row runs the back
+// substitution alike.  For w and acc the wave switches to columns: lane l owns
+// columns CPL l .. CPL l + CPL - 1 (CPL = D / 64) of every value row (loaded
+// one row per instruction) and of every key row (read back from LDS), so both
+// are plain sums over the entries with the coefficients in scalar registers.
+// The window goes to the ring straight from the registers that loaded it.
 
-// One halving step of a reduce-scatter over 16-lane rows: lanes with `up` keep
-// the upper half of x[0 .. 2H - 1], their partner (lane ^ M) the lower half;
-// each adds the half it keeps to the partner's copy of it.
-template <int M, int H, int N>
-__device__ __forceinline__ void rs_halve(float (&x)[N], bool up) {
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    const float send = up ? x[i] : x[i + H];
-    const float keep = up ? x[i + H] : x[i];
-    float got;
-    if constexpr (M == 8) got = dpp_mov<0x128>(send);                   // row_ror:8 is lane ^ 8
-    else if constexpr (M == 4) got = dpp_mov<0x1B>(dpp_mov<0x141>(send));  // half mirror, then quad reverse
-    else if constexpr (M == 2) got = dpp_mov<0x4E>(send);               // quad_perm [2, 3, 0, 1]
-    else got = dpp_mov<0xB1>(send);                                     // quad_perm [1, 0, 3, 2]
-    x[i] = keep + got;
-  }
-}
-// On return x[0] of lane e (e = lane % 16) holds the sum over its 16-lane row of element e.
-__device__ __forceinline__ void reduce_scatter16(float (&x)[16], int e) {
-  rs_halve<8, 8>(x, (e & 8) != 0);
-  rs_halve<4, 4>(x, (e & 4) != 0);
-  rs_halve<2, 2>(x, (e & 2) != 0);
-  rs_halve<1, 1>(x, (e & 1) != 0);
-}
-
-// Dynamic LDS of the one-wave prep (bytes): window queries [T][D] (16-bit),
-// decay-weighted key products [16][16] and key / query products [16][T].
+// Dynamic LDS of the one-wave prep (bytes): window queries [T][D] and key rows
+// [16][D] (16-bit), decay-weighted key products [16][16] and key / query
+// products [16][T] (floats).
 __host__ __device__ inline size_t replay_prep16_lds_bytes(int D, int T) {
-  return (size_t)T * D * 2 + 16 * 16 * sizeof(float) + 16 * (size_t)T * sizeof(float);
+  return (size_t)T * D * 2 + 16 * (size_t)D * 2 + 16 * 16 * sizeof(float) + 16 * (size_t)T * sizeof(float);
 }
+
+// e^x for x <= 0 on the hardware base-2 exponential (underflows to zero)
+__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 template <int D, int IDT>
-__global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayArgs P, float* __restrict__ ws) {
+__global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayArgs P, float* __restrict__ ws) {
   static_assert(D == 64 || D == 128, "two or four 16-byte chunks per lane");
   static_assert(IDT == GDN_BF16 || IDT == GDN_F16, "16-bit inputs");
-  constexpr int NS = D / 32;  // chunks per lane and row
-  constexpr int RB = 2 * D;   // bytes per row
+  constexpr int NS = D / 32;   // MFMA chunks per lane and row
+  constexpr int RB = 2 * D;    // bytes per row
+  constexpr int CPL = D / 64;  // columns per lane in the column layout
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   extern __shared__ uint32_t s_words[];
@@ -721,11 +701,22 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
   const int b = blockIdx.x / p.Hv;
   const int h = blockIdx.x - b * p.Hv;
   const int hk = h / (p.Hv / p.Hk);
-  const int coff = g * NS * 16;  // byte offset of this lane's run in a row
-  uint16_t* s_q = reinterpret_cast<uint16_t*>(s_words);                   // [T][D]
-  float* s_F = reinterpret_cast<float*>(s_words + (T * D) / 2);           // [16][16]
-  float* s_kq = s_F + 16 * 16;                                            // [16][T]
+  const int coff = g * NS * 16;  // byte offset of this lane's MFMA run in a row
+  const int ccol = CPL * lane;   // first column of this lane in the column layout
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(s_words);  // [T][D]
+  uint16_t* s_k = s_q + T * D;                           // [16][D]
+  float* s_F = reinterpret_cast<float*>(s_k + 16 * D);   // [16][16]
+  float* s_kq = s_F + 16 * 16;                           // [16][T]
   const u32x4 z4 = {0u, 0u, 0u, 0u};
+  // this lane's CPL 16-bit columns of a row (zero-extended when CPL = 1)
+  auto cols_at = [&](const void* row) -> uint32_t {
+    if constexpr (CPL == 2) return *reinterpret_cast<const uint32_t*>(static_cast<const char*>(row) + 2 * ccol);
+    else return *reinterpret_cast<const uint16_t*>(static_cast<const char*>(row) + 2 * ccol);
+  };
+  auto widen = [&](uint32_t x, float (&f)[CPL]) {
+    f[0] = IDT == GDN_BF16 ? bf16_bits_to_f32(x & 0xffffu) : f16_bits_to_f32(x & 0xffffu);
+    if constexpr (CPL == 2) f[1] = IDT == GDN_BF16 ? bf16_bits_to_f32(x >> 16) : f16_bits_to_f32(x >> 16);
+  };
 
   // ---- round 1: the slot and the window queries (lane e: query e)
   const int slot = p.slot_map[b];
@@ -751,21 +742,28 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
   }
   asm volatile("" ::: "memory");
 
-  // ---- round 2: lane e loads live entry e, a committed one from ring position
+  // ---- round 2: lane e loads key row e, a committed entry from ring position
   // (st + e) % L and a window one (position e - cnt) from the inputs; that ring
-  // position is also where a window entry is appended
+  // position is also where a window entry is appended.  Value rows go by
+  // columns: row j is one load over the wave.
   const bool live = e < n_all, committed = e < cnt;
   const int tw = committed ? 0 : min(e - cnt, T - 1);
   const int64_t rj = unit * L + (st + e) % L;
   const char* ks = committed ? static_cast<const char*>(R.k) + rj * RB
                              : static_cast<const char*>(p.k) + (((int64_t)b * T + tw) * p.Hk + hk) * RB;
-  const char* vs = committed ? static_cast<const char*>(R.v) + rj * RB
-                             : static_cast<const char*>(p.v) + (((int64_t)b * T + tw) * p.Hv + h) * RB;
-  u32x4 kx[NS], vx[NS];
+  u32x4 kx[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    kx[s] = live ? *reinterpret_cast<const u32x4*>(ks + coff + 16 * s) : z4;
-    vx[s] = live ? *reinterpret_cast<const u32x4*>(vs + coff + 16 * s) : z4;
+  for (int s = 0; s < NS; ++s) kx[s] = live ? *reinterpret_cast<const u32x4*>(ks + coff + 16 * s) : z4;
+  uint32_t vr[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t x = 0u;
+    if (j < n_all) {  // uniform
+      const char* row = j < cnt ? static_cast<const char*>(R.v) + (unit * L + (st + j) % L) * RB
+                                : static_cast<const char*>(p.v) + (((int64_t)b * T + (j - cnt)) * p.Hv + h) * RB;
+      x = cols_at(row);
+    }
+    vr[j] = x;
   }
   float gl = 0.f, bl = 0.f;
   if (live) {
@@ -778,6 +776,7 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
       bl = sigmoid_f(load_elem(p.b, gi, p.in_dt));
     }
   }
+
   // ---- prefix sums G of g in live order (each 16-lane row alike)
   float G = gl;
 #pragma unroll
@@ -786,18 +785,24 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
     if (e >= off) G += y;
   }
 
-  // ---- append the window to the ring and move the pointers
+  // ---- key rows to LDS for the column layout; append the window to the ring
+#pragma unroll
+  for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(s_k + e * D + 8 * (NS * g + s)) = kx[s];
   if (live && !committed) {
     char* kd = static_cast<char*>(R.k) + rj * RB + coff;
-    char* vd = static_cast<char*>(R.v) + rj * RB + coff;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      *reinterpret_cast<u32x4*>(kd + 16 * s) = kx[s];
-      *reinterpret_cast<u32x4*>(vd + 16 * s) = vx[s];
-    }
+    for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(kd + 16 * s) = kx[s];
     if (g == 0) {
       R.g[rj] = gl;
       R.beta[rj] = bl;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= cnt && j < n_all) {  // uniform
+      char* row = static_cast<char*>(R.v) + (unit * L + (st + j) % L) * RB + 2 * ccol;
+      if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(row) = vr[j];
+      else *reinterpret_cast<uint16_t*>(row) = (uint16_t)vr[j];
     }
   }
   if (lane == 0) {
@@ -831,33 +836,32 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
       const float Gi = __shfl(G, i, 64);
-      s_F[i * 16 + e] = e < i ? expf(Gi - G) * kk[r] : 0.f;
-      if (e < T) s_kq[i * T + e] = i <= cnt + e ? expf(Gt - Gi) * kq[r] : 0.f;
+      s_F[i * 16 + e] = e < i ? exp_neg(Gi - G) * kk[r] : 0.f;
+      if (e < T) s_kq[i * T + e] = i <= cnt + e ? exp_neg(Gt - Gi) * kq[r] : 0.f;
     }
   }
-  __syncthreads();  // a single wave: orders the LDS writes before the reads
+  // the LDS writes above are read by other lanes below: a wave-level barrier
+  // (LDS requests of one wave complete in order; this keeps the compiler's)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
-  const float eG = expf(G);
+  const float eG = exp_neg(G);
   for (int t = 0; t < T; ++t) {
-    // the rows stay packed: opaque per position, so their widened values are
-    // not hoisted out of the loop (they would take four times the registers)
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t ku = kx[s][w], vu = vx[s][w];
-        asm volatile("" : "+v"(ku), "+v"(vu));
-        kx[s][w] = ku;
-        vx[s][w] = vu;
-      }
+    // LDS bases made opaque per position: the loop-invariant reads below stay
+    // inside the loop instead of holding 32 registers across it
+    int zoff = 0;
+    asm volatile("" : "+v"(zoff));
+    const float* s_Ft = s_F + zoff;
+    const uint16_t* s_kt = s_k + zoff;
     // ---- back substitution, rows alike: lane e holds the residual of entry e;
     // c_i = beta_i r_i, then every earlier entry drops its term
     float r = s_kq[e * T + t], c = 0.f;
     {
       float fcol[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) fcol[i] = s_F[i * 16 + e];
+      for (int i = 0; i < 16; ++i) fcol[i] = s_Ft[i * 16 + e];
 #pragma unroll
       for (int i = 15; i >= 0; --i) {
         const float ci = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl * r), i));
@@ -865,37 +869,33 @@ __global__ void __launch_bounds__(64, 7) gdn_replay_prep16_kernel(const ReplayAr
         r = fmaf(-fcol[i], ci, r);
       }
     }
-    // ---- w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j and acc_t = sum_j c_j v_j,
-    // a half row at a time (the scheduling barriers keep the widened rows from
-    // being formed all at once, which would take four times the registers)
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- by columns: acc_t = sum_j c_j v_j and w_t = e^{G_n} q_t - sum_j e^{G_j} c_j k_j
     const float ec = eG * c;
-    const float eGn = expf(__shfl(G, cnt + t, 64));
+    const float eGn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, eG), cnt + t));
+    float acc[CPL], w[CPL], x[CPL];
+    widen(cols_at(s_q + t * D), x);
 #pragma unroll
-    for (int hh = 0; hh < NS / 2; ++hh) {
-      const int col = 8 * NS * g + 16 * hh + e;  // the column this lane finishes
-      float x[16];
+    for (int u = 0; u < CPL; ++u) {
+      acc[u] = 0.f;
+      w[u] = eGn * x[u];
+    }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+    for (int j = 0; j < 16; ++j) {
+      const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), j));
+      const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ec), j));
+      widen(vr[j], x);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          x[8 * s2 + 2 * w] = -ec * unpack_lo<IDT>(kx[2 * hh + s2][w]);
-          x[8 * s2 + 2 * w + 1] = -ec * unpack_hi<IDT>(kx[2 * hh + s2][w]);
-        }
-      reduce_scatter16(x, e);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint32_t qh = s_q[t * D + col];
-      wsu[2 * t * D + col] = fmaf(eGn, IDT == GDN_BF16 ? bf16_bits_to_f32(qh) : f16_bits_to_f32(qh), x[0]);
+      for (int u = 0; u < CPL; ++u) acc[u] = fmaf(cj, x[u], acc[u]);
+      widen(cols_at(s_kt + j * D), x);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          x[8 * s2 + 2 * w] = c * unpack_lo<IDT>(vx[2 * hh + s2][w]);
-          x[8 * s2 + 2 * w + 1] = c * unpack_hi<IDT>(vx[2 * hh + s2][w]);
-        }
-      reduce_scatter16(x, e);
-      __builtin_amdgcn_sched_barrier(0);
-      wsu[(2 * t + 1) * D + col] = x[0];
+      for (int u = 0; u < CPL; ++u) w[u] = fmaf(-ej, x[u], w[u]);
+    }
+    if constexpr (CPL == 2) {
+      *reinterpret_cast<float2*>(wsu + 2 * t * D + ccol) = make_float2(w[0], w[1]);
+      *reinterpret_cast<float2*>(wsu + (2 * t + 1) * D + ccol) = make_float2(acc[0], acc[1]);
+    } else {
+      wsu[2 * t * D + ccol] = w[0];
+      wsu[(2 * t + 1) * D + ccol] = acc[0];
     }
   }
 }
