@@ -391,6 +391,283 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
   }
 }
 
+// e^x for x <= 0 on the hardware base-2 exponential (underflows to zero)
+__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// ---------------------------------------------------------------- fold on MFMA
+// The fold in its chunked (WY) form for D = 64 or 128 and rings of at most 16
+// entries.  With G_i the prefix sums of g over the n committed entries,
+//     d = (I + diag(beta) F)^-1 diag(beta) (V - diag(e^G) K S0),
+//     F[i][j] = e^{G_i - G_j} k_i . k_j  (j < i),
+//     S_n = e^{G_n} S0 + K^T diag(e^{G_n - G}) d,
+// which is the sequential recurrence unrolled (the chunked form of the GDN
+// paper's section on hardware-efficient training, with one chunk of n rows).
+// K S0 and the rank-n update are fp32 MFMA chains (v_mfma_f32_16x16x4_f32):
+// wave w holds columns 16 J .. 16 J + 15 (J = NJ w .. NJ w + NJ - 1) of every
+// row in the accumulator layout (block (I, J), element r of lane (c, g): row
+// 16 I + 4 g + r, column 16 J + c).  Both chains take their checkpoint or
+// update operand straight from those registers by running the reduction over
+// rows {16 I + 4 g + r : g} at step (I, r), the same permutation on both
+// sides.  Each wave forms the 16 x 16 factor (I + diag(beta) F)^-1 diag(beta)
+// itself from its own K K^T, so the waves never wait for one another after
+// staging.  Entries past n are zero rows with zero gates and drop out.
+constexpr int kFoldKTS = 20;  // LDS stride of the transposed keys: 16 entries + 4 (conflict-free reads)
+
+__host__ __device__ inline size_t replay_fold_mfma_lds_bytes(int D) {
+  return ((size_t)D * kFoldKTS + 2 * 16 * ((size_t)D + 4) + 2 * 16 + 4 * 16 * 17) * sizeof(float);
+}
+
+template <int SDT, int D, bool NT, int EB, int CDT>
+__global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
+  static_assert(D == 64 || D == 128, "four waves of 16-column blocks");
+  constexpr int NI = D / 16;  // row blocks
+  constexpr int NJ = D / 64;  // column blocks per wave
+  constexpr int KTS = kFoldKTS, VS = D + 4;
+  constexpr int NTH = 256;
+  using ST = typename StateElem<SDT>::T;
+
+  extern __shared__ float s_dyn[];
+  __shared__ int s_list[64];
+  __shared__ int s_n;
+
+  const DecodeArgs& p = P.d;
+  const RingArgs& R = P.ring;
+  const int T = P.T, L = R.L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int units = p.B * p.Hv;
+  float* e_kt = s_dyn;                  // [D][KTS]: key element (entry e, row r) at r KTS + e
+  float* e_k = e_kt + D * KTS;          // [16][VS]: key rows
+  float* e_v = e_k + 16 * VS;           // [16][VS]: value rows
+  float* e_G = e_v + 16 * VS;           // [16] prefix sums of g
+  float* e_b = e_G + 16;                // [16] beta
+  float* s_m = e_b + 16 + wave * 16 * 17;  // this wave's [16][17] factor
+  constexpr int VE = 16 / EB, CPR = D / VE;  // ring row elements per 16-byte load, loads per row
+
+  // Tile elements go through buffer instructions: one per-lane byte offset and
+  // a scalar offset per element, so the 4 NI NJ accesses of a lane need no
+  // address registers of their own.
+  constexpr int SB = (int)sizeof(ST);
+  auto ld_state = [&](__amdgpu_buffer_rsrc_t rs, int voff, int soff) -> float {
+    if constexpr (SDT == GDN_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+    else if constexpr (SDT == GDN_BF16) return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+    else return f16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+  };
+  auto st_state = [&](__amdgpu_buffer_rsrc_t rs, int voff, int soff, float x, auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if constexpr (DT == GDN_F32)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack2<DT>(x, 0.f) & 0xffffu), rs, voff, soff, 0);
+  };
+
+  const int grid_n = gridDim.x;
+  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
+    if (wave == 0) {
+      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
+      const int x = xl < units ? (int)xl : units;
+      bool need = false;
+      if (x < units) {
+        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+        const int slot = p.slot_map[b];
+        if (slot >= 0 && (int64_t)slot < p.num_slots) {
+          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+        }
+      }
+      const uint64_t mask = __ballot(need);
+      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
+      if (lane == 0) s_n = __popcll(mask);
+    }
+    __syncthreads();
+    const int n_fold = s_n;
+    for (int f = 0; f < n_fold; ++f) {
+      const int x = s_list[f];
+      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+      const RingPos rp = ring_pos(R, unit);
+      const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
+
+      // ---- the checkpoint tile in the accumulator layout (lane offset made
+      // opaque per unit so the addresses are not hoisted out of the unit loop)
+      const int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
+      const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<ST*>(p.pool) + unit * (int64_t)(D * D), 0, D * D * SB, 0x00020000);
+      float s0[NI][NJ][4];
+#pragma unroll
+      for (int I = 0; I < NI; ++I)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB);
+
+      // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
+      const int64_t ring_e = unit * L;
+      for (int q = tid; q < 16 * CPR; q += NTH) {
+        const int t = q / CPR, cc = (q - t * CPR) * VE;
+        u32x4 kw = {0u, 0u, 0u, 0u}, vw = kw;
+        if (t < cnt) {
+          const int64_t row = (ring_e + (st + t) % L) * D + cc;
+          kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + row * EB);
+          vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          float kf, vf;
+          if constexpr (EB == 4) {
+            kf = __uint_as_float(kw[e]);
+            vf = __uint_as_float(vw[e]);
+          } else {
+            const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
+            const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
+            kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
+            vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+          }
+          e_kt[(cc + e) * KTS + t] = kf;
+          e_k[t * VS + cc + e] = kf;
+          e_v[t * VS + cc + e] = vf;
+        }
+      }
+      if (wave == 0 && lane < 16) {  // gates in live order, zero past cnt; prefix sums within the row
+        float gg = 0.f, be = 0.f;
+        if (lane < cnt) {
+          const int64_t j = ring_e + (st + lane) % L;
+          gg = R.g[j];
+          be = R.beta[j];
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float y = __shfl_up(gg, off, 16);
+          if (lane >= off) gg += y;
+        }
+        e_G[lane] = gg;
+        e_b[lane] = be;
+      }
+      __syncthreads();
+
+      if (cnt > 0) {
+        const float Gn = e_G[15];  // gates past cnt are zero: entry 15 carries G_cnt
+        // ---- K K^T; element r of lane (c, g) is (4 g + r, c)
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s4 = 0; s4 < D / 4; ++s4) {
+          const float a = e_kt[(4 * s4 + g) * KTS + c];
+          kk = __builtin_amdgcn_mfma_f32_16x16x4f32(a, a, kk, 0, 0, 0);
+        }
+        // M = I + diag(beta) F, strictly lower part (the unit diagonal is implicit)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r;
+          s_m[i * 17 + c] = c < i ? e_b[i] * exp_neg(e_G[i] - e_G[c]) * kk[r] : 0.f;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // X = M^-1 by forward substitution (lane c < 16 owns column c), then
+        // the factor X diag(beta) replaces M in place
+        if (lane < 16) {
+          float xc[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = i == c ? 1.f : 0.f;
+#pragma unroll
+            for (int k = 0; k < i; ++k) v = fmaf(-s_m[i * 17 + k], xc[k], v);
+            xc[i] = v;
+          }
+          const float bc = e_b[c];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s_m[i * 17 + c] = xc[i] * bc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- K S0 for this wave's columns, reduction over rows {16 I + 4 g + r}
+        f32x4 ks[NJ];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) ks[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < NI; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = e_kt[(16 * I + 4 * g + r) * KTS + c];
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) ks[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], ks[jj], 0, 0, 0);
+          }
+        // ---- R = V - diag(e^G) K S0, then d = factor . R (reduction over entries
+        // {4 g + r}), each row scaled by e^{G_n - G_e} for the update
+        f32x4 u[NJ];
+        float eGe[4], wGe[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float Ge = e_G[4 * g + r];
+          eGe[r] = exp_neg(Ge);
+          wGe[r] = exp_neg(Gn - Ge);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int col = 16 * (NJ * wave + jj) + c;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ks[jj][r] = e_v[(4 * g + r) * VS + col] - eGe[r] * ks[jj][r];
+          u[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            u[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_m[c * 17 + 4 * g + r], ks[jj][r], u[jj], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[jj][r] *= wGe[r];
+        }
+        // ---- S_n = e^{G_n} S0 + K^T (scaled d), reduction over entries {4 g + r}
+        const float eGn = exp_neg(Gn);
+#pragma unroll
+        for (int I = 0; I < NI; ++I) {
+          f32x4 acc[NJ];
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[jj][r] = eGn * s0[I][jj][r];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = e_k[(4 * g + r) * VS + 16 * I + c];
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, u[jj][r], acc[jj], 0, 0, 0);
+          }
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
+        }
+        // ---- write back, rounded once
+#pragma unroll
+        for (int I = 0; I < NI; ++I)
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              st_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB, s0[I][jj][r],
+                       std::integral_constant<int, SDT>{});
+      }
+      if constexpr (CDT >= 0) {
+        const __amdgpu_buffer_rsrc_t rs_copy = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D), 0, D * D * 2, 0x00020000);
+        const int coff = (4 * g * D + NJ * 16 * wave + c) * 2;
+#pragma unroll
+        for (int I = 0; I < NI; ++I)
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              st_state(rs_copy, coff, ((16 * I + r) * D + 16 * jj) * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
+      }
+      if (tid == 0) {
+        R.start[unit] = (st + cnt) % L;
+        R.count[unit] = 0;
+      }
+      __syncthreads();  // LDS staging is reused by the next unit
+    }
+    __syncthreads();  // s_list is rewritten by the next check
+  }
+}
+
 // ---------------------------------------------------------------- prep
 // Dynamic LDS of the prep kernel: packed keys and values [L][D * EB / 4 + 1]
 // words each (live entries, at most L: the committed ones then the window),
@@ -679,9 +956,6 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
 __host__ __device__ inline size_t replay_prep16_lds_bytes(int D, int T) {
   return (size_t)T * D * 2 + 16 * (size_t)D * 2 + 16 * 16 * sizeof(float) + 16 * (size_t)T * sizeof(float);
 }
-
-// e^x for x <= 0 on the hardware base-2 exponential (underflows to zero)
-__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 template <int D, int IDT>
 __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayArgs P, float* __restrict__ ws) {
@@ -1003,10 +1277,19 @@ template <int SDT, int D, int EB, int CDT>
 static hipError_t launch_fold(const ReplayArgs& a, hipStream_t s) {
   using G = FoldGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
-  const size_t lds = replay_fold_lds_bytes(D, a.ring.L);
   void (*kern)(const ReplayArgs);
   int threads;
-  if constexpr (D >= 32) {
+  size_t lds = replay_fold_lds_bytes(D, a.ring.L);
+  if constexpr ((D == 64 || D == 128) && CDT < 0) {  // the dual-precision fold measured faster on the VALU
+    if (a.ring.L <= 16) {
+      kern = &gdn_replay_fold_mfma_kernel<SDT, D, NT, EB, CDT>;
+      threads = 256;
+      lds = replay_fold_mfma_lds_bytes(D);
+    } else {
+      kern = &gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>;
+      threads = kFoldColThreads;
+    }
+  } else if constexpr (D >= 32) {
     kern = &gdn_replay_fold_kernel<SDT, D, NT, EB, CDT>;
     threads = kFoldColThreads;
   } else {

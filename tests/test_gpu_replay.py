@@ -142,6 +142,24 @@ def test_replay_strong_decay_folds(D):
     c.check_state("flush")
 
 
+@pytest.mark.parametrize("sdt,in_dt", [("f16", "bf16"), ("bf16", "f16"), ("f32", "f32")])
+@pytest.mark.parametrize("D", [64, 128])
+def test_replay_full_ring_folds(sdt, in_dt, D):
+    """L = 16 (the fold's matrix form, every ring entry live): fp16 / bf16 / fp32 checkpoints with
+    16-bit and fp32 inputs, T = 1 for 17 steps then windows of 3 with rollback, over folds."""
+    c = ReplayCase(70 + D, 3, 1, 2, D, 16, sdt, 5, in_dt=in_dt)
+    for step in range(17):
+        c.step(step, 1, a_shift=-1.0)
+        if step in (0, 15, 16):
+            c.check_state(f"step {step}")
+    for step in range(17, 23):
+        c.step(step, 3, a_shift=-1.0)
+        c.check_state(f"step {step}")
+        c.rollback(step, gen.rejected_counts(70, step, c.B, 2))
+    c.flush()
+    c.check_state("flush")
+
+
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 def test_replay_spec_windows_with_rollback(sdt):
     """T = 3 windows on L = 8 with seeded rejections; then a flush."""
