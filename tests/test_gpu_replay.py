@@ -160,6 +160,21 @@ def test_replay_full_ring_folds(sdt, in_dt, D):
     c.check_state("flush")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_replay_long_windows(D):
+    """L = 16 with windows of 16 (the whole ring, a fold before every step), 7 and 9, with
+    rollback between them; bf16 inputs, fp32 checkpoint."""
+    c = ReplayCase(80 + D, 3, 1, 2, D, 16, "f32", 5)
+    for step, T in enumerate([16, 7, 9, 16, 5, 7]):
+        c.step(step, T, a_shift=-1.0)
+        c.check_state(f"step {step} T={T}")
+        if step in (1, 4):
+            c.rollback(step, gen.rejected_counts(80, step, c.B, 3))
+            c.check_state(f"rollback {step}")
+    c.flush()
+    c.check_state("flush")
+
+
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 def test_replay_spec_windows_with_rollback(sdt):
     """T = 3 windows on L = 8 with seeded rejections; then a flush."""
