@@ -43,6 +43,8 @@ struct ReplayArgs {
   const int32_t* num_rejected;
   void* read_pool;  // dual-precision mode: the 16-bit read copy of the fp32 checkpoint (else null)
   int32_t read_dt;
+  int32_t* rec;     // [B * Hv][4] unit records (slot or -1, start and count after any fold), written by
+                    // the fold's check for the one-wave prep; null when that prep is not used
 };
 
 struct SpecArgs {

@@ -55,8 +55,13 @@ __host__ __device__ inline size_t replay_fold_lds_bytes(int D, int L) {
   return (size_t)L * (2 * ((size_t)D + 1) + 2) * sizeof(float);
 }
 
-size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D) {
+// Workspace: w and acc per (unit, window position) as floats, then one
+// 16-byte record per unit (see ReplayArgs::rec).
+size_t replay_vectors_bytes(int64_t B, int Hv, int T, int D) {
   return (size_t)B * (size_t)Hv * (size_t)T * 2 * (size_t)D * sizeof(float);
+}
+size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D) {
+  return replay_vectors_bytes(B, Hv, T, D) + (size_t)B * (size_t)Hv * 4 * sizeof(int32_t);
 }
 
 struct RingPos {
@@ -123,10 +128,13 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
       if (x < units) {
         const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
         const int slot = p.slot_map[b];
+        int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
           const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
+        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
       }
       const uint64_t mask = __ballot(need);
       if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
@@ -269,10 +277,13 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
       if (x < units) {
         const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
         const int slot = p.slot_map[b];
+        int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
           const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
+        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
       }
       const uint64_t mask = __ballot(need);
       if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
@@ -470,10 +481,13 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
       if (x < units) {
         const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
         const int slot = p.slot_map[b];
+        int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
           const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
+          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
+        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
       }
       const uint64_t mask = __ballot(need);
       if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
@@ -992,8 +1006,10 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
     if constexpr (CPL == 2) f[1] = IDT == GDN_BF16 ? bf16_bits_to_f32(x >> 16) : f16_bits_to_f32(x >> 16);
   };
 
-  // ---- round 1: the slot and the window queries (lane e: query e)
-  const int slot = p.slot_map[b];
+  // ---- round 1: the unit record (slot and the ring pointers after any fold,
+  // written by the fold's check) and the window queries (lane e: query e)
+  const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
+  const int slot = rc.x;
   u32x4 qx[NS];
   {
     const bool qv = e < T;
@@ -1001,11 +1017,10 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
 #pragma unroll
     for (int s = 0; s < NS; ++s) qx[s] = qv ? *reinterpret_cast<const u32x4*>(src + 16 * s) : z4;
   }
-  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
+  if (slot < 0) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
-  const RingPos rp = ring_pos(R, unit);
-  const int st = rp.st;
-  const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
+  const int st = rc.y;                 // in [0, L)
+  const int cnt = min(rc.z, L - T);    // the fold left room for the window
   const int n_all = cnt + T;           // <= L <= 16
 
   // the queries wait in LDS (their registers are free during round 2) for the
@@ -1348,8 +1363,14 @@ static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws,
 }
 
 template <int SDT, int D>
-static hipError_t launch_replay_t(const ReplayArgs& a, float* ws, hipStream_t s) {
-  const bool f32_in = a.d.in_dt == GDN_F32;
+static hipError_t launch_replay_t(const ReplayArgs& a0, float* ws, hipStream_t s) {
+  const bool f32_in = a0.d.in_dt == GDN_F32;
+  ReplayArgs a = a0;
+  a.rec = nullptr;
+  if constexpr (D == 64 || D == 128) {
+    if (!f32_in && a.ring.L <= 16 && a.T > 0 && ws != nullptr)  // the one-wave prep reads unit records
+      a.rec = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + replay_vectors_bytes(a.d.B, a.d.Hv, a.T, D));
+  }
   hipError_t e = f32_in ? launch_fold_any<SDT, D, 4>(a, s) : launch_fold_any<SDT, D, 2>(a, s);
   if (e != hipSuccess || a.T == 0) return e;
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);

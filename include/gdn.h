@@ -190,8 +190,9 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
  *   out    [B, T, Hv, dv] out_dtype
  *   workspace  device scratch of at least gdn_replay_workspace_bytes() bytes,
  *          256-byte aligned, owned by the caller, not read before it is
- *          written (it carries per-unit vectors between the kernels of one
- *          call); calls that share a workspace must not overlap.
+ *          written (it carries per-unit vectors and ring-pointer records
+ *          between the kernels of one call); calls that share a workspace
+ *          must not overlap.
  * Per (sequence, value head): if count + T > L, every committed entry is
  * first folded into the checkpoint (one rounding) and the ring emptied
  * (start += count mod L, count = 0); then the T new entries are appended at
