@@ -965,10 +965,11 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
 // The window goes to the ring straight from the registers that loaded it.
 
 // Dynamic LDS of the one-wave prep (bytes): window queries [T][D] and key rows
-// [16][D] (16-bit), decay-weighted key products [16][16] and key / query
-// products [16][T] (floats).
+// [16][D] (16-bit), the strictly lower decay-weighted key products packed by
+// rows (F[i][j] at i (i - 1) / 2 + j, 120 floats) and key / query products
+// [16][T].  Under 5 KiB at D = 128, T = 1, so 32 waves fit a CU.
 __host__ __device__ inline size_t replay_prep16_lds_bytes(int D, int T) {
-  return (size_t)T * D * 2 + 16 * (size_t)D * 2 + 16 * 16 * sizeof(float) + 16 * (size_t)T * sizeof(float);
+  return (size_t)T * D * 2 + 16 * (size_t)D * 2 + 120 * sizeof(float) + 16 * (size_t)T * sizeof(float);
 }
 
 template <int D, int IDT>
@@ -993,8 +994,8 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   const int ccol = CPL * lane;   // first column of this lane in the column layout
   uint16_t* s_q = reinterpret_cast<uint16_t*>(s_words);  // [T][D]
   uint16_t* s_k = s_q + T * D;                           // [16][D]
-  float* s_F = reinterpret_cast<float*>(s_k + 16 * D);   // [16][16]
-  float* s_kq = s_F + 16 * 16;                           // [16][T]
+  float* s_F = reinterpret_cast<float*>(s_k + 16 * D);   // F[i][j], j < i, at i (i - 1) / 2 + j
+  float* s_kq = s_F + 120;                               // [16][T]
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   // this lane's CPL 16-bit columns of a row (zero-extended when CPL = 1)
   auto cols_at = [&](const void* row) -> uint32_t {
@@ -1125,7 +1126,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
       const float Gi = __shfl(G, i, 64);
-      s_F[i * 16 + e] = e < i ? exp_neg(Gi - G) * kk[r] : 0.f;
+      if (e < i) s_F[i * (i - 1) / 2 + e] = exp_neg(Gi - G) * kk[r];
       if (e < T) s_kq[i * T + e] = i <= cnt + e ? exp_neg(Gt - Gi) * kq[r] : 0.f;
     }
   }
@@ -1150,7 +1151,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
     {
       float fcol[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) fcol[i] = s_Ft[i * 16 + e];
+      for (int i = 0; i < 16; ++i) fcol[i] = e < i ? s_Ft[i * (i - 1) / 2 + e] : 0.f;
 #pragma unroll
       for (int i = 15; i >= 0; --i) {
         const float ci = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl * r), i));
