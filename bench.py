@@ -289,7 +289,7 @@ def bench_spec(torch, gdn, gen, B, sdt, T, reps, cid=4):
 def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
     import numpy as np
     dev = "cuda"
-    lengths = gen.CONFIGS[3].extra["lengths"]
+    lengths = gen.WORKLOADS["prefill"].extra["lengths"]
     N = len(lengths)
     cu = gen.seq_lengths_cu(lengths)
     slot_map = gen.slot_permutation(cid, 16)[:N]
@@ -484,7 +484,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "the per-(sequence, head) units shard across GPUs without any exchange, see DESIGN.md",
+              "the per-(sequence, head) units would shard across GPUs without any exchange",
               file=sys.stderr)
         sys.exit(2)
 

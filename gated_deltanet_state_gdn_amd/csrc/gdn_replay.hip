@@ -764,7 +764,7 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   auto win_v = [&](int t) { return vin + (((int64_t)b * T + t) * p.Hv + h) * D * EB; };
   auto win_q = [&](int t) { return qin + (((int64_t)b * T + t) * p.Hk + hk) * D * EB; };
 
-  // ---- round 1: the slot, the first window rows and the window gate inputs
+  // ---- load round 1: the slot, the first window rows and the window gate inputs
   const int slot = p.slot_map[b];
   u32x4 wk[NR], wv[NR], wq[NR];
   load_batch(0, T, win_k, wk);
@@ -779,7 +779,7 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
 
-  // ---- round 2: the unit's ring pointers, then its live entries (committed,
+  // ---- load round 2: the unit's ring pointers, then its live entries (committed,
   // in ring order from the start pointer) and their gates
   const int64_t ring_e = unit * L;
   const RingPos rp = ring_pos(R, unit);
@@ -1007,7 +1007,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
     if constexpr (CPL == 2) f[1] = IDT == GDN_BF16 ? bf16_bits_to_f32(x >> 16) : f16_bits_to_f32(x >> 16);
   };
 
-  // ---- round 1: the unit record (slot and the ring pointers after any fold,
+  // ---- load round 1: the unit record (slot and the ring pointers after any fold,
   // written by the fold's check) and the window queries (lane e: query e)
   const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
   const int slot = rc.x;
@@ -1024,7 +1024,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   const int cnt = min(rc.z, L - T);    // the fold left room for the window
   const int n_all = cnt + T;           // <= L <= 16
 
-  // the queries wait in LDS (their registers are free during round 2) for the
+  // the queries wait in LDS (their registers are free during load round 2) for the
   // K Q^T operands and the e^{G_n} q term of w
   if (e < T) {
 #pragma unroll
@@ -1032,7 +1032,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   }
   asm volatile("" ::: "memory");
 
-  // ---- round 2: lane e loads key row e, a committed entry from ring position
+  // ---- load round 2: lane e loads key row e, a committed entry from ring position
   // (st + e) % L and a window one (position e - cnt) from the inputs; that ring
   // position is also where a window entry is appended.  Value rows go by
   // columns: row j is one load over the wave.

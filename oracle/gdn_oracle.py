@@ -9,7 +9,7 @@ nothing is blocked, chunked, fused or reordered.  The chunked prefill and the
 replay decode of the library are reformulations of this same recurrence, so
 this one loop is the reference for all three entry points.
 
-Sources (cited by section; see the design doc for the full reading list):
+Sources (cited by page title and section):
   [PR52191]   vLLM PR #52191 summary page (prhub.com.cn): "GDN state kept in
               FP16/BF16 on CPU AMX".  Implementation section, item 3 (the
               fused sigmoid-gating delta-rule decode kernel, the chunked
@@ -35,7 +35,7 @@ Sources (cited by section; see the design doc for the full reading list):
               with the read-out o_t = S_t^T q_t, in this library's dk x dv
               orientation of S.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * gates: g = -exp(A_log) * softplus(a + dt_bias) (a log-decay: the pages
     scale states by exp(g)), beta = sigmoid(b) (the kernel is named after a
     fused sigmoid gating); softplus is the exact max(x,0)+log1p(exp(-|x|));

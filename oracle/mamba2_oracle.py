@@ -23,7 +23,7 @@ Sources:
               head's input (headdim d), B and C (dstate n) are shared by the
               heads of a group and D is a per-head skip.
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
   * the state of a head is [d, n] (n fastest), as the pages' (nheads, d, n);
   * the log-decay is g = -exp(A_log) softplus(dt + dt_bias), the same gate
     form as the GDN path, and the write strength is dt' itself;

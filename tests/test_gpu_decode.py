@@ -68,7 +68,7 @@ def run_decode(cid, B, Hk, Hv, D, sdt, in_dt, steps, num_slots, slot_map, sample
 
 def test_decode_tiny_recurrence():
     """2 sequences, 2 heads, 16 x 16 fp32 state, 8 steps, slots [3, 1] of a 4-slot pool."""
-    cfg = gen.CONFIGS[0]
+    cfg = gen.WORKLOADS["tiny"]
     s = cfg.shape
     run_decode(0, s.B, s.Hk, s.Hv, s.dk, "f32", "f32", cfg.steps, cfg.num_slots, cfg.extra["slot_map"])
 
@@ -84,7 +84,7 @@ def test_decode_full_parity(sdt, D):
 
 def test_decode_layer_f32_64_steps_sampled():
     """Full-size layer: B = 256, 16/32 heads, 128 x 128 fp32 states in a 1024-slot pool, 64 steps."""
-    cfg = gen.CONFIGS[1]
+    cfg = gen.WORKLOADS["decode_f32"]
     s = cfg.shape
     slot_map = gen.slot_permutation(1, cfg.num_slots)[:s.B]
     run_decode(1, s.B, s.Hk, s.Hv, s.dk, "f32", "bf16", cfg.steps, cfg.num_slots, slot_map,
@@ -95,7 +95,7 @@ def test_decode_layer_f32_64_steps_sampled():
 @pytest.mark.parametrize("B", [1, 64, 256, 512])
 def test_decode_layer_lowp_sampled(sdt, B):
     """bf16 / fp16 states, FP32 math, one rounding per step, B in {1, 64, 256, 512}."""
-    cfg = gen.CONFIGS[2]
+    cfg = gen.WORKLOADS["decode_lowp"]
     s = cfg.shape
     slot_map = gen.slot_permutation(2, cfg.num_slots)[:B]
     sample = sorted({0, B // 3, B - 1})

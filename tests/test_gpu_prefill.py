@@ -165,7 +165,7 @@ def test_prefill_wide_heads_16bit_states_with_padding(sdt):
 def test_prefill_workload_sampled(sdt):
     """Full-size workload: 4 packed sequences of 1024, 3000, 8192, 8192 tokens, 16 key / 32 value
     heads, 128 x 128 states read from slots; sampled (sequence, head) pairs against the oracle."""
-    cfg = gen.CONFIGS[3]
+    cfg = gen.WORKLOADS["prefill"]
     s = cfg.shape
     lengths = cfg.extra["lengths"]
     sample = [(0, 0), (1, 31), (2, 17), (3, 6)]

@@ -220,7 +220,7 @@ def test_replay_L1_matches_decode_on_gpu():
 
 def test_replay_layer_f32_sampled_over_a_fold():
     """Full-size layer: B = 512, 128 x 128 fp32 checkpoints, L = 16, 20 steps (fold at 17)."""
-    cfg = gen.CONFIGS[4]
+    cfg = gen.WORKLOADS["replay"]
     s = cfg.shape
     c = ReplayCase(4, s.B, s.Hk, s.Hv, s.dk, cfg.extra["L"], "f32", cfg.num_slots, sample=[0, 211, 511])
     for step in range(20):
@@ -231,7 +231,7 @@ def test_replay_layer_f32_sampled_over_a_fold():
 
 def test_replay_layer_bf16_spec_sampled():
     """Full-size layer, bf16 checkpoints, verify windows of T = 5 with rollback of 0..4 tokens."""
-    cfg = gen.CONFIGS[4]
+    cfg = gen.WORKLOADS["replay"]
     s = cfg.shape
     c = ReplayCase(41, s.B, s.Hk, s.Hv, s.dk, cfg.extra["L"], "bf16", cfg.num_slots, sample=[3, 300])
     T = cfg.extra["T_spec"]

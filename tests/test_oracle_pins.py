@@ -76,7 +76,7 @@ def _brute_force(S0, q, k, v, g, beta, scale):
 
 def test_brute_force_tiny_config():
     """The token loop equals the unrolled product form on the tiny workload."""
-    cfg = gen.CONFIGS[0]
+    cfg = gen.WORKLOADS["tiny"]
     sh = cfg.shape
     A_log, dt_bias = gen.head_params(0, sh.Hv)
     pool = gen.pool_slots(0, range(cfg.num_slots), sh.Hv, sh.dk, sh.dv, "f32")
@@ -102,7 +102,7 @@ def test_brute_force_tiny_config():
 
 def test_decode_driver_matches_brute_force_over_steps():
     """Eight decode steps through slots (f32 pool) track the unrolled form within f32 rounding."""
-    cfg = gen.CONFIGS[0]
+    cfg = gen.WORKLOADS["tiny"]
     sh = cfg.shape
     A_log, dt_bias = gen.head_params(0, sh.Hv)
     pool0 = gen.pool_slots(0, range(cfg.num_slots), sh.Hv, sh.dk, sh.dv, "f32")

@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "DTYPES", "TID", "rng", "store", "to_torch", "from_torch", "head_params",
     "token_inputs", "pool_slots", "slot_permutation", "seq_lengths_cu",
-    "rejected_counts", "split_lengths", "DecodeShape", "CONFIGS", "m2_params", "m2_inputs", "M2_LAYER",
+    "rejected_counts", "split_lengths", "DecodeShape", "CONFIGS", "WORKLOADS", "m2_params", "m2_inputs", "M2_LAYER",
 ]
 
 DTYPES = ("f32", "bf16", "f16")
@@ -199,7 +199,7 @@ CONFIGS = {
     # tiny recurrence: 2 sequences, 2 heads, 16x16 state, 8 steps, fp32 everywhere
     0: Config(0, "tiny", DecodeShape(2, 2, 2, 16, 16), "f32", ("f32",), 4, steps=8,
               extra=dict(slot_map=[3, 1])),
-    # single-step decode, Qwen3.5-like layer (16 key heads, 32 value heads, 128x128)
+    # single-step decode of a hybrid-model GDN layer (16 key heads, 32 value heads, 128x128)
     1: Config(1, "decode_f32", DecodeShape(256, 16, 32, 128, 128), "bf16", ("f32",), 1024, steps=64),
     # same layer with bf16 / fp16 state at B in {1, 64, 256, 512}
     2: Config(2, "decode_lowp", DecodeShape(256, 16, 32, 128, 128), "bf16", ("bf16", "f16"), 1024,
@@ -211,3 +211,5 @@ CONFIGS = {
     4: Config(4, "replay", DecodeShape(512, 16, 32, 128, 128), "bf16", ("f32", "bf16"), 1024,
               extra=dict(L=16, T_spec=5)),
 }
+# the same workloads by name
+WORKLOADS = {c.name: c for c in CONFIGS.values()}
