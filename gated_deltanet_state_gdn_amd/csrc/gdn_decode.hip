@@ -21,8 +21,10 @@
 #include "gdn_launch.h"
 
 // Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles,
-// 2 for 16-bit ones, which then carry as many bytes per lane), and streaming
-// (non-temporal) state access (+7% for fp32 tiles, no gain for 16-bit ones).
+// 2 for 16-bit ones, which then carry as many bytes per lane); fp32 tiles are
+// read and written non-temporally (+7%), 16-bit ones written normally (NT
+// stores measured -1 to -5%) and read non-temporally only when the launch's
+// tiles exceed the Infinity Cache (stream_tile_reads).
 #ifndef GDN_DECODE_WAVES
 #define GDN_DECODE_WAVES 4
 #endif
@@ -41,7 +43,8 @@ namespace gdn {
 template <int SDT, int D>
 using DecodeGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_DECODE_WAVES : GDN_DECODE_WAVES_16>;
 
-template <int SDT, int D, bool NT>
+// NT: non-temporal stores (and loads); NTL: non-temporal loads
+template <int SDT, int D, bool NT, bool NTL>
 __global__ void __launch_bounds__((DecodeGeom<SDT, D>::NW * 64))
 gdn_decode_kernel(const DecodeArgs p) {
   using G = DecodeGeom<SDT, D>;
@@ -72,7 +75,7 @@ gdn_decode_kernel(const DecodeArgs p) {
 
   typename IO::Raw raw[PASSES];
 #pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
+  for (int pp = 0; pp < PASSES; ++pp) raw[pp] = TileIO<SDT, VEC, NT || NTL>::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
 
   // gates (uniform over the workgroup)
   const float g = gate_g(load_elem(p.a, row_bh, p.in_dt), p.A_log[h], p.dt_bias[h]);
@@ -165,7 +168,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   using G = DecodeGeom<SDT, D>;
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hv);
   constexpr bool NT = (SDT == GDN_F32) ? (GDN_DECODE_NT_F32 != 0) : (GDN_DECODE_NT_16 != 0);
-  hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT>), dim3(grid), dim3(G::NW * 64), 0, s, a);
+  if (stream_tile_reads((long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T)))
+    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, false>), dim3(grid), dim3(G::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
+// fp32 tiles are read and written non-temporally; 16-bit source tiles are
+// read non-temporally when the launch's tiles exceed the Infinity Cache
 #ifndef GDN_SPEC_NT_F32
 #define GDN_SPEC_NT_F32 1
 #endif
@@ -31,7 +33,7 @@ using SpecGeom = TileGeom<SDT, D, 4>;
 // Dynamic LDS (floats): k, q, v [T][D] each, then alpha, beta, k.q [T] each.
 size_t spec_lds_bytes(int D, int T) { return ((size_t)3 * T * D + 3 * (size_t)T) * sizeof(float); }
 
-template <int SDT, int D, bool NT>
+template <int SDT, int D, bool NT, bool NTL>
 __global__ void __launch_bounds__((SpecGeom<SDT, D>::NW * 64)) gdn_spec_kernel(const SpecArgs P) {
   using G = SpecGeom<SDT, D>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
@@ -64,7 +66,7 @@ __global__ void __launch_bounds__((SpecGeom<SDT, D>::NW * 64)) gdn_spec_kernel(c
   {
     typename IO::Raw raw[PASSES];
 #pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(stile + (r0 + pp * NW * RPW) * D + c0);
+    for (int pp = 0; pp < PASSES; ++pp) raw[pp] = TileIO<SDT, VEC, NT || NTL>::load_raw(stile + (r0 + pp * NW * RPW) * D + c0);
 #pragma unroll
     for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
   }
@@ -162,7 +164,10 @@ static hipError_t launch_spec_t(const SpecArgs& a, hipStream_t s) {
   using G = SpecGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_SPEC_NT_F32 != 0);
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
-  hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, NT>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);
+  if (stream_tile_reads((long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T)))
+    hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, NT, true>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);
+  else
+    hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, NT, false>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);
   return hipGetLastError();
 }
 
