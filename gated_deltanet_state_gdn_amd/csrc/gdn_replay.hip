@@ -431,7 +431,7 @@ __host__ __device__ inline size_t replay_fold_mfma_lds_bytes(int D) {
 }
 
 template <int SDT, int D, bool NT, int EB, int CDT>
-__global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
+__global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
   static_assert(D == 64 || D == 128, "four waves of 16-column blocks");
   constexpr int NI = D / 16;  // row blocks
   constexpr int NJ = D / 64;  // column blocks per wave
@@ -582,10 +582,12 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
         // X = M^-1 by forward substitution (lane c < 16 owns column c), then
         // the factor X diag(beta) replaces M in place
         if (lane < 16) {
+          int cz = c;  // opaque: keeps the 16 identity entries from being held across units
+          asm volatile("" : "+v"(cz));
           float xc[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float v = i == c ? 1.f : 0.f;
+            float v = i == cz ? 1.f : 0.f;
 #pragma unroll
             for (int k = 0; k < i; ++k) v = fmaf(-s_m[i * 17 + k], xc[k], v);
             xc[i] = v;
