@@ -22,9 +22,9 @@
 
 // Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles,
 // 2 for 16-bit ones, which then carry as many bytes per lane); fp32 tiles are
-// read and written non-temporally (+7%), 16-bit ones written normally (NT
-// stores measured -1 to -5%) and read non-temporally only when the launch's
-// tiles exceed the Infinity Cache (stream_tile_reads).
+// read and written non-temporally (+7%), 16-bit ones read non-temporally when
+// the launch's tiles exceed the Infinity Cache (stream_tile_reads) and also
+// written so past twice that (stream_tile_writes).
 #ifndef GDN_DECODE_WAVES
 #define GDN_DECODE_WAVES 4
 #endif
@@ -168,7 +168,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   using G = DecodeGeom<SDT, D>;
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hv);
   constexpr bool NT = (SDT == GDN_F32) ? (GDN_DECODE_NT_F32 != 0) : (GDN_DECODE_NT_16 != 0);
-  if (stream_tile_reads((long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T)))
+  const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
+  if (!NT && stream_tile_writes(tile_bytes))
+    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, true, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
+  else if (stream_tile_reads(tile_bytes))
     hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, false>), dim3(grid), dim3(G::NW * 64), 0, s, a);

@@ -229,6 +229,11 @@ struct RowStager {
 // decode at 67 MB lost 15% to non-temporal reads).
 constexpr long long kCacheResidentBytes = 192ll << 20;
 inline bool stream_tile_reads(long long bytes) { return bytes > kCacheResidentBytes; }
+// 16-bit tiles are also written non-temporally once one launch writes more
+// than twice that (bf16 and f16 decode at 537 MB: +3%; a 5-token window of
+// 16-bit destination states, 1.3 GB: +5 to +8%); at 268 MB such stores cost
+// 1 to 5%.  fp32 tiles are always streamed.
+inline bool stream_tile_writes(long long bytes) { return bytes > 2 * kCacheResidentBytes; }
 
 // ------------------------------------------------------------------ wave64 reductions
 template <int CTRL>

@@ -18,7 +18,8 @@
 #include "gdn_launch.h"
 
 // fp32 tiles are read and written non-temporally; 16-bit source tiles are
-// read non-temporally when the launch's tiles exceed the Infinity Cache
+// read non-temporally when the launch's tiles exceed the Infinity Cache, and
+// 16-bit tiles are written so when the T destinations exceed twice that
 #ifndef GDN_SPEC_NT_F32
 #define GDN_SPEC_NT_F32 1
 #endif
@@ -164,7 +165,10 @@ static hipError_t launch_spec_t(const SpecArgs& a, hipStream_t s) {
   using G = SpecGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_SPEC_NT_F32 != 0);
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
-  if (stream_tile_reads((long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T)))
+  const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
+  if (!NT && stream_tile_writes(tile_bytes * a.T))  // the T destination tiles
+    hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, true, true>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);
+  else if (stream_tile_reads(tile_bytes))
     hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, NT, true>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);
   else
     hipLaunchKernelGGL((gdn_spec_kernel<SDT, D, NT, false>), dim3(grid), dim3(G::NW * 64), spec_lds_bytes(D, a.T), s, a);

@@ -136,9 +136,11 @@ def test_spec_long_window_bf16_out():
     run_spec(B, T, 1, 2, 64, "bf16", "bf16", num_slots, src, dst, out_dt="bf16", a_shift=-4.0)
 
 
-def test_spec_full_size_sampled():
-    """512 sequences, 16 key / 32 value heads, 128 x 128 fp32 states, 5 positions: 3072 slots."""
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_spec_full_size_sampled(sdt):
+    """512 sequences, 16 key / 32 value heads, 128 x 128 states, 5 positions: 3072 slots.  With
+    bf16 states the 2.7 GB of destination tiles take the non-temporal store path."""
     B, T = 512, 5
     num_slots = B * (T + 1)
     src, dst = _layout(B, T, num_slots, 23)
-    run_spec(B, T, 16, 32, 128, "f32", "bf16", num_slots, src, dst, sample=[0, 137, 511])
+    run_spec(B, T, 16, 32, 128, sdt, "bf16", num_slots, src, dst, sample=[0, 137, 511])
