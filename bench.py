@@ -199,7 +199,7 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None):
     steps_per_cycle = L // T if T > 1 else L
     slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
     ckpt = make_pool(torch, gen, cid, slot_map, sdt, dev)
-    ring = gdn.new_ring(NUM_SLOTS, HV, L, D, D, torch.bfloat16, dev)
+    ring = gdn.new_ring(NUM_SLOTS, HK, HV, L, D, D, torch.bfloat16, dev)
     copy = None
     if copy_dt is not None:
         copy = torch.empty((NUM_SLOTS, HV, D, D), dtype={"bf16": torch.bfloat16, "f16": torch.float16}[copy_dt],

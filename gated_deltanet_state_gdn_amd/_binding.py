@@ -163,8 +163,8 @@ def _pool(pool):
 
 @dataclass
 class Ring:
-    """Per (slot, value head) ring of ReplaySSM inputs (layout of gdn_ring)."""
-    k: object      # [num_slots, Hv, L, dk]
+    """Per (slot, value head) ring of ReplaySSM inputs (layout of gdn_ring; keys once per key head)."""
+    k: object      # [num_slots, Hk, L, dk]
     v: object      # [num_slots, Hv, L, dv]
     g: object      # [num_slots, Hv, L] float32
     beta: object   # [num_slots, Hv, L] float32
@@ -180,10 +180,10 @@ class Ring:
                         _ptr(self.count), int(self.g.shape[0]), self.L, dtype_code(self.k.dtype))
 
 
-def new_ring(num_slots, Hv, L, dk, dv, dtype, device) -> Ring:
+def new_ring(num_slots, Hk, Hv, L, dk, dv, dtype, device) -> Ring:
     torch = _torch()
     z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
-    return Ring(k=z((num_slots, Hv, L, dk), dtype), v=z((num_slots, Hv, L, dv), dtype),
+    return Ring(k=z((num_slots, Hk, L, dk), dtype), v=z((num_slots, Hv, L, dv), dtype),
                 g=z((num_slots, Hv, L), torch.float32), beta=z((num_slots, Hv, L), torch.float32),
                 start=z((num_slots, Hv), torch.int32), count=z((num_slots, Hv), torch.int32))
 

@@ -80,6 +80,16 @@ __device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t unit) {
   return RingPos{st, cnt};
 }
 
+// ---------------------------------------------------------------- ring keys
+// Ring keys are stored once per key head: the value heads of a key head share
+// its entries (their ring pointers always advance together), and the first of
+// them appends the keys of a window.  First key row of the ring entries of
+// value head h of `slot`:
+__device__ __forceinline__ int64_t ring_key_base(const DecodeArgs& p, int64_t slot, int h, int L) {
+  return (slot * p.Hk + h / (p.Hv / p.Hk)) * L;
+}
+__device__ __forceinline__ bool appends_keys(const DecodeArgs& p, int h) { return h % (p.Hv / p.Hk) == 0; }
+
 // ---------------------------------------------------------------- fold
 // Persistent: workgroup w owns units w, w + G, w + 2G, ... (G the grid size,
 // sized to the resident workgroups), checks 64 of them at a time, one per
@@ -161,6 +171,7 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
       for (int pp = 0; pp < PASSES; ++pp) IO::widen(IO::load_raw(tile + pp * NW * RPW * D), s[pp]);
 
       const int64_t ring_e = unit * L;
+      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
       for (int t = tid; t < cnt; t += NTH) {
         const int j = (st + t) % L;
         e_a[t] = expf(R.g[ring_e + j]);
@@ -169,8 +180,9 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
       for (int r0s = 0; r0s < cnt; r0s += kStageRows) {
         Stager sk, sv;
         auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
+        auto key_row = [&](int r) { return (kring_e + (st + r0s + r) % L) * D; };
         const int nr = min(kStageRows, cnt - r0s);
-        sk.issue(R.k, nr, ring_row);
+        sk.issue(R.k, nr, key_row);
         sv.issue(R.v, nr, ring_row);
         sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
         sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
@@ -310,6 +322,7 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
       for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + pp * RS * D);
 
       const int64_t ring_e = unit * L;
+      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
       for (int t = tid; t < cnt; t += NTH) {
         const int j = (st + t) % L;
         e_a[t] = expf(R.g[ring_e + j]);
@@ -317,8 +330,8 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
       }
       for (int q = tid; q < cnt * CPR; q += NTH) {  // keys (permuted) and values, widened
         const int t = q / CPR, cc = (q - t * CPR) * VE;
-        const int64_t row = (ring_e + (st + t) % L) * D + cc;
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + row * EB);
+        const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
         const u32x4 vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
@@ -519,12 +532,13 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
 
       // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
       const int64_t ring_e = unit * L;
+      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
       for (int q = tid; q < 16 * CPR; q += NTH) {
         const int t = q / CPR, cc = (q - t * CPR) * VE;
         u32x4 kw = {0u, 0u, 0u, 0u}, vw = kw;
         if (t < cnt) {
-          const int64_t row = (ring_e + (st + t) % L) * D + cc;
-          kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + row * EB);
+          const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
+          kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
           vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
         }
 #pragma unroll
@@ -790,7 +804,8 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   const int st = rp.st;
   const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
   const int n_all = cnt + T;           // <= L
-  const char* rk = static_cast<const char*>(R.k) + ring_e * D * EB;
+  const int64_t kring_e = ring_key_base(p, slot, h, L);
+  const char* rk = static_cast<const char*>(R.k) + kring_e * D * EB;
   const char* rv = static_cast<const char*>(R.v) + ring_e * D * EB;
   auto live_src_k = [&](int i) { return rk + (int64_t)((st + i) % L) * D * EB; };
   auto live_src_v = [&](int i) { return rv + (int64_t)((st + i) % L) * D * EB; };
@@ -860,11 +875,11 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   const int base = (st + cnt) % L;
   for (int x = tid; x < T * CPR; x += NTH) {
     const int t = x / CPR, c = (x - t * CPR) * VE;
-    const int64_t j = ring_e + (base + t) % L;
+    const int64_t j = ring_e + (base + t) % L, kj = kring_e + (base + t) % L;
     const int64_t ko = ((((int64_t)b * T + t) * p.Hk + hk) * D + c) * EB;
     const int64_t vo = ((((int64_t)b * T + t) * p.Hv + h) * D + c) * EB;
-    *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (j * D + c) * EB) =
-        *reinterpret_cast<const u32x4*>(kin + ko);
+    if (appends_keys(p, h))
+      *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (kj * D + c) * EB) = *reinterpret_cast<const u32x4*>(kin + ko);
     *reinterpret_cast<u32x4*>(static_cast<char*>(R.v) + (j * D + c) * EB) =
         *reinterpret_cast<const u32x4*>(vin + vo);
   }
@@ -1042,8 +1057,8 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   // columns: row j is one load over the wave.
   const bool live = e < n_all, committed = e < cnt;
   const int tw = committed ? 0 : min(e - cnt, T - 1);
-  const int64_t rj = unit * L + (st + e) % L;
-  const char* ks = committed ? static_cast<const char*>(R.k) + rj * RB
+  const int64_t rj = unit * L + (st + e) % L, krj = ring_key_base(p, slot, h, L) + (st + e) % L;
+  const char* ks = committed ? static_cast<const char*>(R.k) + krj * RB
                              : static_cast<const char*>(p.k) + (((int64_t)b * T + tw) * p.Hk + hk) * RB;
   u32x4 kx[NS];
 #pragma unroll
@@ -1083,9 +1098,11 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
 #pragma unroll
   for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(s_k + e * D + 8 * (NS * g + s)) = kx[s];
   if (live && !committed) {
-    char* kd = static_cast<char*>(R.k) + rj * RB + coff;
+    if (appends_keys(p, h)) {
+      char* kd = static_cast<char*>(R.k) + krj * RB + coff;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(kd + 16 * s) = kx[s];
+      for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(kd + 16 * s) = kx[s];
+    }
     if (g == 0) {
       R.g[rj] = gl;
       R.beta[rj] = bl;

@@ -89,15 +89,17 @@ typedef struct {
 
 /* ReplaySSM ring, one per (slot, value head), caller-allocated and separate
  * from the checkpoint pool:
- *   k    [num_slots, Hv, L, dk]  copies of the keys, in `dtype`
+ *   k    [num_slots, Hk, L, dk]  copies of the keys, in `dtype`, once per key head
  *   v    [num_slots, Hv, L, dv]  copies of the values, in `dtype`
  *   g    [num_slots, Hv, L]      float32 log-decays
  *   beta [num_slots, Hv, L]      float32 write strengths
  *   start, count [num_slots, Hv] int32; live entry i (0 <= i < count) sits at
  *                                ring index (start + i) mod L.
  * q is never stored.  Before first use, start and count must be zero (or any
- * 0 <= start < L, 0 <= count <= L).  k and v are stored per value head so
- * that each (slot, value head) unit owns its ring entries outright. */
+ * 0 <= start < L, 0 <= count <= L, equal over the value heads of each key
+ * head).  The value heads of a key head share its key entries: the entry
+ * points advance their pointers together (every head of a row takes the same
+ * window, fold and rollback), and the first of them appends the keys. */
 typedef struct {
   void* k;
   void* v;

@@ -33,8 +33,8 @@ class ReplayCase:
         self.num_slots, self.in_dt = num_slots, in_dt
         self.slot_map = gen.slot_permutation(cid, num_slots)[:B]
         self.ckpt_d, states = poisoned_pool(num_slots, Hv, D, D, sdt, [int(s) for s in self.slot_map], cid)
-        self.ring_d = gdn.new_ring(num_slots, Hv, L, D, D, {"bf16": torch.bfloat16, "f32": torch.float32,
-                                                           "f16": torch.float16}[in_dt], DEV)
+        self.ring_d = gdn.new_ring(num_slots, Hk, Hv, L, D, D, {"bf16": torch.bfloat16, "f32": torch.float32,
+                                                               "f16": torch.float16}[in_dt], DEV)
         self.rows = list(range(B)) if sample is None else list(sample)
         # oracle: mini pool / ring over the sampled rows' slots, local slot i = sample row i
         self.ref_ckpt = states[self.rows]
@@ -111,7 +111,9 @@ class ReplayCase:
                 live = [(int(st[i, h]) + e) % L for e in range(int(cnt[i, h]))]
                 if not live:
                     continue
-                assert np.array_equal(rk[i, h, live], self.ref_ring.k[i, h, live]), f"{what}: ring k"
+                # keys are kept once per key head (the oracle keeps them per value head)
+                assert np.array_equal(rk[i, h // (self.Hv // self.Hk), live], self.ref_ring.k[i, h, live]), \
+                    f"{what}: ring k"
                 assert np.array_equal(rv[i, h, live], self.ref_ring.v[i, h, live]), f"{what}: ring v"
                 np.testing.assert_allclose(rg[i, h, live], self.ref_ring.g[i, h, live], rtol=1e-5, atol=1e-8)
                 np.testing.assert_allclose(rb[i, h, live], self.ref_ring.beta[i, h, live], rtol=1e-5, atol=1e-8)
