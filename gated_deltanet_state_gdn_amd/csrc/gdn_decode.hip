@@ -37,6 +37,10 @@
 #ifndef GDN_DECODE_NT_16
 #define GDN_DECODE_NT_16 0
 #endif
+// fp32 128 x 128 tiles go through the persistent 16-wave kernel
+#ifndef GDN_DECODE_PERSIST
+#define GDN_DECODE_PERSIST 1
+#endif
 
 namespace gdn {
 
@@ -163,11 +167,207 @@ gdn_decode_kernel(const DecodeArgs p) {
   }
 }
 
+// Persistent decode for fp32 128 x 128 states.  One workgroup of 16 waves
+// per compute unit walks the tiles t = blockIdx.x + i G; the loads of the next
+// tile (its state rows, the key and query elements of this lane's rows, the
+// values of its columns and the gate inputs) are in flight while the current
+// tile is reduced, updated and written back, and slot indices are fetched two
+// tiles ahead so no load waits on another.  Lane l of wave w holds columns
+// 4 (l mod 32) .. +3 of rows 2 w + l / 32 + 32 pp (pp < 4).  Column sums of
+// S^T k and S^T q go through LDS in two levels (double-buffered by tile
+// parity, two barriers per tile).  Copies with this shape (64 KiB per
+// 16-wave workgroup, next loads issued before the current stores) run at
+// 5.95 TB/s on MI355X against 5.26 for one-shot 4-wave workgroups; the
+// decode went from 5.25 to 5.70-5.76 TB/s at B = 256 and from 5.40 to 5.93
+// at B = 512.
+constexpr int kPersistNW = 16;
+constexpr int kPersistMaxIter = 512;  // tiles per workgroup whose slot and head scalars sit in LDS
+
+template <bool NT, int IDT>
+__global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(const DecodeArgs p) {
+  constexpr int D = 128, NW = kPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
+  static_assert(PASSES == 4, "four rows per lane");
+  using IO = TileIO<GDN_F32, VEC, NT>;
+  typedef typename IO::Raw Raw;
+  typedef typename std::conditional<IDT == GDN_F32, uint32_t, uint16_t>::type IT;  // input element bits
+
+  __shared__ __attribute__((aligned(16))) float s_red[2][2][NW][D];  // [parity][S^T k | S^T q][wave][column]
+  __shared__ __attribute__((aligned(16))) float s_sum[2][2][D];      // [parity][S^T k | S^T q][column]
+  __shared__ __attribute__((aligned(16))) float s_kqw[2][NW];        // [parity][wave] partial k . q
+  __shared__ int s_slot[kPersistMaxIter];                            // per tile of this workgroup:
+  __shared__ float s_al[kPersistMaxIter], s_db[kPersistMaxIter];     // slot, A_log and dt_bias of its head
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = (lane % LPR) * VEC, r0 = wave * RPW + lane / LPR;
+  const int units = p.B * p.Hv, G = gridDim.x;
+  int t = blockIdx.x;
+  if (t >= units) return;
+  // The scalars of every tile this workgroup visits go to LDS first (one wait
+  // here), so no load inside the loop waits behind the tile traffic.
+  const int n_iter = (units - t + G - 1) / G;  // <= kPersistMaxIter (launcher)
+  for (int i = tid; i < n_iter; i += NW * 64) {
+    const int u = t + i * G, hh = u % p.Hv;
+    s_slot[i] = p.slot_map[u / p.Hv];
+    s_al[i] = p.A_log[hh];
+    s_db[i] = p.dt_bias[hh];
+  }
+  __syncthreads();
+
+  // Loads of a tile in flight behind the current one keep their raw bits and
+  // are widened only when the tile becomes current, so nothing waits on them
+  // early; the per-element input index is made opaque so that the uniform ones
+  // (gates) go through vector loads, which complete in order with the tile.
+  int zl = 0;
+  asm volatile("" : "+v"(zl));
+  const IT* kin = static_cast<const IT*>(p.k);
+  const IT* qin = static_cast<const IT*>(p.q);
+  const IT* vin = static_cast<const IT*>(p.v);
+  const IT* ain = static_cast<const IT*>(p.a);
+  const IT* bin = static_cast<const IT*>(p.b);
+  auto widen = [](uint32_t x) -> float {
+    if constexpr (IDT == GDN_F32) return __uint_as_float(x);
+    else if constexpr (IDT == GDN_BF16) return bf16_bits_to_f32(x);
+    else return f16_bits_to_f32(x);
+  };
+  auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
+  // the values of this lane's columns, packed as loaded (VEC inputs in one access)
+  typedef unsigned int VRaw __attribute__((ext_vector_type(VEC * sizeof(IT) / 4)));
+  struct In {
+    Raw raw[PASSES];
+    VRaw vv;
+    uint32_t kr[PASSES], qr[PASSES], ga, gb;
+  };
+  // Every load is issued unconditionally (a branch around them would make the
+  // compiler wait for all loads in flight where the paths join): a padded row's
+  // tile goes through a zero-size buffer, whose reads return zeros and touch no
+  // memory.
+  auto fetch = [&](int u, int slot, In& x) {
+    const int b = u / p.Hv, h = u - b * p.Hv, hk = h / (p.Hv / p.Hk);
+    const int64_t row_bh = (int64_t)b * p.Hv + h, kq_base = ((int64_t)b * p.Hk + hk) * D;
+    const bool ok = valid(slot);
+    const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tile), 0, ok ? D * D * 4 : 0, 0x00020000);
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp)
+      x.raw[pp] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, (r0 * D + c0) * 4,
+                                                                                 pp * NW * RPW * D * 4, NT ? 2 : 0));
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) {
+      x.kr[pp] = kin[kq_base + r0 + pp * NW * RPW];
+      x.qr[pp] = qin[kq_base + r0 + pp * NW * RPW];
+    }
+    x.vv = *reinterpret_cast<const VRaw*>(vin + row_bh * D + c0);
+    x.ga = ain[row_bh + zl];
+    x.gb = bin[row_bh + zl];
+  };
+
+  In cur, nxt;
+  fetch(t, s_slot[0], cur);
+  for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
+    const int tn = t + G;
+    // past the last tile the loads repeat this tile's inputs, with no state
+    fetch(tn < units ? tn : t, tn < units ? s_slot[it + 1] : -1, nxt);
+    const int slot_c = s_slot[it];
+
+    const int b = t / p.Hv, h = t - b * p.Hv;
+    const int64_t row_bh = (int64_t)b * p.Hv + h;
+    if (!valid(slot_c)) {  // padded row: zero output, no state access (uniform over the workgroup)
+      if (tid < D) store_elem(p.out, row_bh * D + tid, 0.f, p.out_dt);
+    } else {
+      const float g = gate_g(widen(cur.ga), s_al[it], s_db[it]);
+      const float beta = sigmoid_f(widen(cur.gb));
+      const float alpha = expf(g);
+      float kr[PASSES], kvp[VEC], qsp[VEC], kqp = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) kvp[e] = qsp[e] = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) {
+        kr[pp] = widen(cur.kr[pp]);
+        const float qr = widen(cur.qr[pp]);
+        float sv[VEC];
+        IO::widen(cur.raw[pp], sv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          kvp[e] = fmaf(sv[e], kr[pp], kvp[e]);
+          qsp[e] = fmaf(sv[e], qr, qsp[e]);
+        }
+        kqp = fmaf(kr[pp], qr, kqp);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        kvp[e] = xor_sum_from<LPR>(kvp[e]);
+        qsp[e] = xor_sum_from<LPR>(qsp[e]);
+      }
+      // this wave's rows: lanes 0-31 hold rows 2 w + 32 pp, lanes 32-63 rows 2 w + 1 + 32 pp
+      // (summed with every lane active: a cross-lane read inside the lane-0 branch
+      // would see an operand the compiler computed for lane 0 only)
+      kqp = xor_sum_from<LPR>(kqp);
+      if (lane < LPR) {
+        *reinterpret_cast<f32x4*>(&s_red[par][0][wave][c0]) = f32x4{kvp[0], kvp[1], kvp[2], kvp[3]};
+        *reinterpret_cast<f32x4*>(&s_red[par][1][wave][c0]) = f32x4{qsp[0], qsp[1], qsp[2], qsp[3]};
+      }
+      if (lane == 0) s_kqw[par][wave] = kqp;
+      __syncthreads();
+      if (tid < 2 * D) {  // one (kind, column) per thread
+        const int kind = tid / D, col = tid - kind * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += s_red[par][kind][w][col];
+        s_sum[par][kind][col] = acc;
+      }
+      __syncthreads();
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(&s_sum[par][0][c0]);
+      const f32x4 qs = *reinterpret_cast<const f32x4*>(&s_sum[par][1][c0]);
+      float kq = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) kq += s_kqw[par][w];
+      float delta[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float ve;
+        if constexpr (IDT == GDN_F32) ve = __uint_as_float(cur.vv[e]);
+        else ve = widen((e & 1) ? (cur.vv[e >> 1] >> 16) : (cur.vv[e >> 1] & 0xffffu));
+        delta[e] = beta * (ve - alpha * kv[e]);
+        if (wave == 0 && lane < LPR)
+          store_elem(p.out, row_bh * D + c0 + e, p.scale * fmaf(alpha, qs[e], kq * delta[e]), p.out_dt);
+      }
+      float* tile = static_cast<float*>(p.pool) + ((int64_t)slot_c * p.Hv + h) * (int64_t)(D * D);
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) {
+        float sv[VEC];
+        IO::widen(cur.raw[pp], sv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sv[e] = fmaf(alpha, sv[e], kr[pp] * delta[e]);
+        IO::store(tile + (r0 + pp * NW * RPW) * D + c0, sv);
+      }
+    }
+    cur = nxt;
+  }
+}
+
 template <int SDT, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   using G = DecodeGeom<SDT, D>;
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hv);
   constexpr bool NT = (SDT == GDN_F32) ? (GDN_DECODE_NT_F32 != 0) : (GDN_DECODE_NT_16 != 0);
+  if constexpr (SDT == GDN_F32 && D == 128 && GDN_DECODE_PERSIST != 0) {
+    void (*kern)(const DecodeArgs) = a.in_dt == GDN_F32    ? &gdn_decode_persist_kernel<NT, GDN_F32>
+                                     : a.in_dt == GDN_BF16 ? &gdn_decode_persist_kernel<NT, GDN_BF16>
+                                                           : &gdn_decode_persist_kernel<NT, GDN_F16>;
+    int per_cu = 0, cus = 0;
+    hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), kPersistNW * 64, 0, &per_cu);
+    if (e == hipSuccess) e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+    const unsigned pgrid = (unsigned)((int64_t)grid < fill ? (int64_t)grid : fill);
+    // with 8 or fewer tiles per workgroup the pipeline has too little to overlap
+    // (B = 64: 5.06-5.25 TB/s against 5.28-5.30 for the one-shot kernel)
+    if ((int64_t)grid > 8 * (int64_t)pgrid && (int64_t)grid <= (int64_t)pgrid * kPersistMaxIter) {
+      hipLaunchKernelGGL(kern, dim3(pgrid), dim3(kPersistNW * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
   if (!NT && stream_tile_writes(tile_bytes))
     hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, true, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
