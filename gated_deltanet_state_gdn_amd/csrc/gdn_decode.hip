@@ -172,8 +172,9 @@ gdn_decode_kernel(const DecodeArgs p) {
 // tile (its state rows, the key and query elements of this lane's rows, the
 // values of its columns and the gate inputs) are in flight while the current
 // tile is reduced, updated and written back, and slot indices are fetched two
-// tiles ahead so no load waits on another.  Lane l of wave w holds columns
-// 4 (l mod 32) .. +3 of rows 2 w + l / 32 + 32 pp (pp < 4).  Column sums of
+// tiles ahead so no load waits on another.  Lane l of wave w holds VEC = 4
+// (fp32) or 8 (16-bit) columns from VEC (l mod LPR) of rows RPW w + l / LPR
+// + 16 RPW pp (LPR = 128 / VEC lanes per row, RPW = 64 / LPR rows per wave).  Column sums of
 // S^T k and S^T q go through LDS in two levels (double-buffered by tile
 // parity, two barriers per tile).  Copies with this shape (64 KiB per
 // 16-wave workgroup, next loads issued before the current stores) run at
@@ -183,12 +184,17 @@ gdn_decode_kernel(const DecodeArgs p) {
 constexpr int kPersistNW = 16;
 constexpr int kPersistMaxIter = 512;  // tiles per workgroup whose slot and head scalars sit in LDS
 
-template <bool NT, int IDT>
+// NTL / NTS: non-temporal tile loads / stores.
+template <int SDT, bool NTL, bool NTS, int IDT>
 __global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(const DecodeArgs p) {
-  constexpr int D = 128, NW = kPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
-  static_assert(PASSES == 4, "four rows per lane");
-  using IO = TileIO<GDN_F32, VEC, NT>;
+  // 16-byte accesses: 4 fp32 or 8 16-bit columns per lane
+  constexpr int D = 128, NW = kPersistNW, VEC = SDT == GDN_F32 ? 4 : 8, LPR = D / VEC, RPW = 64 / LPR;
+  constexpr int PASSES = D / (RPW * NW);
+  static_assert(PASSES * RPW * NW == D, "whole rows per pass");
+  using IO = TileIO<SDT, VEC, NTS>;
   typedef typename IO::Raw Raw;
+  static_assert(sizeof(Raw) == 16, "16-byte tile accesses");
+  using ST = typename StateElem<SDT>::T;
   typedef typename std::conditional<IDT == GDN_F32, uint32_t, uint16_t>::type IT;  // input element bits
 
   __shared__ __attribute__((aligned(16))) float s_red[2][2][NW][D];  // [parity][S^T k | S^T q][wave][column]
@@ -245,13 +251,14 @@ __global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(
     const int b = u / p.Hv, h = u - b * p.Hv, hk = h / (p.Hv / p.Hk);
     const int64_t row_bh = (int64_t)b * p.Hv + h, kq_base = ((int64_t)b * p.Hk + hk) * D;
     const bool ok = valid(slot);
-    const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tile), 0, ok ? D * D * 4 : 0, 0x00020000);
+    const ST* tile = static_cast<const ST*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<ST*>(tile), 0, ok ? D * D * (int)sizeof(ST) : 0, 0x00020000);
 #pragma unroll
     for (int pp = 0; pp < PASSES; ++pp)
-      x.raw[pp] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, (r0 * D + c0) * 4,
-                                                                                 pp * NW * RPW * D * 4, NT ? 2 : 0));
+      x.raw[pp] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rs, (r0 * D + c0) * (int)sizeof(ST),
+                                              pp * NW * RPW * D * (int)sizeof(ST), NTL ? 2 : 0));
 #pragma unroll
     for (int pp = 0; pp < PASSES; ++pp) {
       x.kr[pp] = kin[kq_base + r0 + pp * NW * RPW];
@@ -299,13 +306,16 @@ __global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(
         kvp[e] = xor_sum_from<LPR>(kvp[e]);
         qsp[e] = xor_sum_from<LPR>(qsp[e]);
       }
-      // this wave's rows: lanes 0-31 hold rows 2 w + 32 pp, lanes 32-63 rows 2 w + 1 + 32 pp
+      // this wave's rows: lane group l / LPR holds rows RPW w + l / LPR + 16 RPW pp
       // (summed with every lane active: a cross-lane read inside the lane-0 branch
       // would see an operand the compiler computed for lane 0 only)
       kqp = xor_sum_from<LPR>(kqp);
       if (lane < LPR) {
-        *reinterpret_cast<f32x4*>(&s_red[par][0][wave][c0]) = f32x4{kvp[0], kvp[1], kvp[2], kvp[3]};
-        *reinterpret_cast<f32x4*>(&s_red[par][1][wave][c0]) = f32x4{qsp[0], qsp[1], qsp[2], qsp[3]};
+#pragma unroll
+        for (int e4 = 0; e4 < VEC; e4 += 4) {
+          *reinterpret_cast<f32x4*>(&s_red[par][0][wave][c0 + e4]) = f32x4{kvp[e4], kvp[e4 + 1], kvp[e4 + 2], kvp[e4 + 3]};
+          *reinterpret_cast<f32x4*>(&s_red[par][1][wave][c0 + e4]) = f32x4{qsp[e4], qsp[e4 + 1], qsp[e4 + 2], qsp[e4 + 3]};
+        }
       }
       if (lane == 0) s_kqw[par][wave] = kqp;
       __syncthreads();
@@ -317,8 +327,17 @@ __global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(
         s_sum[par][kind][col] = acc;
       }
       __syncthreads();
-      const f32x4 kv = *reinterpret_cast<const f32x4*>(&s_sum[par][0][c0]);
-      const f32x4 qs = *reinterpret_cast<const f32x4*>(&s_sum[par][1][c0]);
+      float kv[VEC], qs[VEC];
+#pragma unroll
+      for (int e4 = 0; e4 < VEC; e4 += 4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_sum[par][0][c0 + e4]);
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&s_sum[par][1][c0 + e4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kv[e4 + j] = k4[j];
+          qs[e4 + j] = q4[j];
+        }
+      }
       float kq = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) kq += s_kqw[par][w];
@@ -332,7 +351,7 @@ __global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(
         if (wave == 0 && lane < LPR)
           store_elem(p.out, row_bh * D + c0 + e, p.scale * fmaf(alpha, qs[e], kq * delta[e]), p.out_dt);
       }
-      float* tile = static_cast<float*>(p.pool) + ((int64_t)slot_c * p.Hv + h) * (int64_t)(D * D);
+      ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot_c * p.Hv + h) * (int64_t)(D * D);
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) {
         float sv[VEC];
@@ -351,10 +370,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   using G = DecodeGeom<SDT, D>;
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hv);
   constexpr bool NT = (SDT == GDN_F32) ? (GDN_DECODE_NT_F32 != 0) : (GDN_DECODE_NT_16 != 0);
+  const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
+  // fp32 only: 16-bit tiles (32 KiB) ran at 3.66-3.83 TB/s in it against
+  // 4.62-5.14 for the one-shot two-wave kernel, which keeps eight such tiles in
+  // flight per CU where the pipeline keeps two
   if constexpr (SDT == GDN_F32 && D == 128 && GDN_DECODE_PERSIST != 0) {
-    void (*kern)(const DecodeArgs) = a.in_dt == GDN_F32    ? &gdn_decode_persist_kernel<NT, GDN_F32>
-                                     : a.in_dt == GDN_BF16 ? &gdn_decode_persist_kernel<NT, GDN_BF16>
-                                                           : &gdn_decode_persist_kernel<NT, GDN_F16>;
+    const bool ntl = NT, nts = NT;  // streamed both ways
+    void (*kern)(const DecodeArgs) = nullptr;
+    auto pick = [&](auto ntl_c, auto nts_c) {
+      constexpr bool L = decltype(ntl_c)::value, S = decltype(nts_c)::value;
+      kern = a.in_dt == GDN_F32    ? &gdn_decode_persist_kernel<SDT, L, S, GDN_F32>
+             : a.in_dt == GDN_BF16 ? &gdn_decode_persist_kernel<SDT, L, S, GDN_BF16>
+                                   : &gdn_decode_persist_kernel<SDT, L, S, GDN_F16>;
+    };
+    if (ntl && nts) pick(std::true_type{}, std::true_type{});
+    else if (ntl) pick(std::true_type{}, std::false_type{});
+    else pick(std::false_type{}, std::false_type{});
     int per_cu = 0, cus = 0;
     hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), kPersistNW * 64, 0, &per_cu);
     if (e == hipSuccess) e = device_cus(&cus);
@@ -362,13 +393,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
     const unsigned pgrid = (unsigned)((int64_t)grid < fill ? (int64_t)grid : fill);
     // with 8 or fewer tiles per workgroup the pipeline has too little to overlap
-    // (B = 64: 5.06-5.25 TB/s against 5.28-5.30 for the one-shot kernel)
+    // (fp32 at B = 64: 5.06-5.25 TB/s against 5.28-5.30 for the one-shot kernel)
     if ((int64_t)grid > 8 * (int64_t)pgrid && (int64_t)grid <= (int64_t)pgrid * kPersistMaxIter) {
       hipLaunchKernelGGL(kern, dim3(pgrid), dim3(kPersistNW * 64), 0, s, a);
       return hipGetLastError();
     }
   }
-  const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
   if (!NT && stream_tile_writes(tile_bytes))
     hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, true, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
   else if (stream_tile_reads(tile_bytes))

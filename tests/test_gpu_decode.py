@@ -118,13 +118,14 @@ def test_decode_padded_rows_and_bf16_output():
     del got
 
 
-def test_decode_wide_tiles_padded_rows_over_several_tiles_per_workgroup():
-    """fp32 128 x 128 states: 70 rows x 4 value heads = 280 tiles, more than one per workgroup of
-    the persistent kernel, with padded rows (-1 and past the pool) spread through the walk."""
-    B, num_slots = 70, 80
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_decode_persistent_walk_with_padded_rows(sdt):
+    """128 x 128 states: 80 rows x 32 value heads = 2560 tiles, about ten per workgroup of the
+    persistent kernel, with padded rows (-1 and past the pool) spread through the walk."""
+    B, num_slots = 80, 96
     slot_map = gen.slot_permutation(12, num_slots)[:B].copy()
-    slot_map[[3, 17, 40, 69]] = [-1, num_slots, -5, num_slots + 3]
-    run_decode(12, B, 2, 4, 128, "f32", "bf16", 2, num_slots, slot_map, out_dt="bf16")
+    slot_map[[3, 17, 40, 79]] = [-1, num_slots, -5, num_slots + 3]
+    run_decode(12, B, 16, 32, 128, sdt, "bf16", 2, num_slots, slot_map, out_dt="bf16")
 
 
 def test_decode_identity_token_keeps_state_bit_identical():
