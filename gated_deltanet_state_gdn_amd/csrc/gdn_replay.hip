@@ -33,6 +33,10 @@
 #ifndef GDN_REPLAY_NT_F32
 #define GDN_REPLAY_NT_F32 1
 #endif
+// fp32 128 x 128 one-token windows go through the persistent stream kernel
+#ifndef GDN_REPLAY_STREAM_PERSIST
+#define GDN_REPLAY_STREAM_PERSIST 1
+#endif
 // waves per workgroup of the stream kernel, every checkpoint dtype (for 16-bit
 // tiles two waves ran T = 5 windows 10% slower on MI355X, eight no faster)
 #ifndef GDN_REPLAY_WAVES
@@ -1293,6 +1297,97 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   }
 }
 
+// Persistent stream for fp32 128 x 128 checkpoints and one-token windows (the
+// decode layer's standard step).  One workgroup of 16 waves per compute unit
+// walks the units u = blockIdx.x + i G with the next unit's tile and w / acc
+// rows in flight while the current S0^T w is reduced (the decode kernel's
+// persistent layout and two-level column sums; the tile is only read).  Unit
+// slots are staged in LDS first; every load is unconditional (padded rows read
+// through a zero-size buffer), so the compiler's waits leave the next unit's
+// loads outstanding.
+constexpr int kStreamPersistNW = 16;
+constexpr int kStreamPersistMaxIter = 512;
+
+template <bool NTL>
+__global__ void __launch_bounds__(kStreamPersistNW * 64, 1)
+gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ ws) {
+  constexpr int D = 128, NW = kStreamPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
+  static_assert(PASSES == 4, "four rows per lane");
+  typedef unsigned int Raw __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float s_red[2][NW][D];  // [parity][wave][column]
+  __shared__ __attribute__((aligned(16))) float s_sum[2][D];      // [parity][column]
+  __shared__ int s_slot[kStreamPersistMaxIter];
+
+  const DecodeArgs& p = P.d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = (lane % LPR) * VEC, r0 = wave * RPW + lane / LPR;
+  const int units = p.B * p.Hv, G = gridDim.x;
+  int t = blockIdx.x;
+  if (t >= units) return;
+  const int n_iter = (units - t + G - 1) / G;  // <= kStreamPersistMaxIter (launcher)
+  for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t + i * G) / p.Hv];
+  __syncthreads();
+
+  auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
+  struct In {
+    Raw raw[PASSES];
+    float w[PASSES];
+    f32x4 acc;
+  };
+  auto fetch = [&](int u, int slot, In& x) {
+    const int h = u % p.Hv;
+    const bool ok = valid(slot);
+    const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(tile), 0, ok ? D * D * 4 : 0, 0x00020000);
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp)
+      x.raw[pp] = __builtin_bit_cast(
+          Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, (r0 * D + c0) * 4, pp * NW * RPW * D * 4, NTL ? 2 : 0));
+    const float* wsu = ws + (int64_t)u * 2 * D;  // T = 1: w, then acc
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) x.w[pp] = wsu[r0 + pp * NW * RPW];
+    x.acc = *reinterpret_cast<const f32x4*>(wsu + D + c0);
+  };
+
+  In cur, nxt;
+  fetch(t, s_slot[0], cur);
+  for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
+    const int tn = t + G;
+    // past the last unit the loads repeat this unit's vectors, with no tile
+    fetch(tn < units ? tn : t, tn < units ? s_slot[it + 1] : -1, nxt);
+    const int64_t out_row = (int64_t)t * D;  // (b T + 0) Hv + h with T = 1
+    if (!valid(s_slot[it])) {  // padded row (uniform over the workgroup)
+      if (tid < D) store_elem(p.out, out_row + tid, 0.f, p.out_dt);
+    } else {
+      float part[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part[e] = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) part[e] = fmaf(__uint_as_float(cur.raw[pp][e]), cur.w[pp], part[e]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part[e] = xor_sum_from<LPR>(part[e]);
+      if (lane < LPR) *reinterpret_cast<f32x4*>(&s_red[par][wave][c0]) = f32x4{part[0], part[1], part[2], part[3]};
+      __syncthreads();
+      if (tid < D) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) a += s_red[par][w][tid];
+        s_sum[par][tid] = a;
+      }
+      __syncthreads();
+      if (wave == 0 && lane < LPR) {
+        const f32x4 sm = *reinterpret_cast<const f32x4*>(&s_sum[par][c0]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) store_elem(p.out, out_row + c0 + e, p.scale * (cur.acc[e] + sm[e]), p.out_dt);
+      }
+    }
+    cur = nxt;
+  }
+}
+
 // ---------------------------------------------------------------- rollback
 __global__ void gdn_replay_rollback_kernel(const ReplayArgs P) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1366,6 +1461,22 @@ static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws,
   const size_t lds = (size_t)a.T * D * sizeof(float);
   const bool one = a.T <= 1;
   const bool nt16 = stream_tile_reads((long long)grid * D * D * 2);  // 16-bit checkpoints read once per call
+  if constexpr (D == 128) {
+    if (read_dt == GDN_F32 && a.T == 1 && GDN_REPLAY_STREAM_PERSIST != 0) {
+      const void* kern = reinterpret_cast<const void*>(&gdn_replay_stream_persist_kernel<GDN_REPLAY_NT_F32 != 0>);
+      int per_cu = 0, cus = 0;
+      hipError_t e = resident_blocks(kern, kStreamPersistNW * 64, 0, &per_cu);
+      if (e == hipSuccess) e = device_cus(&cus);
+      if (e != hipSuccess) return e;
+      const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+      const unsigned pgrid = (unsigned)((int64_t)grid < fill ? (int64_t)grid : fill);
+      if ((int64_t)grid > 8 * (int64_t)pgrid && (int64_t)grid <= (int64_t)pgrid * kStreamPersistMaxIter) {
+        hipLaunchKernelGGL((gdn_replay_stream_persist_kernel<GDN_REPLAY_NT_F32 != 0>), dim3(pgrid),
+                           dim3(kStreamPersistNW * 64), 0, s, a, static_cast<const float*>(ws));
+        return hipGetLastError();
+      }
+    }
+  }
   switch (read_dt) {
     case GDN_F32:
       one ? launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, 1>(a, grid, lds, ws, s)
