@@ -566,7 +566,7 @@ def main():
                                "in a 1024-slot pool, bf16 q/k/v/a/b, bf16 out, one token per step",
                    "B": 256, "Hk": HK, "Hv": HV, "dk": D, "dv": D, "state_dtype": "f32",
                    "bytes_per_step": head["bytes_per_step"]},
-        "roofline": dict(head["roofline"], kernel="gdn_decode_kernel<f32,128>",
+        "roofline": dict(head["roofline"], kernel="gdn_decode_persist_kernel<f32,128>",
                          mean_launch_us=head["mean_launch_us"]),
         "cpu_baseline": cpu,
         "rows": rows,
