@@ -68,6 +68,7 @@ class ReplayCase:
             self.ref_ckpt, self.ref_copy, self.ref_ring, o_ref = O.replay_decode_dual(
                 self.ref_ckpt, self.ref_copy, self.ref_ring, *args)
         o = host(out)
+        self.last_out = o
         assert np.all(np.isfinite(o)), "non-finite output"
         tol = "f32" if self.sdt == "f32" and self.copy_dt is None else "bf16"
         assert_close(o[self.rows], o_ref, tol, f"o step {step}")
@@ -243,6 +244,22 @@ def test_replay_layer_bf16_spec_sampled():
     c.check_state("after spec steps")
     c.flush()
     c.check_state("flush")
+
+
+def test_replay_persistent_stream_padded_rows():
+    """fp32 128 x 128 checkpoints, 80 rows x 32 value heads (2560 units, about ten per workgroup of
+    the persistent stream) with padded rows spread through the walk; 18 one-token steps cross a
+    fold.  Padded rows read as zero outputs, the others match the oracle."""
+    import torch
+    c = ReplayCase(44, 80, 16, 32, 128, 16, "f32", 96, sample=[0, 5, 41, 78])
+    pad = [3, 17, 40, 79]
+    sm = c.slot_map.copy()
+    sm[pad] = [-1, 96, -7, 200]
+    c.slot_d = torch.from_numpy(sm).to(DEV)
+    for step in range(18):
+        c.step(step, 1)
+        assert np.all(c.last_out[pad] == 0), f"padded rows, step {step}"
+    c.check_state("after a fold")
 
 
 def test_replay_padded_rows():
