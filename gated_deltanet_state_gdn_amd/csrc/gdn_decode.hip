@@ -41,6 +41,10 @@
 #ifndef GDN_DECODE_PERSIST
 #define GDN_DECODE_PERSIST 1
 #endif
+// 16-bit 128 x 128 tiles through the persistent 8-wave kernel (measured slower)
+#ifndef GDN_DECODE_PERSIST_16
+#define GDN_DECODE_PERSIST_16 0
+#endif
 
 namespace gdn {
 
@@ -185,10 +189,15 @@ constexpr int kPersistNW = 16;
 constexpr int kPersistMaxIter = 512;  // tiles per workgroup whose slot and head scalars sit in LDS
 
 // NTL / NTS: non-temporal tile loads / stores.
+// Waves per workgroup: 16 for fp32 tiles (one workgroup per CU), 8 for 16-bit
+// ones (two per CU, four 16-byte loads per lane either way).
+template <int SDT>
+constexpr int persist_waves() { return SDT == GDN_F32 ? kPersistNW : kPersistNW / 2; }
+
 template <int SDT, bool NTL, bool NTS, int IDT>
-__global__ void __launch_bounds__(kPersistNW * 64, 1) gdn_decode_persist_kernel(const DecodeArgs p) {
+__global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persist_kernel(const DecodeArgs p) {
   // 16-byte accesses: 4 fp32 or 8 16-bit columns per lane
-  constexpr int D = 128, NW = kPersistNW, VEC = SDT == GDN_F32 ? 4 : 8, LPR = D / VEC, RPW = 64 / LPR;
+  constexpr int D = 128, NW = persist_waves<SDT>(), VEC = SDT == GDN_F32 ? 4 : 8, LPR = D / VEC, RPW = 64 / LPR;
   constexpr int PASSES = D / (RPW * NW);
   static_assert(PASSES * RPW * NW == D, "whole rows per pass");
   using IO = TileIO<SDT, VEC, NTS>;
@@ -371,11 +380,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.B * a.Hv);
   constexpr bool NT = (SDT == GDN_F32) ? (GDN_DECODE_NT_F32 != 0) : (GDN_DECODE_NT_16 != 0);
   const long long tile_bytes = (long long)grid * D * D * (long long)sizeof(typename StateElem<SDT>::T);
-  // fp32 only: 16-bit tiles (32 KiB) ran at 3.66-3.83 TB/s in it against
-  // 4.62-5.14 for the one-shot two-wave kernel, which keeps eight such tiles in
-  // flight per CU where the pipeline keeps two
-  if constexpr (SDT == GDN_F32 && D == 128 && GDN_DECODE_PERSIST != 0) {
-    const bool ntl = NT, nts = NT;  // streamed both ways
+  // fp32 by default: 16-bit tiles (32 KiB) ran at 3.66-3.83 TB/s with 16-wave
+  // workgroups and 4.16-4.72 with 8-wave ones (two per CU) against 4.62-5.14
+  // for the one-shot two-wave kernel, which keeps eight such tiles in flight
+  // per CU
+  if constexpr (D == 128 && GDN_DECODE_PERSIST != 0 && (SDT == GDN_F32 || GDN_DECODE_PERSIST_16 != 0)) {
+    // fp32: streamed both ways; 16-bit: the cache rules of the one-shot kernel
+    const bool ntl = SDT == GDN_F32 ? NT : stream_tile_reads(tile_bytes);
+    const bool nts = SDT == GDN_F32 ? NT : stream_tile_writes(tile_bytes);
     void (*kern)(const DecodeArgs) = nullptr;
     auto pick = [&](auto ntl_c, auto nts_c) {
       constexpr bool L = decltype(ntl_c)::value, S = decltype(nts_c)::value;
@@ -387,7 +399,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     else if (ntl) pick(std::true_type{}, std::false_type{});
     else pick(std::false_type{}, std::false_type{});
     int per_cu = 0, cus = 0;
-    hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), kPersistNW * 64, 0, &per_cu);
+    constexpr int nth = persist_waves<SDT>() * 64;
+    hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), nth, 0, &per_cu);
     if (e == hipSuccess) e = device_cus(&cus);
     if (e != hipSuccess) return e;
     const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
@@ -395,7 +408,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     // with 8 or fewer tiles per workgroup the pipeline has too little to overlap
     // (fp32 at B = 64: 5.06-5.25 TB/s against 5.28-5.30 for the one-shot kernel)
     if ((int64_t)grid > 8 * (int64_t)pgrid && (int64_t)grid <= (int64_t)pgrid * kPersistMaxIter) {
-      hipLaunchKernelGGL(kern, dim3(pgrid), dim3(kPersistNW * 64), 0, s, a);
+      hipLaunchKernelGGL(kern, dim3(pgrid), dim3(nth), 0, s, a);
       return hipGetLastError();
     }
   }
