@@ -52,6 +52,37 @@ def test_mamba2_decode_parity(sdt, d, n):
         assert_close(got[s], ref[i], sdt, f"state slot {s}")
 
 
+@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
+def test_mamba2_decode_full_heads_persistent_walk(in_dt):
+    """The benchmark layer's heads (128 of 64 x 128 in 8 groups, fp32 state) at B = 24: 3072
+    units, about twelve per workgroup of the persistent kernel, three padded rows spread through
+    the walk; 2 steps, every element."""
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    lay = gen.M2_LAYER
+    cid, B, H, G, d, n, num_slots = 81, 24, lay["H"], lay["G"], lay["d"], lay["n"], 32
+    slot_map = gen.slot_permutation(cid, num_slots)[:B].copy()
+    slot_map[[2, 11, 23]] = [-1, num_slots, -4]
+    valid = [int(s) for s in slot_map if 0 <= s < num_slots]
+    pool_d, states = poisoned_pool(num_slots, H, d, n, "f32", valid, cid)
+    ref = states
+    ref_map = np.array([valid.index(int(s)) if 0 <= s < num_slots else -1 for s in slot_map], np.int32)
+    A_log, dt_bias, Dk = gen.m2_params(cid, H)
+    P = [dev(t) for t in (A_log, dt_bias, Dk)]
+    sm = torch.from_numpy(slot_map).to(DEV)
+    for step in range(2):
+        inp = gen.m2_inputs(cid, step, (B,), H, G, d, n, in_dt)
+        say(f"mamba2 decode B={B} H={H} in={in_dt} step={step}")
+        y = gdn.gdn_mamba2_decode_step(dev(inp["x"]), dev(inp["Bm"]), dev(inp["Cm"]), dev(inp["dt"]), *P, pool_d, sm)
+        torch.cuda.synchronize()
+        ref, y_ref = O.mamba2_decode_step(ref, ref_map, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], A_log, dt_bias,
+                                          Dk)
+        assert_close(host(y), y_ref, "f32", f"y step {step}")
+    got = host(pool_d)
+    for i, s in enumerate(valid):
+        assert_close(got[s], ref[i], "f32", f"state slot {s}")
+
+
 class M2Case:
     def __init__(self, cid, B, H, G, d, n, L, sdt, num_slots, sample=None, in_dt="bf16"):
         import torch
