@@ -1297,8 +1297,9 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   }
 }
 
-// Persistent stream for fp32 128 x 128 checkpoints and one-token windows (the
-// decode layer's standard step).  One workgroup of 16 waves per compute unit
+// Persistent stream for fp32 128 x 128 checkpoints and windows of up to
+// kStreamPersistTMax positions (the decode layer's standard step and its
+// verify windows).  One workgroup of 16 waves per compute unit
 // walks the units u = blockIdx.x + i G with the next unit's tile and w / acc
 // rows in flight while the current S0^T w is reduced (the decode kernel's
 // persistent layout and two-level column sums; the tile is only read).  Unit
@@ -1307,18 +1308,23 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
 // loads outstanding.
 constexpr int kStreamPersistNW = 16;
 constexpr int kStreamPersistMaxIter = 512;
+constexpr int kStreamPersistTMax = 5;  // window positions per unit (LDS: 80 KiB of partials at 5)
 
-template <bool NTL>
-__global__ void __launch_bounds__(kStreamPersistNW * 64, 1)
+template <bool NTL, int TMAX>
+__global__ void __launch_bounds__(kStreamPersistNW * 64, 4)
 gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   constexpr int D = 128, NW = kStreamPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
   static_assert(PASSES == 4, "four rows per lane");
+  static_assert(TMAX * D <= NW * 64, "one w / acc element per thread");
   typedef unsigned int Raw __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) float s_red[2][NW][D];  // [parity][wave][column]
-  __shared__ __attribute__((aligned(16))) float s_sum[2][D];      // [parity][column]
+  __shared__ __attribute__((aligned(16))) float s_red[2][TMAX][NW][D];  // [parity][position][wave][column]
+  __shared__ __attribute__((aligned(16))) float s_sum[2][TMAX][D];      // [parity][position][column]
+  __shared__ __attribute__((aligned(16))) float s_w[2][TMAX][D];        // [parity][position][row]: w
+  __shared__ __attribute__((aligned(16))) float s_acc[2][TMAX][D];      // [parity][position][column]: acc
   __shared__ int s_slot[kStreamPersistMaxIter];
 
   const DecodeArgs& p = P.d;
+  const int T = P.T;  // 1 <= T <= TMAX (launcher)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = (lane % LPR) * VEC, r0 = wave * RPW + lane / LPR;
   const int units = p.B * p.Hv, G = gridDim.x;
@@ -1326,15 +1332,18 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   if (t >= units) return;
   const int n_iter = (units - t + G - 1) / G;  // <= kStreamPersistMaxIter (launcher)
   for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t + i * G) / p.Hv];
-  __syncthreads();
 
   auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
+  // thread tid < T D carries element tid of the unit's w and acc vectors (w_t, acc_t by position)
+  const int wi = tid < T * D ? tid : T * D - 1, wt = wi / D, wc = wi - wt * D;
   struct In {
     Raw raw[PASSES];
-    float w[PASSES];
-    f32x4 acc;
+    float w, acc;
   };
   auto fetch = [&](int u, int slot, In& x) {
+    const float* wsu = ws + (int64_t)u * T * 2 * D;  // per position: w, then acc
+    x.w = wsu[2 * wt * D + wc];  // before the tile: waiting for these leaves the tile in flight
+    x.acc = wsu[(2 * wt + 1) * D + wc];
     const int h = u % p.Hv;
     const bool ok = valid(slot);
     const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
@@ -1344,46 +1353,62 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
     for (int pp = 0; pp < PASSES; ++pp)
       x.raw[pp] = __builtin_bit_cast(
           Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, (r0 * D + c0) * 4, pp * NW * RPW * D * 4, NTL ? 2 : 0));
-    const float* wsu = ws + (int64_t)u * 2 * D;  // T = 1: w, then acc
-#pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) x.w[pp] = wsu[r0 + pp * NW * RPW];
-    x.acc = *reinterpret_cast<const f32x4*>(wsu + D + c0);
   };
 
   In cur, nxt;
+  __syncthreads();  // s_slot
   fetch(t, s_slot[0], cur);
+  if (tid < T * D) {
+    s_w[0][wt][wc] = cur.w;
+    s_acc[0][wt][wc] = cur.acc;
+  }
+  __syncthreads();
   for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
     const int tn = t + G;
-    // past the last unit the loads repeat this unit's vectors, with no tile
+    // past the last unit the loads repeat this unit's, with no tile
     fetch(tn < units ? tn : t, tn < units ? s_slot[it + 1] : -1, nxt);
-    const int64_t out_row = (int64_t)t * D;  // (b T + 0) Hv + h with T = 1
-    if (!valid(s_slot[it])) {  // padded row (uniform over the workgroup)
-      if (tid < D) store_elem(p.out, out_row + tid, 0.f, p.out_dt);
-    } else {
-      float part[VEC];
+    const int b = t / p.Hv, h = t - b * p.Hv;
+    auto out_row = [&](int tt) { return (((int64_t)b * T + tt) * p.Hv + h) * D; };
+    const bool live = valid(s_slot[it]);  // uniform over the workgroup
+    if (live) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) part[e] = 0.f;
+      for (int tt = 0; tt < TMAX; ++tt) {
+        if (tt < T) {
+          float part[VEC];
 #pragma unroll
-      for (int pp = 0; pp < PASSES; ++pp)
+          for (int e = 0; e < VEC; ++e) part[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) part[e] = fmaf(__uint_as_float(cur.raw[pp][e]), cur.w[pp], part[e]);
+          for (int pp = 0; pp < PASSES; ++pp) {
+            const float wr = s_w[par][tt][r0 + pp * NW * RPW];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) part[e] = xor_sum_from<LPR>(part[e]);
-      if (lane < LPR) *reinterpret_cast<f32x4*>(&s_red[par][wave][c0]) = f32x4{part[0], part[1], part[2], part[3]};
-      __syncthreads();
-      if (tid < D) {
-        float a = 0.f;
+            for (int e = 0; e < VEC; ++e) part[e] = fmaf(__uint_as_float(cur.raw[pp][e]), wr, part[e]);
+          }
 #pragma unroll
-        for (int w = 0; w < NW; ++w) a += s_red[par][w][tid];
-        s_sum[par][tid] = a;
-      }
-      __syncthreads();
-      if (wave == 0 && lane < LPR) {
-        const f32x4 sm = *reinterpret_cast<const f32x4*>(&s_sum[par][c0]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) store_elem(p.out, out_row + c0 + e, p.scale * (cur.acc[e] + sm[e]), p.out_dt);
+          for (int e = 0; e < VEC; ++e) part[e] = xor_sum_from<LPR>(part[e]);
+          if (lane < LPR)
+            *reinterpret_cast<f32x4*>(&s_red[par][tt][wave][c0]) = f32x4{part[0], part[1], part[2], part[3]};
+        }
       }
     }
+    __syncthreads();
+    if (live) {
+      for (int i = tid; i < T * D; i += NW * 64) {  // one (position, column) per thread
+        const int tt = i / D, col = i - tt * D;
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) a += s_red[par][tt][w][col];
+        s_sum[par][tt][col] = a;
+      }
+    }
+    // the next unit's w and acc, published by the barrier below
+    if (tid < T * D) {
+      s_w[par ^ 1][wt][wc] = nxt.w;
+      s_acc[par ^ 1][wt][wc] = nxt.acc;
+    }
+    __syncthreads();
+    if (tid < T * D)  // position wt, column wc (padded rows: zeros)
+      store_elem(p.out, out_row(wt) + wc, live ? p.scale * (s_acc[par][wt][wc] + s_sum[par][wt][wc]) : 0.f,
+                 p.out_dt);
     cur = nxt;
   }
 }
@@ -1462,17 +1487,20 @@ static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws,
   const bool one = a.T <= 1;
   const bool nt16 = stream_tile_reads((long long)grid * D * D * 2);  // 16-bit checkpoints read once per call
   if constexpr (D == 128) {
-    if (read_dt == GDN_F32 && a.T == 1 && GDN_REPLAY_STREAM_PERSIST != 0) {
-      const void* kern = reinterpret_cast<const void*>(&gdn_replay_stream_persist_kernel<GDN_REPLAY_NT_F32 != 0>);
+    if (read_dt == GDN_F32 && a.T >= 1 && a.T <= kStreamPersistTMax && GDN_REPLAY_STREAM_PERSIST != 0) {
+      constexpr bool NTL = GDN_REPLAY_NT_F32 != 0;
+      void (*kern)(const ReplayArgs, const float*) = a.T == 1 ? &gdn_replay_stream_persist_kernel<NTL, 1>
+                                                              : &gdn_replay_stream_persist_kernel<NTL, kStreamPersistTMax>;
       int per_cu = 0, cus = 0;
-      hipError_t e = resident_blocks(kern, kStreamPersistNW * 64, 0, &per_cu);
+      hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), kStreamPersistNW * 64, 0, &per_cu);
+      // one workgroup per CU even where two fit (T = 1: 164 against 168 us per call)
+      per_cu = per_cu > 1 ? 1 : per_cu;
       if (e == hipSuccess) e = device_cus(&cus);
       if (e != hipSuccess) return e;
       const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
       const unsigned pgrid = (unsigned)((int64_t)grid < fill ? (int64_t)grid : fill);
       if ((int64_t)grid > 8 * (int64_t)pgrid && (int64_t)grid <= (int64_t)pgrid * kStreamPersistMaxIter) {
-        hipLaunchKernelGGL((gdn_replay_stream_persist_kernel<GDN_REPLAY_NT_F32 != 0>), dim3(pgrid),
-                           dim3(kStreamPersistNW * 64), 0, s, a, static_cast<const float*>(ws));
+        hipLaunchKernelGGL(kern, dim3(pgrid), dim3(kStreamPersistNW * 64), 0, s, a, static_cast<const float*>(ws));
         return hipGetLastError();
       }
     }

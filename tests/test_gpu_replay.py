@@ -246,18 +246,19 @@ def test_replay_layer_bf16_spec_sampled():
     c.check_state("flush")
 
 
-def test_replay_persistent_stream_padded_rows():
+@pytest.mark.parametrize("T", [1, 3, 5])
+def test_replay_persistent_stream_padded_rows(T):
     """fp32 128 x 128 checkpoints, 80 rows x 32 value heads (2560 units, about ten per workgroup of
-    the persistent stream) with padded rows spread through the walk; 18 one-token steps cross a
-    fold.  Padded rows read as zero outputs, the others match the oracle."""
+    the persistent stream) with padded rows spread through the walk, windows of T tokens over
+    enough steps to cross folds.  Padded rows read as zero outputs, the others match the oracle."""
     import torch
-    c = ReplayCase(44, 80, 16, 32, 128, 16, "f32", 96, sample=[0, 5, 41, 78])
+    c = ReplayCase(44 + T, 80, 16, 32, 128, 16, "f32", 96, sample=[0, 5, 41, 78])
     pad = [3, 17, 40, 79]
     sm = c.slot_map.copy()
     sm[pad] = [-1, 96, -7, 200]
     c.slot_d = torch.from_numpy(sm).to(DEV)
-    for step in range(18):
-        c.step(step, 1)
+    for step in range(18 if T == 1 else 8):
+        c.step(step, T)
         assert np.all(c.last_out[pad] == 0), f"padded rows, step {step}"
     c.check_state("after a fold")
 
