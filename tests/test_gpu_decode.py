@@ -118,14 +118,15 @@ def test_decode_padded_rows_and_bf16_output():
     del got
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
-def test_decode_persistent_walk_with_padded_rows(sdt):
+@pytest.mark.parametrize("sdt,in_dt", [("f32", "bf16"), ("f32", "f32"), ("f32", "f16"), ("bf16", "bf16")])
+def test_decode_persistent_walk_with_padded_rows(sdt, in_dt):
     """128 x 128 states: 80 rows x 32 value heads = 2560 tiles, about ten per workgroup of the
-    persistent kernel, with padded rows (-1 and past the pool) spread through the walk."""
+    persistent kernel (fp32 states; each input dtype is its own instantiation), with padded
+    rows (-1 and past the pool) spread through the walk."""
     B, num_slots = 80, 96
     slot_map = gen.slot_permutation(12, num_slots)[:B].copy()
     slot_map[[3, 17, 40, 79]] = [-1, num_slots, -5, num_slots + 3]
-    run_decode(12, B, 16, 32, 128, sdt, "bf16", 2, num_slots, slot_map, out_dt="bf16")
+    run_decode(12, B, 16, 32, 128, sdt, in_dt, 2, num_slots, slot_map, out_dt="bf16")
 
 
 def test_decode_identity_token_keeps_state_bit_identical():
