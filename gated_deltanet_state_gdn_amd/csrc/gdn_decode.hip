@@ -278,9 +278,13 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
     x.gb = bin[row_bh + zl];
   };
 
+  // LDS parity flips on live tiles only.  A padded tile passes no barrier, so
+  // a wave may run ahead through it to the next live tile while a slower wave
+  // still reads the k . q partials of the previous one: the two live tiles
+  // must use different buffers, whatever the padded tiles between them.
   In cur, nxt;
   fetch(t, s_slot[0], cur);
-  for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
+  for (int it = 0, par = 0; t < units; t += G, ++it) {
     const int tn = t + G;
     // past the last tile the loads repeat this tile's inputs, with no state
     fetch(tn < units ? tn : t, tn < units ? s_slot[it + 1] : -1, nxt);
@@ -369,6 +373,7 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
         for (int e = 0; e < VEC; ++e) sv[e] = fmaf(alpha, sv[e], kr[pp] * delta[e]);
         IO::store(tile + (r0 + pp * NW * RPW) * D + c0, sv);
       }
+      par ^= 1;
     }
     cur = nxt;
   }
