@@ -149,6 +149,21 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _keep_for_stream(tensors, stream):
+    """Buffers this binding allocated on the current stream but hands to a launch on another
+    stream are marked as used there, so the caching allocator does not give their memory to a
+    later allocation on the current stream while the launch may still run."""
+    torch = _torch()
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _dims(Hk, Hv, dk, dv, scale):
     return gdn_dims(int(Hk), int(Hv), int(dk), int(dv), float(scale) if scale else 0.0)
 
@@ -197,6 +212,7 @@ def gdn_decode_step(q, k, v, a, b, A_log, dt_bias, pool, slot_map, out=None, out
     Hv, dv = v.shape[1], v.shape[2]
     if out is None:
         out = torch.empty((B, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+        _keep_for_stream([out], stream)
     dims = _dims(Hk, Hv, dk, dv, scale)
     _check(lib().gdn_decode_step(ctypes.byref(dims), B, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
                                  ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(pool)),
@@ -213,6 +229,7 @@ def gdn_spec_decode(q, k, v, a, b, A_log, dt_bias, pool, src_slots, dst_slots, o
     Hv, dv = v.shape[2], v.shape[3]
     if out is None:
         out = torch.empty((B, T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+        _keep_for_stream([out], stream)
     dims = _dims(Hk, Hv, dk, dv, scale)
     _check(lib().gdn_spec_decode(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
                                  ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(pool)),
@@ -278,9 +295,11 @@ def gdn_chunk_prefill(q, k, v, a, b, A_log, dt_bias, pool, slot_map, cu_seqlens,
     N = int(cu_seqlens.shape[0]) - 1
     if out is None:
         out = torch.empty((T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+        _keep_for_stream([out], stream)
     need = gdn_chunk_prefill_workspace_bytes(Hk, Hv, dk, dv, N, T, chunk)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _keep_for_stream([workspace], stream)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dims = _dims(Hk, Hv, dk, dv, scale)
@@ -305,9 +324,11 @@ def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring,
     Hv, dv = v.shape[2], v.shape[3]
     if out is None:
         out = torch.empty((B, T, Hv, dv), dtype=out_dtype or torch.float32, device=q.device)
+        _keep_for_stream([out], stream)
     need = gdn_replay_workspace_bytes(Hk, Hv, dk, dv, B, T)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _keep_for_stream([workspace], stream)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dims = _dims(Hk, Hv, dk, dv, scale)
@@ -393,6 +414,7 @@ def gdn_mamba2_decode_step(x, Bm, Cm, dt, A_log, dt_bias, D, pool, slot_map, out
     G, n = Bm.shape[1], Bm.shape[2]
     if out is None:
         out = torch.empty((B, H, d), dtype=out_dtype or torch.float32, device=x.device)
+        _keep_for_stream([out], stream)
     dims = gdn_m2_dims(H, G, d, n)
     _check(lib().gdn_mamba2_decode_step(ctypes.byref(dims), B, _ptr(x), _ptr(Bm), _ptr(Cm), dtype_code(x.dtype),
                                         ctypes.byref(_m2_params(dt, A_log, dt_bias, D)), ctypes.byref(_pool(pool)),
@@ -408,6 +430,7 @@ def gdn_mamba2_replay_decode(x, Bm, Cm, dt, A_log, dt_bias, D, ckpt, slot_map, r
     G, n = Bm.shape[2], Bm.shape[3]
     if out is None:
         out = torch.empty((B, T, H, d), dtype=out_dtype or torch.float32, device=x.device)
+        _keep_for_stream([out], stream)
     dims = gdn_m2_dims(H, G, d, n)
     rs = ring.c_struct()
     _check(lib().gdn_mamba2_replay_decode(ctypes.byref(dims), B, T, _ptr(x), _ptr(Bm), _ptr(Cm), dtype_code(x.dtype),
