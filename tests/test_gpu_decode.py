@@ -88,7 +88,28 @@ def test_decode_layer_f32_64_steps_sampled():
     s = cfg.shape
     slot_map = gen.slot_permutation(1, cfg.num_slots)[:s.B]
     run_decode(1, s.B, s.Hk, s.Hv, s.dk, "f32", "bf16", cfg.steps, cfg.num_slots, slot_map,
-               sample=[0, 1, 97, 128, 200, 255], check_every=8)
+               sample=[0, 1, 31, 97, 128, 129, 200, 254, 255], check_every=8)
+
+
+def test_decode_layer_f32_B512_sampled():
+    """The fp32 layer at B = 512 (16384 tiles, 64 per workgroup of the persistent kernel), 16 steps,
+    sampled rows spread over the batch."""
+    cfg = gen.WORKLOADS["decode_f32"]
+    s = cfg.shape
+    B = 512
+    slot_map = gen.slot_permutation(11, cfg.num_slots)[:B]
+    run_decode(11, B, s.Hk, s.Hv, s.dk, "f32", "bf16", 16, cfg.num_slots, slot_map,
+               sample=[0, 1, 63, 64, 255, 256, 300, 449, 510, 511], check_every=5)
+
+
+@pytest.mark.parametrize("B", [256, 512])
+def test_decode_layer_f32_every_row(B):
+    """Every output and every state element of the fp32 layer at B = 256 and 512 (the persistent
+    kernel's launches of the headline and the large-batch row), over two steps."""
+    cfg = gen.WORKLOADS["decode_f32"]
+    s = cfg.shape
+    slot_map = gen.slot_permutation(13, cfg.num_slots)[:B]
+    run_decode(13, B, s.Hk, s.Hv, s.dk, "f32", "bf16", 2, cfg.num_slots, slot_map)
 
 
 @pytest.mark.parametrize("sdt", ["bf16", "f16"])
@@ -118,15 +139,25 @@ def test_decode_padded_rows_and_bf16_output():
     del got
 
 
-@pytest.mark.parametrize("sdt,in_dt", [("f32", "bf16"), ("f32", "f32"), ("f32", "f16"), ("bf16", "bf16")])
-def test_decode_persistent_walk_with_padded_rows(sdt, in_dt):
-    """128 x 128 states: 80 rows x 32 value heads = 2560 tiles, about ten per workgroup of the
-    persistent kernel (fp32 states; each input dtype is its own instantiation), with padded
-    rows (-1 and past the pool) spread through the walk."""
+@pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
+def test_decode_persistent_walk_with_padded_rows(in_dt):
+    """fp32 128 x 128 states: 80 rows x 32 value heads = 2560 tiles, about ten per workgroup of the
+    persistent kernel (each input dtype is its own instantiation), with padded rows (-1 and past
+    the pool) spread through the walk, two of them back to back, so live tiles sit on both sides
+    of padded ones within a workgroup's walk."""
     B, num_slots = 80, 96
     slot_map = gen.slot_permutation(12, num_slots)[:B].copy()
-    slot_map[[3, 17, 40, 79]] = [-1, num_slots, -5, num_slots + 3]
-    run_decode(12, B, 16, 32, 128, sdt, in_dt, 2, num_slots, slot_map, out_dt="bf16")
+    slot_map[[3, 17, 18, 40, 79]] = [-1, num_slots, -2, -5, num_slots + 3]
+    run_decode(12, B, 16, 32, 128, "f32", in_dt, 3, num_slots, slot_map, out_dt="bf16")
+
+
+def test_decode_one_shot_16bit_walk_with_padded_rows():
+    """The same 2560-tile launch with bf16 states, which the one-shot kernel serves (one workgroup
+    per tile), with the same padded rows."""
+    B, num_slots = 80, 96
+    slot_map = gen.slot_permutation(12, num_slots)[:B].copy()
+    slot_map[[3, 17, 18, 40, 79]] = [-1, num_slots, -2, -5, num_slots + 3]
+    run_decode(12, B, 16, 32, 128, "bf16", "bf16", 2, num_slots, slot_map, out_dt="bf16")
 
 
 def test_decode_identity_token_keeps_state_bit_identical():

@@ -209,3 +209,44 @@ def test_mamba2_replay_full_layer_sampled():
         c.step(step, 1)
         if step in (15, 16, 17):
             c.check_state(f"step {step}")
+
+
+def test_mamba2_replay_B512_sampled():
+    """The benchmark row's shape: B = 512 of the 128-head layer (64 x 128 fp32 checkpoints in a
+    600-slot pool), L = 16, 18 steps over a fold, sampled rows spread over the batch."""
+    lay = gen.M2_LAYER
+    c = M2Case(6, 512, lay["H"], lay["G"], lay["d"], lay["n"], 16, "f32", 600, sample=[0, 200, 511])
+    for step in range(18):
+        c.step(step, 1)
+        if step in (0, 15, 16, 17):
+            c.check_state(f"step {step}")
+
+
+def test_mamba2_decode_B512_sampled():
+    """The benchmark row's decode: B = 512 of the 128-head layer, fp32 state, 3 steps; sampled rows
+    against the oracle, every output finite."""
+    import torch
+    import gated_deltanet_state_gdn_amd as gdn
+    lay = gen.M2_LAYER
+    cid, B, H, G, d, n, num_slots = 7, 512, lay["H"], lay["G"], lay["d"], lay["n"], 600
+    rows = [0, 300, 511]
+    slot_map = gen.slot_permutation(cid, num_slots)[:B]
+    pool_d, states = poisoned_pool(num_slots, H, d, n, "f32", [int(s) for s in slot_map], cid)
+    ref = states[rows]
+    A_log, dt_bias, Dk = gen.m2_params(cid, H)
+    P = [dev(t) for t in (A_log, dt_bias, Dk)]
+    sm = torch.from_numpy(slot_map).to(DEV)
+    for step in range(3):
+        inp = gen.m2_inputs(cid, step, (B,), H, G, d, n, "bf16")
+        say(f"mamba2 decode B={B} step={step}")
+        y = gdn.gdn_mamba2_decode_step(dev(inp["x"]), dev(inp["Bm"]), dev(inp["Cm"]), dev(inp["dt"]), *P, pool_d, sm)
+        torch.cuda.synchronize()
+        sub = {k: v[rows] for k, v in inp.items()}
+        ref, y_ref = O.mamba2_decode_step(ref, np.arange(len(rows), dtype=np.int32), sub["x"], sub["Bm"], sub["Cm"],
+                                          sub["dt"], A_log, dt_bias, Dk)
+        yh = host(y)
+        assert np.all(np.isfinite(yh)), "non-finite output"
+        assert_close(yh[rows], y_ref, "f32", f"y step {step}")
+    got = host(pool_d)
+    for i, r in enumerate(rows):
+        assert_close(got[int(slot_map[r])], ref[i], "f32", f"state row {r}")

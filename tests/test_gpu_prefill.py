@@ -93,31 +93,32 @@ def test_prefill_fp32_inputs_slow_decay():
     run_prefill(72, [700, 129], 2, 2, 64, "f32", in_dt="f32", a_shift=-6.0)
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
-def test_prefill_two_call_split_equals_one_call(sdt):
-    """First 55% of each sequence, then the rest, equals one call: the state is carried exactly
-    (one extra rounding at the split for a bf16 state)."""
+def run_split(cid, lengths, Hk, Hv, D, sdt, num_slots, sample=None, a_shift=0.0):
+    """One call over the whole sequences against two calls (the first 55% of each sequence, then the
+    rest) on a copy of the pool: outputs and final states equal within the state dtype's bar (one
+    extra rounding at the split), and the split path matches the oracle's two calls, on every
+    (sequence, head) pair or on the sampled ones."""
     import torch
     import gated_deltanet_state_gdn_amd as gdn
-    lengths = [300, 129, 64]
     first, second = gen.split_lengths(lengths)
-    Hk, Hv, D, cid = 2, 4, 64, 73
     N = len(lengths)
-    slot_map = gen.slot_permutation(cid, 6)[:N]
-    pool1, st = poisoned_pool(6, Hv, D, D, sdt, [int(s) for s in slot_map], cid)
+    slot_map = gen.slot_permutation(cid, num_slots)[:N]
+    pool1, st = poisoned_pool(num_slots, Hv, D, D, sdt, [int(s) for s in slot_map], cid)
     pool2 = pool1.clone()
     cu = gen.seq_lengths_cu(lengths)
-    inp = gen.token_inputs(cid, 0, (int(cu[-1]),), Hk, Hv, D, D, "bf16", -3.0)
+    inp = gen.token_inputs(cid, 0, (int(cu[-1]),), Hk, Hv, D, D, "bf16", a_shift)
     A_log, dt_bias = gen.head_params(cid, Hv)
     args = (dev(A_log), dev(dt_bias))
     sm = torch.from_numpy(slot_map).to(DEV)
-    say("prefill two-call split: one call")
+    say(f"prefill two-call split: one call, lengths {list(lengths)} Hk={Hk} Hv={Hv} D={D} state={sdt}")
     o_one = gdn.gdn_chunk_prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]), *args,
                                   pool1, sm, torch.from_numpy(cu).to(DEV))
     o_two = torch.empty_like(o_one)
     off = [0] * N
+    parts = []
     for part in (first, second):
         idx = np.concatenate([np.arange(cu[n] + off[n], cu[n] + off[n] + part[n]) for n in range(N)])
+        parts.append((part, idx))
         sub = {k: v[idx] for k, v in inp.items()}
         say(f"prefill two-call split: part {part}")
         o_p = gdn.gdn_chunk_prefill(dev(sub["q"]), dev(sub["k"]), dev(sub["v"]), dev(sub["a"]), dev(sub["b"]),
@@ -125,22 +126,51 @@ def test_prefill_two_call_split_equals_one_call(sdt):
         o_two[torch.from_numpy(idx).to(DEV)] = o_p
         off = [o_ + p for o_, p in zip(off, part)]
     torch.cuda.synchronize()
-    assert_close(host(o_two), host(o_one), "f32" if sdt == "f32" else "bf16", "outputs")
-    assert_close(host(pool2)[slot_map], host(pool1)[slot_map], sdt, "final states")
-    # and the split path against the oracle's two calls
-    mini = np.stack([st[i] for i in range(N)])
-    ref = mini
+    otol = "f32" if sdt == "f32" else "bf16"
+    o_two_h, o_one_h = host(o_two), host(o_one)
+    assert np.all(np.isfinite(o_two_h)), "non-finite output"
+    assert_close(o_two_h, o_one_h, otol, "two calls vs one call: outputs")
+    assert_close(host(pool2)[slot_map], host(pool1)[slot_map], sdt, "two calls vs one call: final states")
+    # the split path against the oracle's two calls (rounding to the state dtype at the split)
+    # (one oracle run per sampled pair, so only those pairs are computed)
+    groups = [(None, None)] if sample is None else [([n], [h]) for n, h in sample]
+    ref = np.stack([st[i] for i in range(N)])
     ref_o = np.zeros((int(cu[-1]), Hv, D))
-    off = [0] * N
-    for part in (first, second):
-        idx = np.concatenate([np.arange(cu[n] + off[n], cu[n] + off[n] + part[n]) for n in range(N)])
-        sub = {k: v[idx] for k, v in inp.items()}
-        ref, o_p = O.chunk_prefill(ref, np.arange(N), gen.seq_lengths_cu(part), sub["q"], sub["k"], sub["v"],
-                                   sub["a"], sub["b"], A_log, dt_bias)
-        ref_o[idx] = o_p
-        off = [o_ + p for o_, p in zip(off, part)]
-    assert_close(host(o_two), ref_o, "f32" if sdt == "f32" else "bf16", "split outputs vs oracle")
-    assert_close(host(pool2)[slot_map], ref, sdt, "split states vs oracle")
+    for seqs, heads in groups:
+        for part, idx in parts:
+            sub = {k: v[idx] for k, v in inp.items()}
+            ref, o_p = O.chunk_prefill(ref, np.arange(N), gen.seq_lengths_cu(part), sub["q"], sub["k"], sub["v"],
+                                       sub["a"], sub["b"], A_log, dt_bias, heads=heads, seqs=seqs)
+            if seqs is None:
+                ref_o[idx] = o_p
+            else:
+                mask = (idx >= cu[seqs[0]]) & (idx < cu[seqs[0] + 1])
+                ref_o[idx[mask], heads[0]] = o_p[mask, heads[0]]
+    got_pool = host(pool2)
+    pairs = sample if sample is not None else [(n, h) for n in range(N) for h in range(Hv)]
+    for n, h in pairs:
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        assert_close(o_two_h[sl, h], ref_o[sl, h], otol, f"split outputs vs oracle, seq {n} head {h}")
+        assert_close(got_pool[slot_map[n], h], ref[n, h], sdt, f"split state vs oracle, seq {n} head {h}")
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
+def test_prefill_two_call_split_equals_one_call(sdt):
+    """First 55% of each sequence, then the rest, equals one call: the state is carried exactly
+    (one extra rounding at the split for a 16-bit state); every (sequence, head) checked."""
+    run_split(73, [300, 129, 64], 2, 4, 64, sdt, 6, a_shift=-3.0)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
+def test_prefill_two_call_split_workload(sdt):
+    """The split at the full workload: 4 packed sequences of 1024, 3000, 8192, 8192 tokens split at
+    55% (563/461, 1650/1350, 4505/3687, 4505/3687), 16 key / 32 value heads, 128 x 128 states
+    read from slots.  Two calls equal one call on every element; sampled (sequence, head) pairs
+    against the oracle."""
+    cfg = gen.WORKLOADS["prefill"]
+    s = cfg.shape
+    sample = [(0, 3), (1, 30), (2, 0), (3, 19)]
+    run_split(31, cfg.extra["lengths"], s.Hk, s.Hv, s.dk, sdt, cfg.num_slots, sample=sample)
 
 
 def test_prefill_padded_sequence():
@@ -161,7 +191,7 @@ def test_prefill_wide_heads_16bit_states_with_padding(sdt):
     assert np.all(o[130:170] == 0)
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 def test_prefill_workload_sampled(sdt):
     """Full-size workload: 4 packed sequences of 1024, 3000, 8192, 8192 tokens, 16 key / 32 value
     heads, 128 x 128 states read from slots; sampled (sequence, head) pairs against the oracle."""
