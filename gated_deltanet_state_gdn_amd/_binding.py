@@ -21,7 +21,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ELAUNCH = 0, 1, 2, 3
 # every symbol include/gdn.h declares
 EXPORTS = (
     "gdn_decode_step", "gdn_spec_decode", "gdn_copy_state_blocks", "gdn_chunk_prefill_workspace_bytes", "gdn_chunk_prefill", "gdn_replay_workspace_bytes",
-    "gdn_replay_decode",
+    "gdn_replay_decode", "gdn_replay_decode_noalloc",
     "gdn_replay_flush", "gdn_replay_rollback", "gdn_replay_decode_dual", "gdn_replay_flush_dual",
     "gdn_mamba2_decode_step", "gdn_mamba2_replay_decode", "gdn_mamba2_replay_flush", "gdn_mamba2_replay_rollback",
     "gdn_status_string", "gdn_last_error",
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "gdn_chunk_prefill": (INT, [pd, I32, P, I64, I32, P, P, P, INT, pg, pp, P, P, INT, P, SZ, P]),
         "gdn_replay_workspace_bytes": (SZ, [pd, I32, I32]),
         "gdn_replay_decode": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P, SZ, P]),
+        "gdn_replay_decode_noalloc": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, P, pr, P, INT, P]),
         "gdn_replay_flush": (INT, [pd, I32, pp, P, pr, P]),
         "gdn_replay_decode_dual": (INT, [pd, I32, I32, P, P, P, INT, pg, pp, pp, P, pr, P, INT, P, SZ, P]),
         "gdn_replay_flush_dual": (INT, [pd, I32, pp, pp, P, pr, P]),
@@ -340,6 +341,21 @@ def gdn_replay_decode(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring,
         _check(lib().gdn_replay_decode(*head, *tail))
     else:
         _check(lib().gdn_replay_decode_dual(*head, ctypes.byref(_pool(read_copy)), *tail))
+    return out
+
+
+def gdn_replay_decode_noalloc(q, k, v, a, b, A_log, dt_bias, ckpt, slot_map, ring: Ring, out, scale=None,
+                              stream=None):
+    """gdn_replay_decode on the library's fixed device scratch: no workspace argument, and `out`
+    must be given (nothing is allocated)."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dims = _dims(Hk, Hv, dk, dv, scale)
+    rs = ring.c_struct()
+    _check(lib().gdn_replay_decode_noalloc(ctypes.byref(dims), B, T, _ptr(q), _ptr(k), _ptr(v), dtype_code(q.dtype),
+                                           ctypes.byref(_gates(a, b, A_log, dt_bias)), ctypes.byref(_pool(ckpt)),
+                                           _ptr(slot_map), ctypes.byref(rs), _ptr(out), dtype_code(out.dtype),
+                                           _stream(stream)))
     return out
 
 

@@ -373,6 +373,27 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
                             workspace, workspace_bytes, stream);
 }
 
+gdn_status gdn_replay_decode_noalloc(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
+                                     const void* v, gdn_dtype in_dtype, const gdn_gates* gates, const gdn_pool* ckpt,
+                                     const int32_t* slot_map, const gdn_ring* ring, void* out, gdn_dtype out_dtype,
+                                     void* stream) {
+  GDN_TRY(check_dims(dims));
+  GDN_REQUIRE(B >= 0, GDN_EINVAL, "B=%d must be >= 0", B);
+  GDN_REQUIRE(T >= 1, GDN_EINVAL, "window T=%d must be >= 1", T);
+  if (B == 0) return replay_decode_impl(dims, B, T, q, k, v, in_dtype, gates, ckpt, nullptr, slot_map, ring, out,
+                                        out_dtype, nullptr, 0, stream);
+  const size_t need = gdn_replay_workspace_bytes(dims, B, T);
+  GDN_REQUIRE(need <= gdn::kReplayScratchBytes, GDN_EUNSUPPORTED,
+              "B=%d x Hv=%d x T=%d at dv=%d needs %zu bytes of workspace; the fixed scratch holds %zu "
+              "(use gdn_replay_decode with a caller workspace)",
+              B, dims->num_v_heads, T, dims->dv, need, gdn::kReplayScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = gdn::replay_scratch(&ws);
+  if (e != hipSuccess) return fail(GDN_ELAUNCH, "device scratch lookup failed: %s", hipGetErrorString(e));
+  return replay_decode_impl(dims, B, T, q, k, v, in_dtype, gates, ckpt, nullptr, slot_map, ring, out, out_dtype, ws,
+                            gdn::kReplayScratchBytes, stream);
+}
+
 gdn_status gdn_replay_decode_dual(const gdn_dims* dims, int32_t B, int32_t T, const void* q, const void* k,
                                   const void* v, gdn_dtype in_dtype, const gdn_gates* gates,
                                   const gdn_pool* master, const gdn_pool* read_copy, const int32_t* slot_map,

@@ -138,6 +138,14 @@ constexpr size_t kMaxLds = 65536;
 // (sequence, value head, window position).
 size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D);
 
+// Fixed device scratch that gdn_replay_decode_noalloc uses in place of a caller
+// workspace: one array per GPU the library runs on, kept until the process
+// ends.  kReplayScratchBytes holds the workspace of 512 rows x 32 value heads
+// x 5-token windows at head dim 128 (81.25 MiB).  replay_scratch() returns its
+// device address on the current device, looked up once per device.
+constexpr size_t kReplayScratchBytes = (size_t)96 << 20;
+hipError_t replay_scratch(void** ptr);
+
 // Workspace of the chunked prefill: per (chunk slot, value head) the inverse
 // T, the causal decay-weighted Q K^T, gamma and beta of one chunk.
 size_t prefill_workspace_bytes(int N, int64_t total, int Hv);

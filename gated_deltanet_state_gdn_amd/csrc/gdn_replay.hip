@@ -24,6 +24,9 @@
 // <= 0).  The c are one small back substitution over the Gram matrix of the
 // live keys and their products with q, so a window position costs
 // O(n (dk + dv)) plus O(n^2) scalars and S_n itself is never materialised.
+#include <map>
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -68,6 +71,31 @@ size_t replay_vectors_bytes(int64_t B, int Hv, int T, int D) {
 }
 size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D) {
   return replay_vectors_bytes(B, Hv, T, D) + (size_t)B * (size_t)Hv * 4 * sizeof(int32_t);
+}
+
+// The no-allocation variant's workspace.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address hipGetSymbolAddress
+// returns for the current device may reach a kernel.  Every call on one GPU
+// shares its copy; nothing in it is read before the same call writes it.
+static __device__ __align__(256) unsigned char scratch[kReplayScratchBytes];
+
+hipError_t replay_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of that device's copy
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 struct RingPos {

@@ -26,7 +26,8 @@
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
  *     struct arguments themselves live in host memory and are read during
  *     the call only.  The caller allocates and owns every buffer; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls (the one
+ *     exception is the fixed device scratch of gdn_replay_decode_noalloc).
  *   - Calls only validate and enqueue work on `stream` (a hipStream_t; NULL
  *     is the default stream).  They return before the work runs.
  *   - Tensors are dense and row-major with the last dimension fastest.
@@ -211,6 +212,24 @@ gdn_status gdn_replay_decode(const gdn_dims* dims, int32_t B, int32_t T, const v
                              const int32_t* slot_map, const gdn_ring* ring, void* out,
                              gdn_dtype out_dtype, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* gdn_replay_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a fixed device array
+ * inside the library, one per GPU, 96 MiB, held from the first call on that
+ * GPU until the process ends; the call itself allocates nothing.  Arguments,
+ * results and errors are those of gdn_replay_decode, plus GDN_EUNSUPPORTED
+ * when gdn_replay_workspace_bytes(dims, B, T) exceeds 96 MiB (B * Hv * T <=
+ * 96,790 at dv = 128, e.g. 512 rows x 32 value heads x 5-token windows), and
+ * GDN_ELAUNCH if the array's device address cannot be obtained.  Every call on
+ * one GPU uses the same array: calls that overlap on one GPU (on different
+ * streams, or from different threads without ordering) race and give
+ * undefined results. */
+gdn_status gdn_replay_decode_noalloc(const gdn_dims* dims, int32_t B, int32_t T, const void* q,
+                                     const void* k, const void* v, gdn_dtype in_dtype,
+                                     const gdn_gates* gates, const gdn_pool* ckpt,
+                                     const int32_t* slot_map, const gdn_ring* ring, void* out,
+                                     gdn_dtype out_dtype, void* stream);
 
 /* Fold every committed ring entry of the mapped slots into their checkpoints
  * (one rounding each) and empty their rings.  After it, the checkpoint is the

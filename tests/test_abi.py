@@ -253,3 +253,19 @@ def test_replay_dual_validation(L):
     assert dec(B=0) == gdn.GDN_OK
     st = L.gdn_replay_flush_dual(ctypes.byref(dims), 4, ctypes.byref(master), None, FAKE, ctypes.byref(ring), None)
     assert st == gdn.GDN_EINVAL
+
+
+def test_replay_noalloc_validation(L):
+    """The fixed-scratch replay step rejects a workspace beyond its 96 MiB before any device call
+    (B = 1024 x 32 value heads x T = 5 at dv = 128 needs 162.5 MiB), and a B = 0 call is a no-op."""
+    dims = _dims()
+    ring, pool = _ring(), _pool()
+
+    def call(B, T):
+        return L.gdn_replay_decode_noalloc(ctypes.byref(dims), B, T, FAKE, FAKE, FAKE, gdn.GDN_BF16,
+                                           ctypes.byref(_gates()), ctypes.byref(pool), FAKE, ctypes.byref(ring),
+                                           FAKE, gdn.GDN_F32, None)
+    assert call(1024, 5) == gdn.GDN_EUNSUPPORTED
+    assert "fixed scratch" in gdn.gdn_last_error()
+    assert call(0, 5) == gdn.GDN_OK
+    assert call(4, 0) == gdn.GDN_EINVAL
