@@ -179,13 +179,14 @@ def _pool(pool):
 
 @dataclass
 class Ring:
-    """Per (slot, value head) ring of ReplaySSM inputs (layout of gdn_ring; keys once per key head)."""
+    """ReplaySSM ring of inputs per slot (layout of gdn_ring; keys once per key head, one pointer pair
+    per slot)."""
     k: object      # [num_slots, Hk, L, dk]
     v: object      # [num_slots, Hv, L, dv]
     g: object      # [num_slots, Hv, L] float32
     beta: object   # [num_slots, Hv, L] float32
-    start: object  # [num_slots, Hv] int32
-    count: object  # [num_slots, Hv] int32
+    start: object  # [num_slots] int32
+    count: object  # [num_slots] int32
 
     @property
     def L(self) -> int:
@@ -201,7 +202,7 @@ def new_ring(num_slots, Hk, Hv, L, dk, dv, dtype, device) -> Ring:
     z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
     return Ring(k=z((num_slots, Hk, L, dk), dtype), v=z((num_slots, Hv, L, dv), dtype),
                 g=z((num_slots, Hv, L), torch.float32), beta=z((num_slots, Hv, L), torch.float32),
-                start=z((num_slots, Hv), torch.int32), count=z((num_slots, Hv), torch.int32))
+                start=z((num_slots,), torch.int32), count=z((num_slots,), torch.int32))
 
 
 # ------------------------------------------------------------------ entry points

@@ -102,11 +102,18 @@ struct RingPos {
   int st, cnt;
 };
 
-// Ring pointers are clamped into range so that a corrupted pointer pair cannot
-// send an access outside the unit's entries.
-__device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t unit) {
+// Ring pointers are kept per slot: every value head of a slot takes the same
+// windows, folds and rollbacks, so one pair serves them all, and the heads
+// cannot disagree about where the entries they share (the keys) sit.  They are
+// clamped into range so that a corrupted pair cannot send an access outside
+// the slot's entries.  Within a step no kernel writes a pair that another
+// kernel of the same step reads: the fold's check records each unit's pointers
+// after any fold, the prep reads only those records and the first value head's
+// prep writes the slot's new pair; a flush moves the pairs in a kernel of its
+// own after the fold.
+__device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t slot) {
   const int L = R.L;
-  int st = R.start[unit], cnt = R.count[unit];
+  int st = R.start[slot], cnt = R.count[slot];
   st = ((st % L) + L) % L;
   cnt = cnt < 0 ? 0 : (cnt > L ? L : cnt);
   return RingPos{st, cnt};
@@ -174,7 +181,7 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
         const int slot = p.slot_map[b];
         int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          const RingPos rp = ring_pos(R, slot);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
           rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
@@ -190,7 +197,7 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
       const int x = s_list[f];
       const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
       const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, unit);
+      const RingPos rp = ring_pos(R, p.slot_map[b]);
       const int st = rp.st, cnt = rp.cnt;
 
       // the lane offset is made opaque per unit so that the per-pass addresses
@@ -266,10 +273,6 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
 #pragma unroll
         for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * NW * RPW * D, s[pp]);
       }
-      if (tid == 0) {
-        R.start[unit] = (st + cnt) % L;
-        R.count[unit] = 0;
-      }
       __syncthreads();  // LDS staging is reused by the next unit
     }
     __syncthreads();  // s_list is rewritten by the next check
@@ -325,7 +328,7 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
         const int slot = p.slot_map[b];
         int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          const RingPos rp = ring_pos(R, slot);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
           rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
@@ -341,7 +344,7 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
       const int x = s_list[f];
       const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
       const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, unit);
+      const RingPos rp = ring_pos(R, p.slot_map[b]);
       const int st = rp.st, cnt = rp.cnt;
 
       // the lane offset is made opaque per unit so that the per-pass addresses
@@ -439,10 +442,6 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
 #pragma unroll
         for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * RS * D, s[pp]);
       }
-      if (tid == 0) {
-        R.start[unit] = (st + cnt) % L;
-        R.count[unit] = 0;
-      }
       __syncthreads();  // LDS staging is reused by the next unit
     }
     __syncthreads();  // s_list is rewritten by the next check
@@ -530,7 +529,7 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
         const int slot = p.slot_map[b];
         int4 rc = {-1, 0, 0, 0};
         if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, (int64_t)slot * p.Hv + h);
+          const RingPos rp = ring_pos(R, slot);
           need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
           rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
         }
@@ -546,7 +545,7 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
       const int x = s_list[f];
       const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
       const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, unit);
+      const RingPos rp = ring_pos(R, p.slot_map[b]);
       const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
 
       // ---- the checkpoint tile in the accumulator layout (lane offset made
@@ -722,10 +721,6 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
             for (int r = 0; r < 4; ++r)
               st_state(rs_copy, coff, ((16 * I + r) * D + 16 * jj) * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
       }
-      if (tid == 0) {
-        R.start[unit] = (st + cnt) % L;
-        R.count[unit] = 0;
-      }
       __syncthreads();  // LDS staging is reused by the next unit
     }
     __syncthreads();  // s_list is rewritten by the next check
@@ -814,8 +809,10 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
   auto win_v = [&](int t) { return vin + (((int64_t)b * T + t) * p.Hv + h) * D * EB; };
   auto win_q = [&](int t) { return qin + (((int64_t)b * T + t) * p.Hk + hk) * D * EB; };
 
-  // ---- load round 1: the slot, the first window rows and the window gate inputs
-  const int slot = p.slot_map[b];
+  // ---- load round 1: the unit record (slot and the ring pointers after any fold,
+  // written by the fold's check), the first window rows and the window gate inputs
+  const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
+  const int slot = rc.x;
   u32x4 wk[NR], wv[NR], wq[NR];
   load_batch(0, T, win_k, wk);
   load_batch(0, T, win_v, wv);
@@ -826,15 +823,14 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
     ga = load_elem(p.a, gi, p.in_dt);
     gb = load_elem(p.b, gi, p.in_dt);
   }
-  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded row (the stream kernel writes zeros)
+  if (slot < 0) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
 
-  // ---- load round 2: the unit's ring pointers, then its live entries (committed,
-  // in ring order from the start pointer) and their gates
+  // ---- load round 2: the unit's live entries (committed, in ring order from the
+  // start pointer) and their gates
   const int64_t ring_e = unit * L;
-  const RingPos rp = ring_pos(R, unit);
-  const int st = rp.st;
-  const int cnt = min(rp.cnt, L - T);  // the fold kernel left room for the window
+  const int st = rc.y;                 // in [0, L)
+  const int cnt = min(rc.z, L - T);    // the fold kernel left room for the window
   const int n_all = cnt + T;           // <= L
   const int64_t kring_e = ring_key_base(p, slot, h, L);
   const char* rk = static_cast<const char*>(R.k) + kring_e * D * EB;
@@ -920,9 +916,9 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
     R.g[j] = wg;
     R.beta[j] = wbeta;
   }
-  if (tid == 0) {
-    R.start[unit] = st;
-    R.count[unit] = n_all;
+  if (tid == 0 && h == 0) {  // the slot's pointers, once per slot
+    R.start[slot] = st;
+    R.count[slot] = n_all;
   }
 
   // ---- decay-weighted key products s_F[i][j] = e^{G_i - G_j} k_j . k_i (j < i)
@@ -1148,9 +1144,9 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
       else *reinterpret_cast<uint16_t*>(row) = (uint16_t)vr[j];
     }
   }
-  if (lane == 0) {
-    R.start[unit] = st;
-    R.count[unit] = n_all;
+  if (lane == 0 && h == 0) {  // the slot's pointers, once per slot
+    R.start[slot] = st;
+    R.count[slot] = n_all;
   }
 
   // ---- K K^T and K Q^T; element r of lane (e, g) is row 4 g + r, column e
@@ -1443,18 +1439,29 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
 
 // ---------------------------------------------------------------- rollback
 __global__ void gdn_replay_rollback_kernel(const ReplayArgs P) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
   const DecodeArgs& p = P.d;
-  if (i >= (int64_t)p.B * p.Hv) return;
-  const int b = (int)(i / p.Hv);
-  const int h = (int)(i - (int64_t)b * p.Hv);
+  if (b >= p.B) return;
   const int slot = p.slot_map[b];
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;
   int r = P.num_rejected[b];
   r = r < 0 ? 0 : r;
-  int32_t* cnt = P.ring.count + (int64_t)slot * p.Hv + h;
+  int32_t* cnt = P.ring.count + slot;
   const int c = *cnt - r;
   *cnt = c < 0 ? 0 : c;
+}
+
+// After a flush's fold: every mapped slot's ring is empty, its start moved past
+// the folded entries (one thread per row).
+__global__ void gdn_replay_advance_kernel(const ReplayArgs P) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const DecodeArgs& p = P.d;
+  if (b >= p.B) return;
+  const int slot = p.slot_map[b];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) return;
+  const RingPos rp = ring_pos(P.ring, slot);
+  P.ring.start[slot] = (rp.st + rp.cnt) % P.ring.L;
+  P.ring.count[slot] = 0;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1565,12 +1572,14 @@ static hipError_t launch_replay_t(const ReplayArgs& a0, float* ws, hipStream_t s
   const bool f32_in = a0.d.in_dt == GDN_F32;
   ReplayArgs a = a0;
   a.rec = nullptr;
-  if constexpr (D == 64 || D == 128) {
-    if (!f32_in && a.ring.L <= 16 && a.T > 0 && ws != nullptr)  // the one-wave prep reads unit records
-      a.rec = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + replay_vectors_bytes(a.d.B, a.d.Hv, a.T, D));
-  }
+  if (a.T > 0)  // the preps read the unit records the fold's check writes
+    a.rec = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + replay_vectors_bytes(a.d.B, a.d.Hv, a.T, D));
   hipError_t e = f32_in ? launch_fold_any<SDT, D, 4>(a, s) : launch_fold_any<SDT, D, 2>(a, s);
-  if (e != hipSuccess || a.T == 0) return e;
+  if (e != hipSuccess) return e;
+  if (a.T == 0) {  // flush: the slots' pointers move once every head has folded
+    hipLaunchKernelGGL(gdn_replay_advance_kernel, dim3((unsigned)((a.d.B + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   constexpr int NWP = GDN_REPLAY_PREP_WAVES;
   if constexpr (D == 64 || D == 128) {
@@ -1627,8 +1636,7 @@ hipError_t launch_replay_flush(const ReplayArgs& a, int state_dt, int D, hipStre
 
 hipError_t launch_replay_rollback(const ReplayArgs& a, hipStream_t s) {
   if (a.d.B == 0) return hipSuccess;
-  const int64_t n = (int64_t)a.d.B * a.d.Hv;
-  const unsigned grid = (unsigned)((n + 255) / 256);
+  const unsigned grid = (unsigned)((a.d.B + 255) / 256);
   hipLaunchKernelGGL(gdn_replay_rollback_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -88,19 +88,20 @@ typedef struct {
   int64_t num_slots;
 } gdn_pool;
 
-/* ReplaySSM ring, one per (slot, value head), caller-allocated and separate
- * from the checkpoint pool:
+/* ReplaySSM ring of a slot, caller-allocated and separate from the checkpoint
+ * pool:
  *   k    [num_slots, Hk, L, dk]  copies of the keys, in `dtype`, once per key head
  *   v    [num_slots, Hv, L, dv]  copies of the values, in `dtype`
  *   g    [num_slots, Hv, L]      float32 log-decays
  *   beta [num_slots, Hv, L]      float32 write strengths
- *   start, count [num_slots, Hv] int32; live entry i (0 <= i < count) sits at
- *                                ring index (start + i) mod L.
+ *   start, count [num_slots]     int32, one pair per slot for all its heads;
+ *                                live entry i (0 <= i < count) of every head
+ *                                sits at ring index (start + i) mod L.
  * q is never stored.  Before first use, start and count must be zero (or any
- * 0 <= start < L, 0 <= count <= L, equal over the value heads of each key
- * head).  The value heads of a key head share its key entries: the entry
- * points advance their pointers together (every head of a row takes the same
- * window, fold and rollback), and the first of them appends the keys. */
+ * 0 <= start < L, 0 <= count <= L).  Every head of a slot takes the same
+ * windows, folds and rollbacks, so one pointer pair serves them all and the
+ * value heads of a key head find its shared key entries where they wrote
+ * them. */
 typedef struct {
   void* k;
   void* v;
@@ -196,8 +197,8 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
  *          written (it carries per-unit vectors and ring-pointer records
  *          between the kernels of one call); calls that share a workspace
  *          must not overlap.
- * Per (sequence, value head): if count + T > L, every committed entry is
- * first folded into the checkpoint (one rounding) and the ring emptied
+ * Per sequence: if count + T > L, every committed entry of each value head is
+ * first folded into that head's checkpoint (one rounding) and the ring emptied
  * (start += count mod L, count = 0); then the T new entries are appended at
  * ring indices (start + count + t) mod L and count += T; window position t
  * outputs scale * S_t^T q_t where S_t is the checkpoint advanced over the
@@ -259,9 +260,9 @@ gdn_status gdn_replay_flush_dual(const gdn_dims* dims, int32_t B, const gdn_pool
                                  const gdn_pool* read_copy, const int32_t* slot_map,
                                  const gdn_ring* ring, void* stream);
 
-/* Drop the last num_rejected[b] live entries of row b's slot, for every value
- * head: count <- max(count - r, 0) (the pointer move that replaces a state
- * rollback).  num_rejected: device int32 [B], each >= 0. */
+/* Drop the last num_rejected[b] live entries of row b's slot (all its heads):
+ * count <- max(count - r, 0), the pointer move that replaces a state
+ * rollback.  num_rejected: device int32 [B]; a negative entry counts as 0. */
 gdn_status gdn_replay_rollback(const gdn_dims* dims, int32_t B, const int32_t* slot_map,
                                const int32_t* num_rejected, const gdn_ring* ring, void* stream);
 
