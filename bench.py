@@ -71,6 +71,13 @@ def replay_step_bytes(B, sdt, n_before, T, L, ib=2, ob=2, Hk=HK, Hv=HV, d=D, cop
     return state + entries + appended + inputs + B * T * Hv * d * ob
 
 
+def replay_rows_step_bytes(counts, sdt, T, L, copy_dt=None):
+    """replay_step_bytes for rows that hold different numbers of entries (the gate parameters,
+    read once per step, are counted once)."""
+    head = 2 * HV * 4
+    return head + sum(replay_step_bytes(1, sdt, int(n), T, L, copy_dt=copy_dt) - head for n in counts)
+
+
 def spec_bytes(B, sdt, T, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
     """Algorithmic bytes of one speculative window that keeps every state: the source read once, T
     destination states written, inputs, gates, slot tables and outputs."""
@@ -86,12 +93,34 @@ def prefill_bytes(lengths, sdt, ib=2, ob=2, Hk=HK, Hv=HV, d=D):
 
 
 def prefill_flops(lengths, Hv=HV, d=D, C=64):
-    """FLOPs of the chunked form as computed: per (chunk, value head) K K^T, Q K^T, T R and P U
-    (2 C^2 d each) and [K; Q] S, K~^T U (2 C d^2 each, three)."""
+    """FLOPs of the chunked form as this library computes it: per (chunk, value head) K K^T, Q K^T,
+    T R and P U (2 C^2 d each) and [K; Q] S, K~^T U (2 C d^2 each, three).  U = T R with
+    R = diag(beta)(V - diag(e^gamma) K S) replaces W = T diag(beta e^gamma) K, W S and
+    U' = T diag(beta) V, one C^2 d product fewer than the textbook count below."""
     chunks = sum((n + C - 1) // C for n in lengths)
     per = 4 * 2 * C * C * d + 3 * 2 * C * d * d
     state_kernel = 2 * 2 * C * C * d + 3 * 2 * C * d * d
     return chunks * Hv * per, chunks * Hv * state_kernel
+
+
+def prefill_flops_method(lengths, Hv=HV, d=D, C=64):
+    """The method's chunked-form work per token and value head: K K^T, the two WY factors
+    W = T diag(beta e^gamma) K and U' = T diag(beta) V, Q K^T and (M o Q K^T) U (2 C d each per
+    token), W S, Q S and K~^T U (2 d^2 each), and the triangular inverse (C^2 / 3): 181.6 kFLOP
+    per token per value head at C = 64, d = 128."""
+    return sum(lengths) * Hv * (5 * 2 * C * d + 3 * 2 * d * d + C * C // 3)
+
+
+def counters_for(key, sources):
+    """The whole counter record (traffic and MFMA counters) if taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC) as f:
+            t = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha256") != kernel_sources_sha(sources):
+        return None
+    return t
 
 
 # ------------------------------------------------------------------ timing helpers
@@ -192,9 +221,13 @@ def bench_decode(torch, gdn, gen, B, sdt, steps, warmup, cid=1):
     return res
 
 
-def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None):
+def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None, staggered=False):
     """Aligned rings (every sequence starts empty): 1 untimed cycle, then `cycles` timed cycles.
-    copy_dt selects the dual-precision checkpoint (sdt is then the f32 master)."""
+    copy_dt selects the dual-precision checkpoint (sdt is then the f32 master).  staggered: the
+    steady serving layout; L one-token steps fill every ring, then a seeded rollback of 0..L-1
+    entries per row leaves the rows' counts spread over 1..L, so each step folds about 1/L of the
+    rows (untimed setup, then the same warm-up and timed cycles)."""
+    import numpy as np
     dev = "cuda"
     steps_per_cycle = L // T if T > 1 else L
     slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
@@ -217,24 +250,37 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None):
     ws = torch.empty(gdn.gdn_replay_workspace_bytes(HK, HV, D, D, B, T), dtype=torch.uint8, device=dev)
     warm = steps_per_cycle
     n = cycles * steps_per_cycle
+    cnt = np.zeros(B, np.int64)  # every row's committed entries before the next step
 
     def fn(i):
         q, k, v, a, b = ins[i % n_in]
         gdn.gdn_replay_decode(q, k, v, a, b, A_d, dt_d, ckpt, sm, ring, out=out, workspace=ws, read_copy=copy)
 
+    if staggered:
+        for i in range(L):  # fill every ring with one-token steps
+            q, k, v, a, b = ins[i % n_in]
+            gdn.gdn_replay_decode(q[:, :1].contiguous(), k[:, :1].contiguous(), v[:, :1].contiguous(),
+                                  a[:, :1].contiguous(), b[:, :1].contiguous(), A_d, dt_d, ckpt, sm, ring,
+                                  out=out[:, :1].contiguous(), workspace=ws, read_copy=copy)
+        r = gen.rejected_counts(cid, 0, B, L - 1)
+        gdn.gdn_replay_rollback(sm, torch.from_numpy(r).to(dev), ring, HK, D)
+        torch.cuda.synchronize()
+        cnt = L - r.astype(np.int64)
+        got = ring.count[torch.from_numpy(slot_map.astype(np.int64)).to(dev)].cpu().numpy()
+        assert np.array_equal(got, cnt), "staggered ring counts"
     t = timed_launches(torch, fn, n, warm)
-    # byte model follows the (deterministic) per-slot count of the aligned schedule
-    cnt, nbytes = 0, 0
+    # byte model follows the (deterministic) per-row counts of the schedule
+    nbytes = 0
     for i in range(warm + n):
-        b_i = replay_step_bytes(B, sdt, cnt, T, L, copy_dt=copy_dt)
-        if cnt + T > L:
-            cnt = 0
-        cnt += T
+        b_i = replay_rows_step_bytes(cnt, sdt, T, L, copy_dt=copy_dt)
+        cnt = np.where(cnt + T > L, 0, cnt) + T
         if i >= warm:
             nbytes += b_i
     ms = t["span_ms"] / n
     res = {
         "B": B, "ckpt": sdt if copy_dt is None else f"{sdt} master + {copy_dt} read copy", "L": L, "T": T,
+        "rings": "staggered (counts spread over 1..L by a seeded rollback after a full ring)" if staggered
+                 else "aligned (every row starts empty)",
         "ms_per_step": round(ms, 5),
         "mean_launch_us": round(t["mean_launch_ms"] * 1e3, 2),
         "GB_per_s": round(nbytes / n / (ms * 1e-3) / 1e9, 1), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
@@ -243,6 +289,7 @@ def bench_replay(torch, gdn, gen, B, sdt, T, cycles, L=16, cid=4, copy_dt=None):
     }
     src = ["gdn_replay.hip", "gdn_device.h"]
     key = f"replay_{sdt}_B{B}_T{T}" if copy_dt is None else f"replay_dual_{copy_dt}_B{B}_T{T}"
+    key += "_staggered" if staggered else ""
     res["roofline"] = roofline_bw(nbytes / n, t["mean_launch_ms"], traffic_for(key, src))
     del ckpt, ring, ins, ws, copy
     torch.cuda.empty_cache()
@@ -313,18 +360,28 @@ def bench_prefill(torch, gdn, gen, sdt, reps, cid=3):
 
     t = timed_launches(torch, fn, reps, 2)
     nbytes = prefill_bytes(lengths, sdt)
-    flops, flops_state = prefill_flops(lengths)
+    flops_lib, flops_state = prefill_flops(lengths)
+    flops = prefill_flops_method(lengths)
     ms = t["span_ms"] / reps
     tf = flops / (ms * 1e-3) / 1e12
+    rec = counters_for(f"prefill_{sdt}", ["gdn_prefill.hip", "gdn_device.h"])
     res = {
         "lengths": lengths, "state": sdt, "ms_per_call": round(ms, 4), "tokens_per_s": round(sum(lengths) / (ms * 1e-3)),
         "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes, "flops_per_call": flops,
+        "flops_as_computed": flops_lib,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(tf / FP32_MFMA_PEAK_TFS, 4), "traffic": None,
-                     "scope": "whole call (chunk kernel + state kernel); fp32-accurate products, those with a key or "
-                              "query operand run as three-term bf16 splits; against the fp32 MFMA peak"},
+                     "frac": round(tf / FP32_MFMA_PEAK_TFS, 4), "traffic": rec["bytes_per_launch"] if rec else None,
+                     "scope": "whole call (chunk kernel + state kernel); the method's chunked-form FLOPs "
+                              "(181.6 kFLOP per token per value head); fp32-accurate products, those with a key "
+                              "or query operand run as three-term bf16 splits; against the fp32 MFMA peak"},
         "workspace_MiB": round(ws.numel() / 2 ** 20, 1),
     }
+    if rec and "mfma" in rec:
+        m = rec["mfma"]
+        # time the issued MFMA instructions would take at their own peaks, against the measured call
+        at_peak_us = (m["bf16_flops"] / 2.5e15 + m["f32_flops"] / (FP32_MFMA_PEAK_TFS * 1e12)) * 1e6
+        res["mfma_counters"] = dict(m, issued_mix_at_peak_us=round(at_peak_us, 1),
+                                    issued_mix_utilisation=round(at_peak_us / (ms * 1e3), 4))
     del pool, ws, out, args
     torch.cuda.empty_cache()
     return res
@@ -444,35 +501,114 @@ def bench_copy(torch, nbytes=1 << 30, reps=4):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(gen, seconds=12.0):
-    """The CPU oracle on a bounded sample of the headline workload, one thread."""
+# The plain oracle (float64 numpy, token by token) on the host cores, in four legs: the headline
+# decode layer (fp32 state), the same layer with a bf16 state, the chunked-prefill workload and
+# one 16-step replay cycle.  Each leg is a bounded sample of its workload, split over a pool of
+# worker processes (one BLAS thread each).  Inputs are generated once in the parent; the pool is
+# forked after that and before the GPU is first touched, so the workers share the inputs
+# copy-on-write and never hold a GPU context.
+CPU_MAX_WORKERS = 16           # the host share of one GPU on the benchmark boxes
+_CPU = {}                      # leg inputs, inherited by the forked workers
+
+
+def _cpu_worker_init():
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:  # pragma: no cover - threadpoolctl is present in this image
-        limiter = None
+        pass
+
+
+def _cpu_task(task):
+    """One share of a leg; returns the oracle's compute seconds."""
+    import numpy as np
     import oracle as O
-    B, cid = 256, 1
-    slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
-    A_log, dt_bias = gen.head_params(cid, HV)
-    rows, done, elapsed, step = 64, 0, 0.0, 0
-    pool = gen.pool_slots(cid, slot_map[:rows], HV, D, D, "f32")
-    local = list(range(rows))
-    while elapsed < seconds and step < 64:
-        inp = gen.token_inputs(cid, step, (B,), HK, HV, D, D, "bf16")
-        sub = {k: v[:rows] for k, v in inp.items()}
+    kind, idx = task
+    d = _CPU[kind]
+    t0 = time.perf_counter()
+    if kind.startswith("decode"):
+        rows = d["shares"][idx]
+        pool = d["states"][rows]
+        local = np.arange(len(rows))
+        for inp in d["inputs"]:
+            pool, _ = O.decode_step(pool, local, *(inp[x][rows] for x in "qkvab"), d["A_log"], d["dt_bias"])
+    elif kind == "prefill":
+        n, heads = d["shares"][idx]
+        lo, hi = int(d["cu"][n]), int(d["cu"][n + 1])
+        inp = {x: d["inputs"][x][lo:hi] for x in "qkvab"}
+        O.chunk_prefill(d["states"][n:n + 1], [0], [0, hi - lo], *(inp[x] for x in "qkvab"), d["A_log"],
+                        d["dt_bias"], heads=heads)
+    elif kind == "replay":
+        rows = d["shares"][idx]
+        ck = d["states"][rows]
+        ring = O.new_ring(len(rows), HV, d["L"], D, D)
+        local = np.arange(len(rows))
+        for inp in d["inputs"]:
+            ck, ring, _ = O.replay_decode(ck, ring, local, *(inp[x][rows] for x in "qkvab"), d["A_log"],
+                                          d["dt_bias"])
+    return time.perf_counter() - t0
+
+
+def cpu_prepare(gen, cores):
+    """Generate the inputs of the four legs (before the worker pool is forked)."""
+    import numpy as np
+    B, steps = 256, 8
+    for kind, sdt, cid in (("decode_f32", "f32", 1), ("decode_bf16", "bf16", 2)):
+        slot_map = gen.slot_permutation(cid, NUM_SLOTS)[:B]
+        A_log, dt_bias = gen.head_params(cid, HV)
+        _CPU[kind] = dict(states=gen.pool_slots(cid, slot_map, HV, D, D, sdt), A_log=A_log, dt_bias=dt_bias,
+                          inputs=[gen.token_inputs(cid, s, (B,), HK, HV, D, D, "bf16") for s in range(steps)],
+                          shares=np.array_split(np.arange(B), cores), B=B, steps=steps, sdt=sdt)
+    lengths = gen.WORKLOADS["prefill"].extra["lengths"]
+    cu = gen.seq_lengths_cu(lengths)
+    slot_map = gen.slot_permutation(3, 16)[:len(lengths)]
+    A_log, dt_bias = gen.head_params(3, HV)
+    # sample: all 32 heads of the 1024- and 3000-token sequences (one share per (sequence, 4 heads))
+    shares = [(n, list(range(h, h + 4))) for n in (0, 1) for h in range(0, HV, 4)]
+    _CPU["prefill"] = dict(states=gen.pool_slots(3, slot_map, HV, D, D, "f32"), A_log=A_log, dt_bias=dt_bias,
+                           inputs=gen.token_inputs(3, 0, (int(cu[-1]),), HK, HV, D, D, "bf16"), cu=cu,
+                           shares=shares, head_tokens=sum(4 * lengths[n] for n, _ in shares), lengths=lengths)
+    Br, L = 32, 16
+    slot_map = gen.slot_permutation(4, NUM_SLOTS)[:Br]
+    A_log, dt_bias = gen.head_params(4, HV)
+    _CPU["replay"] = dict(states=gen.pool_slots(4, slot_map, HV, D, D, "f32"), A_log=A_log, dt_bias=dt_bias,
+                          inputs=[gen.token_inputs(4, s, (Br, 1), HK, HV, D, D, "bf16") for s in range(L)],
+                          shares=np.array_split(np.arange(Br), cores), B=Br, L=L)
+
+
+def cpu_baseline(pool, cores):
+    """Time the four legs on the worker pool; tokens/s and GB/s use the GPU rows' byte models."""
+    legs = {}
+    for kind in ("decode_f32", "decode_bf16", "prefill", "replay"):
+        d = _CPU[kind]
+        tasks = [(kind, i) for i in range(len(d["shares"]))]
         t0 = time.perf_counter()
-        pool, _ = O.decode_step(pool, local, sub["q"], sub["k"], sub["v"], sub["a"], sub["b"], A_log, dt_bias)
-        elapsed += time.perf_counter() - t0
-        done += rows
-        step += 1
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    tok_s = done / elapsed
-    return {"value": round(tok_s * decode_bytes(1, "f32") / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_s": round(tok_s, 1),
-            "sample": f"{rows} sequences x 32 value heads x {step} decode steps of the B=256 fp32-state layer "
-                      f"({elapsed:.1f} s of oracle compute, float64 numpy, one thread)"}
+        busy = sum(pool.map(_cpu_task, tasks, chunksize=1))
+        wall = time.perf_counter() - t0
+        if kind.startswith("decode"):
+            tok = d["B"] * d["steps"] / wall
+            legs[kind] = {"tokens_per_s": round(tok, 1), "GB_per_s": round(tok * decode_bytes(1, d["sdt"]) / 1e9, 4),
+                          "sample": f"B={d['B']} rows x 32 value heads x {d['steps']} decode steps, "
+                                    f"{d['sdt']} state", "wall_s": round(wall, 2), "busy_s": round(busy, 1)}
+        elif kind == "prefill":
+            tok = d["head_tokens"] / HV / wall  # whole-layer tokens (all 32 heads) per second
+            per_tok = prefill_bytes(d["lengths"], "f32") / sum(d["lengths"])
+            legs[kind] = {"tokens_per_s": round(tok, 1), "GB_per_s": round(tok * per_tok / 1e9, 4),
+                          "sample": "every value head of the 1024- and 3000-token sequences of the 4-sequence "
+                                    "workload, one call, fp32 state", "wall_s": round(wall, 2),
+                          "busy_s": round(busy, 1)}
+        else:
+            L = d["L"]
+            cyc = sum(replay_step_bytes(1, "f32", n, 1, L) for n in range(L))  # one row, one 16-step cycle
+            tok = d["B"] * L / wall
+            legs[kind] = {"tokens_per_s": round(tok, 1), "GB_per_s": round(tok * cyc / L / 1e9, 4),
+                          "sample": f"B={d['B']} rows x 32 value heads, one 16-step fold cycle (T=1, L=16), "
+                                    "fp32 checkpoint", "wall_s": round(wall, 2), "busy_s": round(busy, 1)}
+    head = legs["decode_f32"]
+    return {"value": head["GB_per_s"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "tokens_per_s": head["tokens_per_s"],
+            "sample": f"plain oracle (float64 numpy, token by token) on {cores} worker processes, one BLAS thread "
+                      f"each; value: {head['sample']} of the headline layer", "legs": legs}
 
 
 # ------------------------------------------------------------------ main
@@ -481,7 +617,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t> | replay_dual_<dt>_T<t> | "
+    ap.add_argument("--only", default=None, help="comma-separated rows only: decode_<dt>_B<n> | replay_<dt>_T<t>[_staggered] | replay_dual_<dt>_T<t> | "
                                                     "spec_<dt>_T<t> | mamba2_<decode|replay>_<dt>[_T<t>] | prefill_<dt> | blockcopy | copy")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -495,6 +631,14 @@ def main():
     import torch
     import gated_deltanet_state_gdn_amd as gdn
     from workloads import gen
+    cpu_pool = None
+    if not args.no_cpu and not args.only:
+        # before any GPU call: the workers are forked from a process without a GPU context
+        import multiprocessing as mp
+        cores = min(len(os.sched_getaffinity(0)), CPU_MAX_WORKERS)
+        log(f"cpu baseline: generating oracle inputs, {cores} workers")
+        cpu_prepare(gen, cores)
+        cpu_pool = mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -510,7 +654,8 @@ def main():
                 r = bench_replay(torch, gdn, gen, 512, "f32", int(rest[2][1:]) if len(rest) > 2 else 1, 2,
                                  copy_dt=rest[1])
             elif kind == "replay":
-                r = bench_replay(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 1, 2)
+                r = bench_replay(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 1, 2,
+                                 staggered=rest[-1] == "staggered")
             elif kind == "spec":
                 r = bench_spec(torch, gdn, gen, 512, rest[0], int(rest[1][1:]) if len(rest) > 1 else 5,
                                max(args.steps // 4, 4))
@@ -538,6 +683,9 @@ def main():
         for dt, T, cyc in (("f32", 1, 4), ("bf16", 1, 4), ("f32", 5, 8)):
             log(f"row: replay B=512 {dt} checkpoint T={T}")
             rows[f"replay_{dt}_B512_T{T}"] = bench_replay(torch, gdn, gen, 512, dt, T, cyc)
+        for dt in ("f32", "bf16"):
+            log(f"row: replay B=512 {dt} checkpoint T=1, staggered rings")
+            rows[f"replay_{dt}_B512_T1_staggered"] = bench_replay(torch, gdn, gen, 512, dt, 1, 4, staggered=True)
         log("row: replay B=512 fp32 master + bf16 read copy T=1")
         rows["replay_dual_bf16_B512_T1"] = bench_replay(torch, gdn, gen, 512, "f32", 1, 4, copy_dt="bf16")
         for dt in ("f32", "bf16"):
@@ -552,9 +700,11 @@ def main():
             log(f"row: chunked prefill {dt} state")
             rows[f"prefill_{dt}"] = bench_prefill(torch, gdn, gen, dt, 8)
     cpu = None
-    if not args.no_cpu:
-        log("cpu baseline: oracle sample")
-        cpu = cpu_baseline(gen)
+    if cpu_pool is not None:
+        log("cpu baseline: oracle legs")
+        cpu = cpu_baseline(cpu_pool, cores)
+        cpu_pool.close()
+        cpu_pool.join()
 
     ms = head["ms_per_step"]
     line = {
