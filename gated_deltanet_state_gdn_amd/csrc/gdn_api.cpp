@@ -263,7 +263,7 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
               workspace_bytes, need);
   GDN_REQUIRE(need == 0 || (workspace != nullptr && aligned(workspace, 256)), GDN_EINVAL,
               "workspace is NULL or not 256-byte aligned");
-  GDN_REQUIRE(gdn::prefill_chunk_slots_fit(N, total_tokens, dims->num_v_heads), GDN_EINVAL,
+  GDN_REQUIRE(gdn::prefill_chunk_slots_fit(N, total_tokens, dims->num_k_heads, dims->num_v_heads), GDN_EINVAL,
               "N + total_tokens / 64 chunk slots exceed the grid limit");
   gdn::PrefillArgs a{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, state->base, slot_map, cu_seqlens,
                      out, state->num_slots, total_tokens, N, dims->num_k_heads, dims->num_v_heads,

@@ -149,6 +149,6 @@ hipError_t replay_scratch(void** ptr);
 // Workspace of the chunked prefill: per (chunk slot, value head) the inverse
 // T, the causal decay-weighted Q K^T, gamma and beta of one chunk.
 size_t prefill_workspace_bytes(int N, int64_t total, int Hv);
-bool prefill_chunk_slots_fit(int N, int64_t total, int Hv);
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv);
 
 }  // namespace gdn

@@ -49,9 +49,10 @@ size_t prefill_workspace_bytes(int N, int64_t total, int Hv) {
   return (size_t)prefill_chunk_slots(N, total) * (size_t)Hv * kWsFloats * sizeof(float);
 }
 
-bool prefill_chunk_slots_fit(int N, int64_t total, int Hv) {
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv) {
   const int64_t units = ((int64_t)N * Hv + 7) / 8 * 8 * 4;
-  return prefill_chunk_slots(N, total) <= INT32_MAX && Hv <= 65535 && units <= INT32_MAX;
+  const int64_t grouped = ((int64_t)N * Hk + 7) / 8 * 8 * (Hv / Hk) * 4;
+  return prefill_chunk_slots(N, total) <= INT32_MAX && Hv <= 65535 && units <= INT32_MAX && grouped <= INT32_MAX;
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -107,24 +108,29 @@ __device__ __forceinline__ f32x4_t rows_xyt(const uint32_t* X, const uint32_t* Y
 }
 
 // ---------------------------------------------------------------- kernel 1
+// One workgroup per (chunk slot, key head) for its R = Hv / Hk value heads:
+// the key and query rows are loaded and K K^T, Q K^T formed once, then each
+// value head scales them by its own gates and inverts its own (I + A).  The
+// gate inputs of the first two value heads load with the rows, so at R <= 2 the
+// workgroup waits on memory once; further heads load theirs two at a time.
 template <int D, int EB>
 __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
   constexpr int LDT = kC + 4;
   constexpr int LDW = D * EB / 4 + 4;  // words per packed key / query row: 16-byte rows, 4 mod 8 banks
   constexpr int VE = 16 / EB, CPR = D / VE;
+  constexpr int RMAX = 2;              // value heads whose gates are staged at once
   // two buffers: K rows then T, Q rows then A (about 40 KB in all at D = 128,
   // so four work-groups share a CU and cover each other's memory waits)
   constexpr int UW = kC * LDW > kC * LDT ? kC * LDW : kC * LDT;
   __shared__ __align__(16) uint32_t s_u0[UW];
   __shared__ __align__(16) uint32_t s_u1[UW];
   __shared__ float s_M[4][16][17];
-  uint32_t* const s_k = s_u0;
-  uint32_t* const s_q = s_u1;
-  float (*const s_T)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u0);
-  float (*const s_A)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u1);
-  __shared__ float s_g[kC], s_beta[kC], s_gam[kC];
+  uint32_t* const s_k = s_u0;  // then T (below)
+  uint32_t* const s_q = s_u1;  // then A
+  __shared__ float s_g[RMAX][kC], s_beta[RMAX][kC], s_gam[kC];
 
-  const int cs = blockIdx.x, h = blockIdx.y;
+  const int cs = blockIdx.x, hk = blockIdx.y;
+  const int R = p.Hv / p.Hk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int* cu = p.cu_seqlens;
   // largest n with n + cu[n] / C <= cs (the key is strictly increasing in n)
@@ -141,10 +147,9 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded sequence: kernel 2 writes zeros
   const int t0 = seq_lo + c * kC;
   const int len = min(kC, seq_hi - t0);
-  const int hk = h / (p.Hv / p.Hk);
 
-  // keys and queries stay packed in their input dtype, rows >= len zeroed; the
-  // gate inputs are loaded alongside, so the work-group waits on memory once
+  // keys and queries stay packed in their input dtype, rows >= len zeroed; thread
+  // (r, t) = (tid / C, tid mod C) loads the gate inputs of value head hk R + r, token t
   {
     constexpr int IT = (kC * CPR + 255) / 256;
     u32x4 xk[IT], xq[IT];
@@ -160,9 +165,12 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       xk[u] = zk;
       xq[u] = zq;
     }
+    const int gr = tid / kC, gt = tid - gr * kC;
+    const bool gl = gr < RMAX && gr < R;
     float ga = 0.f, gb = 0.f, al = 0.f, db = 0.f;
-    if (tid < kC) {
-      const int64_t gi = (int64_t)(t0 + min(tid, len - 1)) * p.Hv + h;
+    if (gl) {
+      const int h = hk * R + gr;
+      const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + h;
       ga = load_elem(p.a, gi, p.in_dt);
       gb = load_elem(p.b, gi, p.in_dt);
       al = p.A_log[h];
@@ -176,105 +184,125 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
         *reinterpret_cast<u32x4*>(s_q + r * LDW + cc * 4) = xq[u];
       }
     }
-    if (tid < kC) {
-      const bool live = tid < len;
-      s_g[tid] = live ? gate_g(ga, al, db) : 0.f;
-      s_beta[tid] = live ? sigmoid_f(gb) : 0.f;
+    if (gl) {
+      const bool live = gt < len;
+      s_g[gr][gt] = live ? gate_g(ga, al, db) : 0.f;
+      s_beta[gr][gt] = live ? sigmoid_f(gb) : 0.f;
     }
   }
   __syncthreads();
-  if (wave == 0) {  // inclusive prefix sum of g over the chunk
-    float x = s_g[lane];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    s_gam[lane] = x;
-  }
-  __syncthreads();
-
-  float* wsp = ws + ((int64_t)cs * p.Hv + h) * kWsFloats;
-  float* ws_T = wsp;
-  float* ws_P = wsp + kC * kC;
-  // A (strictly lower) and P (causal, to the workspace): 16 tiles each, wave w
-  // takes tile rows I = w.. of both; A stays in registers until Q is no longer read
-  f32x4_t a_t[4];
+  const int lane0 = lane, tid0 = tid;
+  // K K^T and Q K^T tiles (16 of each; wave w takes tile rows I = w..), formed
+  // once for every value head (16-bit rows: the exact bf16 / f16 products, fp32
+  // accumulation); the upper tiles are not needed
+  f32x4_t kt[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int job = wave + 4 * k;
     const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (J <= I)  // X Y^T on MFMA (16-bit rows: the exact bf16 / f16 products, fp32 accumulation)
-      acc = rows_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, s_k + 16 * J * LDW, LDW, p.in_dt, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * I + acc_row(lane, r), s = 16 * J + acc_col(lane);
-      if (isP) {
-        ws_P[t * kC + s] = (s <= t) ? expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
-      } else {
-        a_t[k][r] = (s < t) ? s_beta[t] * expf(s_gam[t] - s_gam[s]) * acc[r] : 0.f;
-      }
-    }
+    kt[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (J <= I) kt[k] = rows_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, s_k + 16 * J * LDW, LDW, p.in_dt, lane);
   }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {  // A into the Q buffer
-    const int job = wave + 4 * k, I = (job >> 2) & 3, J = job & 3;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_A[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = a_t[k][r];
-  }
-  __syncthreads();
 
-  // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, lane = (block, column)
-  if (wave == 0) {
-    const int blk = lane >> 4, j = lane & 15, base = 16 * blk;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-#pragma unroll
-      for (int s = 0; s < i; ++s) x[i] = fmaf(-s_A[base + i][base + s], x[s], x[i]);
+  for (int r = 0; r < R; ++r) {
+    const int h = hk * R + r, rg = r % RMAX;
+    // LDS bases and the thread indices made opaque per head, so the addresses of
+    // the loop body are not hoisted out of it (they would hold a hundred registers)
+    int zoff = 0, lane = lane0, tid = tid0;
+    asm volatile("" : "+v"(zoff), "+v"(lane), "+v"(tid));
+    float (*const s_T)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u0 + zoff);
+    float (*const s_A)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u1 + zoff);
+    __syncthreads();  // the key and query rows are read (first head), s_T is written out (later heads)
+    if (rg == 0 && r > 0) {  // the next heads' gates
+      const int gr = tid / kC, gt = tid - gr * kC;
+      if (gr < RMAX && r + gr < R) {
+        const int hg = h + gr;
+        const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + hg;
+        const float ga = load_elem(p.a, gi, p.in_dt), gb = load_elem(p.b, gi, p.in_dt);
+        const bool live = gt < len;
+        s_g[gr][gt] = live ? gate_g(ga, p.A_log[hg], p.dt_bias[hg]) : 0.f;
+        s_beta[gr][gt] = live ? sigmoid_f(gb) : 0.f;
+      }
+      __syncthreads();
     }
+    if (wave == 0) {  // inclusive prefix sum of this head's g over the chunk
+      float x = s_g[rg][lane];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s_T[base + i][base + j] = x[i];
-  }
-  for (int i = tid; i < kC * kC; i += 256) {  // blocks above the diagonal are zero
-    const int r = i / kC, cc = i - r * kC;
-    if ((cc >> 4) > (r >> 4)) s_T[r][cc] = 0.f;
-  }
-  __syncthreads();
-  // off-diagonal blocks, one level (I - J = lev) at a time:
-  //   T_IJ = -T_II (sum_{k=J}^{I-1} A_Ik T_kJ)
-  for (int lev = 1; lev < 4; ++lev) {
-    const int J = wave, I = wave + lev;
-    const bool act = I < 4;
-    if (act) {
-      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < 16 * lev; k0 += 16) {
-        m = mma16<16>(m, [&](int i, int k) { return s_A[16 * I + i][16 * J + k0 + k]; },
-                      [&](int k, int jj) { return s_T[16 * J + k0 + k][16 * J + jj]; }, lane);
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      s_gam[lane] = x;
+    }
+    __syncthreads();
+
+    float* wsp = ws + ((int64_t)cs * p.Hv + h) * kWsFloats;
+    float* ws_T = wsp;
+    float* ws_P = wsp + kC * kC;
+    // A (strictly lower, into the Q buffer) and P (causal, to the workspace)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int job = wave + 4 * k;
+      const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + acc_row(lane, e), sc = 16 * J + acc_col(lane);
+        if (isP) ws_P[t * kC + sc] = (sc <= t) ? expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
+        else s_A[t][sc] = (sc < t) ? s_beta[rg][t] * expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, lane = (block, column)
+    if (wave == 0) {
+      const int blk = lane >> 4, j = lane & 15, base = 16 * blk;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+#pragma unroll
+        for (int s = 0; s < i; ++s) x[i] = fmaf(-s_A[base + i][base + s], x[s], x[i]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_M[wave][acc_row(lane, r)][acc_col(lane)] = m[r];
+      for (int i = 0; i < 16; ++i) s_T[base + i][base + j] = x[i];
+    }
+    for (int i = tid; i < kC * kC; i += 256) {  // blocks above the diagonal are zero
+      const int rr = i / kC, cc = i - rr * kC;
+      if ((cc >> 4) > (rr >> 4)) s_T[rr][cc] = 0.f;
     }
     __syncthreads();
-    if (act) {
-      f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-      t = mma16<16>(t, [&](int i, int k) { return s_T[16 * I + i][16 * I + k]; },
-                    [&](int k, int jj) { return s_M[wave][k][jj]; }, lane);
+    // off-diagonal blocks, one level (I - J = lev) at a time:
+    //   T_IJ = -T_II (sum_{k=J}^{I-1} A_Ik T_kJ)
+    for (int lev = 1; lev < 4; ++lev) {
+      const int J = wave, I = wave + lev;
+      const bool act = I < 4;
+      if (act) {
+        f32x4_t m = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < 16 * lev; k0 += 16) {
+          m = mma16<16>(m, [&](int i, int k) { return s_A[16 * I + i][16 * J + k0 + k]; },
+                        [&](int k, int jj) { return s_T[16 * J + k0 + k][16 * J + jj]; }, lane);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_T[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = -t[r];
+        for (int e = 0; e < 4; ++e) s_M[wave][acc_row(lane, e)][acc_col(lane)] = m[e];
+      }
+      __syncthreads();
+      if (act) {
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+        t = mma16<16>(t, [&](int i, int k) { return s_T[16 * I + i][16 * I + k]; },
+                      [&](int k, int jj) { return s_M[wave][k][jj]; }, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_T[16 * I + acc_row(lane, e)][16 * J + acc_col(lane)] = -t[e];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  for (int i = tid; i < kC * kC; i += 256) ws_T[i] = s_T[i / kC][i % kC];
-  if (tid < kC) {
-    wsp[2 * kC * kC + tid] = s_gam[tid];
-    wsp[2 * kC * kC + kC + tid] = s_beta[tid];
-    wsp[2 * kC * kC + 2 * kC + tid] = expf(s_gam[tid]);
-    wsp[2 * kC * kC + 3 * kC + tid] = expf(s_gam[kC - 1] - s_gam[tid]);
+    for (int i = tid; i < kC * kC; i += 256) ws_T[i] = s_T[i / kC][i % kC];
+    if (tid < kC) {
+      wsp[2 * kC * kC + tid] = s_gam[tid];
+      wsp[2 * kC * kC + kC + tid] = s_beta[rg][tid];
+      wsp[2 * kC * kC + 2 * kC + tid] = expf(s_gam[tid]);
+      wsp[2 * kC * kC + 3 * kC + tid] = expf(s_gam[kC - 1] - s_gam[tid]);
+    }
   }
 }
 
@@ -475,6 +503,18 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
 // (U^T ready), after the outputs and the state update (S^T ready).
 constexpr int kS16Threads = 1024;
 
+// XCD-aware order of the k-contiguous state kernels' workgroups: every workgroup
+// of one (sequence, key head), its Hv / Hk value heads times NB column blocks,
+// shares bid mod 8, so one XCD's L2 fetches that key head's key and query rows
+// for all of them.  unit = n Hv + h, or -1 past the last group.
+__device__ __forceinline__ void key_group_unit(int bid, int NB, const PrefillArgs& p, int& unit, int& blk) {
+  const int R = p.Hv / p.Hk, per = R * NB;
+  const int x8 = bid & 7, y = bid >> 3;
+  const int sub = y % per, grp = (y / per) * 8 + x8;
+  blk = sub % NB;
+  unit = grp < p.N * p.Hk ? grp * R + sub / NB : -1;
+}
+
 template <int IDT>
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
@@ -533,11 +573,9 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state16_kernel(const 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
-  const int bid = blockIdx.x;  // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
-  const int x8 = bid & 7, y = bid >> 3;
-  const int blk = y % NB;
-  const int unit = (y / NB) * 8 + x8;
-  if (unit >= p.N * p.Hv) return;
+  int unit, blk;
+  key_group_unit(blockIdx.x, NB, p, unit, blk);
+  if (unit < 0) return;
   const int n = unit / p.Hv, h = unit - n * p.Hv;
   const int hk = h / (p.Hv / p.Hk);
   const int seq_lo = p.cu_seqlens[n], seq_hi = p.cu_seqlens[n + 1];
@@ -843,11 +881,9 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
-  const int bid = blockIdx.x;  // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
-  const int x8 = bid & 7, y = bid >> 3;
-  const int blk = y % NB;
-  const int unit = (y / NB) * 8 + x8;
-  if (unit >= p.N * p.Hv) return;
+  int unit, blk;
+  key_group_unit(blockIdx.x, NB, p, unit, blk);
+  if (unit < 0) return;
   const int n = unit / p.Hv, h = unit - n * p.Hv;
   const int hk = h / (p.Hv / p.Hk);
   const int seq_lo = p.cu_seqlens[n], seq_hi = p.cu_seqlens[n + 1];
@@ -1197,12 +1233,13 @@ static hipError_t launch_state16(const PrefillArgs& a, int state_dt, unsigned gr
 template <int D, int EB>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
   const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens);
-  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB>), dim3((unsigned)ncs, (unsigned)a.Hv), dim3(256), 0, s, a, ws);
+  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB>), dim3((unsigned)ncs, (unsigned)a.Hk), dim3(256), 0, s, a, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.N * a.Hv;
   if constexpr (EB == 2 && (D == 64 || D == 128)) {  // 16-bit inputs, wide heads: the k-contiguous kernel
-    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * (D / 32));
+    const int64_t groups = (int64_t)a.N * a.Hk;
+    const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * (a.Hv / a.Hk) * (D / 32));
     return a.in_dt == GDN_BF16 ? launch_state_bf16<D>(a, state_dt, grid, ws, s)
                                : launch_state16<D, GDN_F16>(a, state_dt, grid, ws, s);
   } else {

@@ -83,6 +83,14 @@ def test_prefill_ragged_lengths_wide_heads(D, in_dt):
     run_prefill(74 + D, [1, 63, 64, 65, 0, 130], 2, 4, D, "f32", in_dt=in_dt, a_shift=-1.0)
 
 
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (1, 3), (2, 8), (1, 5)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_gqa_ratios(Hk, Hv, D):
+    """1, 3, 4 and 5 value heads per key head: the chunk kernel forms a key head's products once and
+    scales them per value head, staging the gates of two value heads at a time."""
+    run_prefill(91 + D + Hv, [70, 129, 1], Hk, Hv, D, "f32", a_shift=-1.0)
+
+
 @pytest.mark.parametrize("D", [16, 64, 128])
 def test_prefill_head_dims(D):
     run_prefill(71 + D, [100, 37, 192], 1, 2, D, "f32")
