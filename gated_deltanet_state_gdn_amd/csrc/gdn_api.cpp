@@ -237,8 +237,9 @@ gdn_status gdn_copy_state_blocks(const gdn_state_ref* refs, int32_t P, uint64_t 
 }
 
 size_t gdn_chunk_prefill_workspace_bytes(const gdn_dims* dims, int32_t N, int64_t total_tokens, int32_t chunk) {
-  if (dims == nullptr || N <= 0 || total_tokens <= 0 || chunk != 64 || dims->num_v_heads < 1) return 0;
-  return gdn::prefill_workspace_bytes(N, total_tokens, dims->num_v_heads);
+  if (dims == nullptr || N <= 0 || total_tokens <= 0 || dims->num_v_heads < 1) return 0;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+  return gdn::prefill_workspace_bytes(N, total_tokens, dims->num_v_heads, chunk);
 }
 
 gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_seqlens, int64_t total_tokens,
@@ -249,7 +250,8 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
   GDN_REQUIRE(N >= 0, GDN_EINVAL, "N=%d must be >= 0", N);
   GDN_REQUIRE(total_tokens >= 0 && total_tokens <= INT32_MAX, GDN_EINVAL, "total_tokens=%lld out of [0, 2^31)",
               (long long)total_tokens);
-  GDN_REQUIRE(chunk == 64, GDN_EUNSUPPORTED, "chunk=%d: only 64 is compiled", chunk);
+  GDN_REQUIRE(chunk == 16 || chunk == 32 || chunk == 64, GDN_EUNSUPPORTED, "chunk=%d: 16, 32 and 64 are compiled",
+              chunk);
   GDN_REQUIRE((int64_t)N * dims->num_v_heads <= INT32_MAX / 4, GDN_EINVAL, "N * Hv exceeds the grid limit");
   GDN_TRY(check_dtypes(in_dtype, out_dtype));
   if (N == 0 || total_tokens == 0) return ok();  // nothing is read or written
@@ -263,8 +265,8 @@ gdn_status gdn_chunk_prefill(const gdn_dims* dims, int32_t N, const int32_t* cu_
               workspace_bytes, need);
   GDN_REQUIRE(need == 0 || (workspace != nullptr && aligned(workspace, 256)), GDN_EINVAL,
               "workspace is NULL or not 256-byte aligned");
-  GDN_REQUIRE(gdn::prefill_chunk_slots_fit(N, total_tokens, dims->num_k_heads, dims->num_v_heads), GDN_EINVAL,
-              "N + total_tokens / 64 chunk slots exceed the grid limit");
+  GDN_REQUIRE(gdn::prefill_chunk_slots_fit(N, total_tokens, dims->num_k_heads, dims->num_v_heads, chunk), GDN_EINVAL,
+              "N + total_tokens / chunk chunk slots exceed the grid limit");
   gdn::PrefillArgs a{q, k, v, gates->a, gates->b, gates->A_log, gates->dt_bias, state->base, slot_map, cu_seqlens,
                      out, state->num_slots, total_tokens, N, dims->num_k_heads, dims->num_v_heads,
                      (int32_t)in_dtype, (int32_t)out_dtype, eff_scale(dims)};

@@ -146,9 +146,10 @@ size_t replay_workspace_bytes(int64_t B, int Hv, int T, int D);
 constexpr size_t kReplayScratchBytes = (size_t)96 << 20;
 hipError_t replay_scratch(void** ptr);
 
-// Workspace of the chunked prefill: per (chunk slot, value head) the inverse
-// T, the causal decay-weighted Q K^T, gamma and beta of one chunk.
-size_t prefill_workspace_bytes(int N, int64_t total, int Hv);
-bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv);
+// Workspace of the chunked prefill for chunks of C tokens: per (chunk slot,
+// value head) the inverse T, the causal decay-weighted Q K^T, gamma and beta
+// of one chunk.
+size_t prefill_workspace_bytes(int N, int64_t total, int Hv, int C);
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv, int C);
 
 }  // namespace gdn

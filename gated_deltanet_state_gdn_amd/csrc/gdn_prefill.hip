@@ -36,23 +36,29 @@
 
 namespace gdn {
 
-constexpr int kC = 64;                        // chunk length
-constexpr int kWsFloats = 2 * kC * kC + 4 * kC;  // T, P, gamma, beta, e^gamma, e^{gamma_C - gamma} per (chunk slot, head)
+// Chunk lengths: 16, 32 or 64 tokens (a multiple of the 16-row MFMA tile).
+// The k-contiguous state kernels for 16-bit inputs are written for 64; the
+// LDS-staged kernel takes any of the three.
+constexpr int kC = 64;
+// floats per (chunk slot, head) of the workspace: T, P, gamma, beta, e^gamma, e^{gamma_C - gamma}
+template <int C>
+constexpr int ws_floats() { return 2 * C * C + 4 * C; }
+constexpr int kWsFloats = ws_floats<kC>();
 
 // Chunk slot of chunk c of sequence n: n + floor(cu[n] / C) + c.  It is unique
 // and below N + ceil(total / C) (floor((x+l)/C) >= floor(x/C) + ceil(l/C) - 1).
-__host__ __device__ inline int64_t prefill_chunk_slots(int64_t N, int64_t total) {
-  return N + (total + kC - 1) / kC;
+__host__ __device__ inline int64_t prefill_chunk_slots(int64_t N, int64_t total, int C) {
+  return N + (total + C - 1) / C;
 }
 
-size_t prefill_workspace_bytes(int N, int64_t total, int Hv) {
-  return (size_t)prefill_chunk_slots(N, total) * (size_t)Hv * kWsFloats * sizeof(float);
+size_t prefill_workspace_bytes(int N, int64_t total, int Hv, int C) {
+  return (size_t)prefill_chunk_slots(N, total, C) * (size_t)Hv * (2 * (size_t)C * C + 4 * (size_t)C) * sizeof(float);
 }
 
-bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv) {
+bool prefill_chunk_slots_fit(int N, int64_t total, int Hk, int Hv, int C) {
   const int64_t units = ((int64_t)N * Hv + 7) / 8 * 8 * 4;
   const int64_t grouped = ((int64_t)N * Hk + 7) / 8 * 8 * (Hv / Hk) * 4;
-  return prefill_chunk_slots(N, total) <= INT32_MAX && Hv <= 65535 && units <= INT32_MAX && grouped <= INT32_MAX;
+  return prefill_chunk_slots(N, total, C) <= INT32_MAX && Hv <= 65535 && units <= INT32_MAX && grouped <= INT32_MAX;
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -113,21 +119,24 @@ __device__ __forceinline__ f32x4_t rows_xyt(const uint32_t* X, const uint32_t* Y
 // value head scales them by its own gates and inverts its own (I + A).  The
 // gate inputs of the first two value heads load with the rows, so at R <= 2 the
 // workgroup waits on memory once; further heads load theirs two at a time.
-template <int D, int EB>
+template <int D, int EB, int C>
 __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArgs p, float* __restrict__ ws) {
-  constexpr int LDT = kC + 4;
+  static_assert(C == 16 || C == 32 || C == 64, "chunk of 16, 32 or 64 tokens");
+  constexpr int NT = C / 16;           // 16-row tiles per chunk
+  constexpr int JPW = (2 * NT * NT + 3) / 4;  // K K^T and Q K^T tiles per wave
+  constexpr int LDT = C + 4;
   constexpr int LDW = D * EB / 4 + 4;  // words per packed key / query row: 16-byte rows, 4 mod 8 banks
   constexpr int VE = 16 / EB, CPR = D / VE;
   constexpr int RMAX = 2;              // value heads whose gates are staged at once
   // two buffers: K rows then T, Q rows then A (about 40 KB in all at D = 128,
-  // so four work-groups share a CU and cover each other's memory waits)
-  constexpr int UW = kC * LDW > kC * LDT ? kC * LDW : kC * LDT;
+  // C = 64, so four work-groups share a CU and cover each other's memory waits)
+  constexpr int UW = C * LDW > C * LDT ? C * LDW : C * LDT;
   __shared__ __align__(16) uint32_t s_u0[UW];
   __shared__ __align__(16) uint32_t s_u1[UW];
   __shared__ float s_M[4][16][17];
   uint32_t* const s_k = s_u0;  // then T (below)
   uint32_t* const s_q = s_u1;  // then A
-  __shared__ float s_g[RMAX][kC], s_beta[RMAX][kC], s_gam[kC];
+  __shared__ float s_g[RMAX][C], s_beta[RMAX][C], s_gam[C];
 
   const int cs = blockIdx.x, hk = blockIdx.y;
   const int R = p.Hv / p.Hk;
@@ -137,27 +146,27 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (mid + cu[mid] / kC <= cs) lo = mid; else hi = mid - 1;
+    if (mid + cu[mid] / C <= cs) lo = mid; else hi = mid - 1;
   }
   const int n = lo;
-  const int c = cs - (n + cu[n] / kC);
+  const int c = cs - (n + cu[n] / C);
   const int seq_lo = cu[n], seq_hi = cu[n + 1];
-  if (c < 0 || (int64_t)c * kC >= (int64_t)(seq_hi - seq_lo)) return;  // unused chunk slot
+  if (c < 0 || (int64_t)c * C >= (int64_t)(seq_hi - seq_lo)) return;  // unused chunk slot
   const int slot = p.slot_map[n];
   if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // padded sequence: kernel 2 writes zeros
-  const int t0 = seq_lo + c * kC;
-  const int len = min(kC, seq_hi - t0);
+  const int t0 = seq_lo + c * C;
+  const int len = min(C, seq_hi - t0);
 
   // keys and queries stay packed in their input dtype, rows >= len zeroed; thread
   // (r, t) = (tid / C, tid mod C) loads the gate inputs of value head hk R + r, token t
   {
-    constexpr int IT = (kC * CPR + 255) / 256;
+    constexpr int IT = (C * CPR + 255) / 256;
     u32x4 xk[IT], xq[IT];
 #pragma unroll
     for (int u = 0; u < IT; ++u) {
       const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
       u32x4 zk = {0u, 0u, 0u, 0u}, zq = zk;
-      if (x < kC * CPR && r < len) {
+      if (x < C * CPR && r < len) {
         const int64_t off = (((int64_t)(t0 + r) * p.Hk + hk) * D + cc * VE) * EB;
         zk = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
         zq = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
@@ -165,7 +174,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       xk[u] = zk;
       xq[u] = zq;
     }
-    const int gr = tid / kC, gt = tid - gr * kC;
+    const int gr = tid / C, gt = tid - gr * C;
     const bool gl = gr < RMAX && gr < R;
     float ga = 0.f, gb = 0.f, al = 0.f, db = 0.f;
     if (gl) {
@@ -179,7 +188,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
 #pragma unroll
     for (int u = 0; u < IT; ++u) {
       const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
-      if (x < kC * CPR) {
+      if (x < C * CPR) {
         *reinterpret_cast<u32x4*>(s_k + r * LDW + cc * 4) = xk[u];
         *reinterpret_cast<u32x4*>(s_q + r * LDW + cc * 4) = xq[u];
       }
@@ -192,16 +201,17 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   }
   __syncthreads();
   const int lane0 = lane, tid0 = tid;
-  // K K^T and Q K^T tiles (16 of each; wave w takes tile rows I = w..), formed
-  // once for every value head (16-bit rows: the exact bf16 / f16 products, fp32
+  // K K^T and Q K^T tiles (NT x NT of each; job = wave + 4 k), formed once for
+  // every value head (16-bit rows: the exact bf16 / f16 products, fp32
   // accumulation); the upper tiles are not needed
-  f32x4_t kt[8];
+  f32x4_t kt[JPW];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < JPW; ++k) {
     const int job = wave + 4 * k;
-    const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
+    const int isP = job / (NT * NT), I = (job / NT) % NT, J = job % NT;
     kt[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (J <= I) kt[k] = rows_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, s_k + 16 * J * LDW, LDW, p.in_dt, lane);
+    if (job < 2 * NT * NT && J <= I)
+      kt[k] = rows_xyt<D, EB>((isP ? s_q : s_k) + 16 * I * LDW, s_k + 16 * J * LDW, LDW, p.in_dt, lane);
   }
 
   for (int r = 0; r < R; ++r) {
@@ -214,7 +224,7 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
     float (*const s_A)[LDT] = reinterpret_cast<float (*)[LDT]>(s_u1 + zoff);
     __syncthreads();  // the key and query rows are read (first head), s_T is written out (later heads)
     if (rg == 0 && r > 0) {  // the next heads' gates
-      const int gr = tid / kC, gt = tid - gr * kC;
+      const int gr = tid / C, gt = tid - gr * C;
       if (gr < RMAX && r + gr < R) {
         const int hg = h + gr;
         const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + hg;
@@ -226,35 +236,37 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       __syncthreads();
     }
     if (wave == 0) {  // inclusive prefix sum of this head's g over the chunk
-      float x = s_g[rg][lane];
+      float x = lane < C ? s_g[rg][lane] : 0.f;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
+      for (int off = 1; off < C; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
       }
-      s_gam[lane] = x;
+      if (lane < C) s_gam[lane] = x;
     }
     __syncthreads();
 
-    float* wsp = ws + ((int64_t)cs * p.Hv + h) * kWsFloats;
+    float* wsp = ws + ((int64_t)cs * p.Hv + h) * ws_floats<C>();
     float* ws_T = wsp;
-    float* ws_P = wsp + kC * kC;
+    float* ws_P = wsp + C * C;
     // A (strictly lower, into the Q buffer) and P (causal, to the workspace)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < JPW; ++k) {
       const int job = wave + 4 * k;
-      const int isP = job >> 4, I = (job >> 2) & 3, J = job & 3;
+      const int isP = job / (NT * NT), I = (job / NT) % NT, J = job % NT;
+      if (job < 2 * NT * NT) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * I + acc_row(lane, e), sc = 16 * J + acc_col(lane);
-        if (isP) ws_P[t * kC + sc] = (sc <= t) ? expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
-        else s_A[t][sc] = (sc < t) ? s_beta[rg][t] * expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * I + acc_row(lane, e), sc = 16 * J + acc_col(lane);
+          if (isP) ws_P[t * C + sc] = (sc <= t) ? expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
+          else s_A[t][sc] = (sc < t) ? s_beta[rg][t] * expf(s_gam[t] - s_gam[sc]) * kt[k][e] : 0.f;
+        }
       }
     }
     __syncthreads();
 
     // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, lane = (block, column)
-    if (wave == 0) {
+    if (wave == 0 && lane < C) {
       const int blk = lane >> 4, j = lane & 15, base = 16 * blk;
       float x[16];
 #pragma unroll
@@ -267,16 +279,16 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
 #pragma unroll
       for (int i = 0; i < 16; ++i) s_T[base + i][base + j] = x[i];
     }
-    for (int i = tid; i < kC * kC; i += 256) {  // blocks above the diagonal are zero
-      const int rr = i / kC, cc = i - rr * kC;
+    for (int i = tid; i < C * C; i += 256) {  // blocks above the diagonal are zero
+      const int rr = i / C, cc = i - rr * C;
       if ((cc >> 4) > (rr >> 4)) s_T[rr][cc] = 0.f;
     }
     __syncthreads();
     // off-diagonal blocks, one level (I - J = lev) at a time:
     //   T_IJ = -T_II (sum_{k=J}^{I-1} A_Ik T_kJ)
-    for (int lev = 1; lev < 4; ++lev) {
+    for (int lev = 1; lev < NT; ++lev) {
       const int J = wave, I = wave + lev;
-      const bool act = I < 4;
+      const bool act = I < NT;
       if (act) {
         f32x4_t m = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < 16 * lev; k0 += 16) {
@@ -296,12 +308,12 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
       }
       __syncthreads();
     }
-    for (int i = tid; i < kC * kC; i += 256) ws_T[i] = s_T[i / kC][i % kC];
-    if (tid < kC) {
-      wsp[2 * kC * kC + tid] = s_gam[tid];
-      wsp[2 * kC * kC + kC + tid] = s_beta[rg][tid];
-      wsp[2 * kC * kC + 2 * kC + tid] = expf(s_gam[tid]);
-      wsp[2 * kC * kC + 3 * kC + tid] = expf(s_gam[kC - 1] - s_gam[tid]);
+    for (int i = tid; i < C * C; i += 256) ws_T[i] = s_T[i / C][i % C];
+    if (tid < C) {
+      wsp[2 * C * C + tid] = s_gam[tid];
+      wsp[2 * C * C + C + tid] = s_beta[rg][tid];
+      wsp[2 * C * C + 2 * C + tid] = expf(s_gam[tid]);
+      wsp[2 * C * C + 3 * C + tid] = expf(s_gam[C - 1] - s_gam[tid]);
     }
   }
 }
@@ -327,20 +339,21 @@ struct PrefillGeom {
   static constexpr int NJ = BV / 16;
 };
 
-template <int SDT, int D, int EB>
+template <int SDT, int D, int EB, int C>
 __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const PrefillArgs p, const float* __restrict__ ws) {
   using G = PrefillGeom<D>;
   constexpr int BV = G::BV, NB = G::NB, NJ = G::NJ;
-  constexpr int LDK = D + 4, LDV = BV + 4, LDT = kC + 4;
-  constexpr int QRU = (kC * LDK > 2 * kC * LDV) ? kC * LDK : 2 * kC * LDV;
-  __shared__ float s_k[kC][LDK];
+  constexpr int NT = C / 16;  // 16-row tiles per chunk
+  constexpr int LDK = D + 4, LDV = BV + 4, LDT = C + 4;
+  constexpr int QRU = (C * LDK > 2 * C * LDV) ? C * LDK : 2 * C * LDV;
+  __shared__ float s_k[C][LDK];
   __shared__ float s_qru[QRU];  // Q [C][LDK], then R [C][LDV] and U [C][LDV]
-  __shared__ float s_v[kC][LDV];
-  __shared__ float s_T[kC][LDT], s_P[kC][LDT];
+  __shared__ float s_v[C][LDV];
+  __shared__ float s_T[C][LDT], s_P[C][LDT];
   __shared__ float s_S[D][LDV];
-  __shared__ float s_X[2 * kC][LDV];  // K S (rows 0..C-1), Q S (rows C..2C-1)
-  __shared__ float s_gb[2][kC];  // gamma, beta of the chunk
-  __shared__ float s_eg[kC], s_dec[kC], s_egC;
+  __shared__ float s_X[2 * C][LDV];  // K S (rows 0..C-1), Q S (rows C..2C-1)
+  __shared__ float s_gb[2][C];  // gamma, beta of the chunk
+  __shared__ float s_eg[C], s_dec[C], s_egC;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // XCD-aware order: the NB column blocks of one (sequence, head) share bid % 8
@@ -372,73 +385,73 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
 
   float* s_q = s_qru;
   float* s_R = s_qru;
-  float* s_U = s_qru + kC * LDV;
+  float* s_U = s_qru + C * LDV;
   const float* s_beta = s_gb[1];
-  const int nch = (len + kC - 1) / kC;
+  const int nch = (len + C - 1) / C;
 
   // chunk inputs are staged through registers: the loads of chunk c + 1 are
   // issued right after chunk c reaches LDS and complete under its GEMMs
-  RowStager<D, kC, kStateThreads, EB> stk, stq;
-  RowStager<BV, kC, kStateThreads, EB> stv;
-  RowStager<kC, kC, kStateThreads, 4> stT, stP;
-  RowStager<kC, 2, kStateThreads, 4> stg;
+  RowStager<D, C, kStateThreads, EB> stk, stq;
+  RowStager<BV, C, kStateThreads, EB> stv;
+  RowStager<C, C, kStateThreads, 4> stT, stP;
+  RowStager<C, 2, kStateThreads, 4> stg;
   auto issue = [&](int c) {
-    const int t0 = seq_lo + c * kC;
-    const int L = min(kC, seq_hi - t0);
-    const float* wsp = ws + ((int64_t)(n + seq_lo / kC + c) * p.Hv + h) * kWsFloats;
+    const int t0 = seq_lo + c * C;
+    const int L = min(C, seq_hi - t0);
+    const float* wsp = ws + ((int64_t)(n + seq_lo / C + c) * p.Hv + h) * ws_floats<C>();
     auto krow = [&](int t) { return ((int64_t)(t0 + t) * p.Hk + hk) * D; };
     stk.issue(p.k, L, krow);
     stq.issue(p.q, L, krow);
     stv.issue(p.v, L, [&](int t) { return ((int64_t)(t0 + t) * p.Hv + h) * D + col0; });
-    auto mrow = [](int r) { return (int64_t)r * kC; };
-    stT.issue(wsp, kC, mrow);
-    stP.issue(wsp + kC * kC, kC, mrow);
-    stg.issue(wsp + 2 * kC * kC, 2, mrow);
+    auto mrow = [](int r) { return (int64_t)r * C; };
+    stT.issue(wsp, C, mrow);
+    stP.issue(wsp + C * C, C, mrow);
+    stg.issue(wsp + 2 * C * C, 2, mrow);
   };
   issue(0);
   for (int c = 0; c < nch; ++c) {
-    const int t0 = seq_lo + c * kC;
-    const int L = min(kC, seq_hi - t0);
+    const int t0 = seq_lo + c * C;
+    const int L = min(C, seq_hi - t0);
     stk.commit(&s_k[0][0], LDK, p.in_dt);
     stq.commit(s_q, LDK, p.in_dt);
     stv.commit(&s_v[0][0], LDV, p.in_dt);
     stT.commit(&s_T[0][0], LDT, GDN_F32);
     stP.commit(&s_P[0][0], LDT, GDN_F32);
-    stg.commit(&s_gb[0][0], kC, GDN_F32);
+    stg.commit(&s_gb[0][0], C, GDN_F32);
     __syncthreads();
     if (c + 1 < nch) issue(c + 1);
-    if (tid < kC) {  // read after the next barrier
-      const float gt = s_gb[0][tid], gC = s_gb[0][kC - 1];
+    if (tid < C) {  // read after the next barrier
+      const float gt = s_gb[0][tid], gC = s_gb[0][C - 1];
       s_eg[tid] = expf(gt);
       s_dec[tid] = expf(gC - gt);
       if (tid == 0) s_egC = expf(gC);
     }
 
     // X = [K; Q] S
-    for (int job = wave; job < 8 * NJ; job += kStateThreads / 64) {
+    for (int job = wave; job < 2 * NT * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if (I < 4)
+      if (I < NT)
         acc = mma16<D>(acc, [&](int i, int k) { return s_k[16 * I + i][k]; },
                        [&](int k, int j) { return s_S[k][16 * J + j]; }, lane);
       else
-        acc = mma16<D>(acc, [&](int i, int k) { return s_q[(16 * (I - 4) + i) * LDK + k]; },
+        acc = mma16<D>(acc, [&](int i, int k) { return s_q[(16 * (I - NT) + i) * LDK + k]; },
                        [&](int k, int j) { return s_S[k][16 * J + j]; }, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_X[16 * I + acc_row(lane, r)][16 * J + acc_col(lane)] = acc[r];
     }
     __syncthreads();
     // R = diag(beta) (V - diag(e^gamma) K S)   (overwrites Q)
-    for (int i = tid; i < kC * BV; i += kStateThreads) {
+    for (int i = tid; i < C * BV; i += kStateThreads) {
       const int t = i / BV, j = i - t * BV;
       s_R[t * LDV + j] = s_beta[t] * (s_v[t][j] - s_eg[t] * s_X[t][j]);
     }
     __syncthreads();
     // U = T R
-    for (int job = wave; job < 4 * NJ; job += kStateThreads / 64) {
+    for (int job = wave; job < NT * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma16<kC>(acc, [&](int i, int k) { return s_T[16 * I + i][k]; },
+      acc = mma16<C>(acc, [&](int i, int k) { return s_T[16 * I + i][k]; },
                       [&](int k, int j) { return s_R[k * LDV + 16 * J + j]; }, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_U[(16 * I + acc_row(lane, r)) * LDV + 16 * J + acc_col(lane)] = acc[r];
@@ -446,16 +459,16 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
     __syncthreads();
     // O = scale (diag(e^gamma) Q S + P U)  and  S <- e^{gamma_C} S + (diag(dec) K)^T U
     const float egC = s_egC;
-    for (int job = wave; job < (4 + D / 16) * NJ; job += kStateThreads / 64) {
+    for (int job = wave; job < (NT + D / 16) * NJ; job += kStateThreads / 64) {
       const int I = job / NJ, J = job - I * NJ;
       f32x4_t acc;
-      if (I < 4) {
+      if (I < NT) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * I + acc_row(lane, r);
-          acc[r] = s_eg[t] * s_X[kC + t][16 * J + acc_col(lane)];
+          acc[r] = s_eg[t] * s_X[C + t][16 * J + acc_col(lane)];
         }
-        acc = mma16<kC>(acc, [&](int i, int k) { return s_P[16 * I + i][k]; },
+        acc = mma16<C>(acc, [&](int i, int k) { return s_P[16 * I + i][k]; },
                         [&](int k, int j) { return s_U[k * LDV + 16 * J + j]; }, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -465,10 +478,10 @@ __global__ void __launch_bounds__(kStateThreads) gdn_prefill_state_kernel(const 
                        p.out_dt);
         }
       } else {
-        const int Is = I - 4;
+        const int Is = I - NT;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = egC * s_S[16 * Is + acc_row(lane, r)][16 * J + acc_col(lane)];
-        acc = mma16<kC>(acc, [&](int i, int k) { return s_k[k][16 * Is + i] * s_dec[k]; },
+        acc = mma16<C>(acc, [&](int i, int k) { return s_k[k][16 * Is + i] * s_dec[k]; },
                         [&](int k, int j) { return s_U[k * LDV + 16 * J + j]; }, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_S[16 * Is + acc_row(lane, r)][16 * J + acc_col(lane)] = acc[r];
@@ -1230,14 +1243,14 @@ static hipError_t launch_state16(const PrefillArgs& a, int state_dt, unsigned gr
   return hipGetLastError();
 }
 
-template <int D, int EB>
+template <int D, int EB, int C>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
-  const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens);
-  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB>), dim3((unsigned)ncs, (unsigned)a.Hk), dim3(256), 0, s, a, ws);
+  const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens, C);
+  hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB, C>), dim3((unsigned)ncs, (unsigned)a.Hk), dim3(256), 0, s, a, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.N * a.Hv;
-  if constexpr (EB == 2 && (D == 64 || D == 128)) {  // 16-bit inputs, wide heads: the k-contiguous kernel
+  if constexpr (EB == 2 && (D == 64 || D == 128) && C == kC) {  // 16-bit inputs, wide heads: the k-contiguous kernel
     const int64_t groups = (int64_t)a.N * a.Hk;
     const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * (a.Hv / a.Hk) * (D / 32));
     return a.in_dt == GDN_BF16 ? launch_state_bf16<D>(a, state_dt, grid, ws, s)
@@ -1246,13 +1259,13 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * PrefillGeom<D>::NB);
     switch (state_dt) {
       case GDN_F32:
-        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F32, D, EB, C>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
         break;
       case GDN_BF16:
-        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_BF16, D, EB, C>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
         break;
       case GDN_F16:
-        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
+        hipLaunchKernelGGL((gdn_prefill_state_kernel<GDN_F16, D, EB, C>), dim3(grid), dim3(kStateThreads), 0, s, a, ws);
         break;
       default: return hipErrorInvalidValue;
     }
@@ -1260,18 +1273,27 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws
   }
 }
 
-template <int D>
+template <int D, int C>
 static hipError_t launch_prefill_eb(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
-  return a.in_dt == GDN_F32 ? launch_prefill_d<D, 4>(a, state_dt, ws, s) : launch_prefill_d<D, 2>(a, state_dt, ws, s);
+  return a.in_dt == GDN_F32 ? launch_prefill_d<D, 4, C>(a, state_dt, ws, s) : launch_prefill_d<D, 2, C>(a, state_dt, ws, s);
+}
+
+template <int C>
+static hipError_t launch_prefill_c(const PrefillArgs& a, int state_dt, int D, float* ws, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_prefill_eb<16, C>(a, state_dt, ws, s);
+    case 32: return launch_prefill_eb<32, C>(a, state_dt, ws, s);
+    case 64: return launch_prefill_eb<64, C>(a, state_dt, ws, s);
+    case 128: return launch_prefill_eb<128, C>(a, state_dt, ws, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int state_dt, int D, int chunk, float* ws, hipStream_t s) {
-  if (chunk != kC) return hipErrorInvalidValue;
-  switch (D) {
-    case 16: return launch_prefill_eb<16>(a, state_dt, ws, s);
-    case 32: return launch_prefill_eb<32>(a, state_dt, ws, s);
-    case 64: return launch_prefill_eb<64>(a, state_dt, ws, s);
-    case 128: return launch_prefill_eb<128>(a, state_dt, ws, s);
+  switch (chunk) {
+    case 16: return launch_prefill_c<16>(a, state_dt, D, ws, s);
+    case 32: return launch_prefill_c<32>(a, state_dt, D, ws, s);
+    case 64: return launch_prefill_c<64>(a, state_dt, D, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

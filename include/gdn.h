@@ -169,7 +169,9 @@ gdn_status gdn_spec_decode(const gdn_dims* dims, int32_t B, int32_t T, const voi
  *               one call up to that one extra rounding.
  *   out         [total_tokens, Hv, dv] out_dtype
  *   chunk       tokens per chunk, counted from each sequence's start in this
- *               call: 64 (the only compiled size).
+ *               call: 16, 32 or 64 (the chunked form is exact for any chunk
+ *               length; 64 runs the fastest kernels for 16-bit inputs at
+ *               dk = 64 and 128), else GDN_EUNSUPPORTED.
  *   workspace   device scratch of at least gdn_chunk_prefill_workspace_bytes()
  *               bytes, 256-byte aligned, owned by the caller, not read before
  *               it is written; NULL is allowed when that size is 0.

@@ -181,13 +181,16 @@ def test_prefill_validation_and_workspace(L):
     need = L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 64)
     # (N + ceil(T / 64)) chunk slots x Hv x (2 * 64 * 64 + 4 * 64) floats
     assert need == (4 + 319) * 32 * (2 * 64 * 64 + 256) * 4
-    assert L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 32) == 0
+    assert L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 48) == 0
+    # chunks of 32: (N + ceil(T / 32)) chunk slots x Hv x (2 * 32 * 32 + 4 * 32) floats
+    assert L.gdn_chunk_prefill_workspace_bytes(ctypes.byref(dims), 4, 20408, 32) == (4 + 638) * 32 * 2176 * 4
 
     def call(N=4, T=20408, chunk=64, ws=FAKE, wsb=need, cu=FAKE):
         return L.gdn_chunk_prefill(ctypes.byref(dims), N, cu, T, chunk, FAKE, FAKE, FAKE, gdn.GDN_BF16,
                                    ctypes.byref(_gates()), ctypes.byref(_pool()), FAKE, FAKE, gdn.GDN_F32, ws, wsb,
                                    None)
-    assert call(chunk=32) == gdn.GDN_EUNSUPPORTED
+    assert call(chunk=48) == gdn.GDN_EUNSUPPORTED
+    assert call(chunk=128) == gdn.GDN_EUNSUPPORTED
     assert call(wsb=need - 1) == gdn.GDN_EINVAL
     assert call(ws=None) == gdn.GDN_EINVAL
     assert call(ws=FAKE + 64) == gdn.GDN_EINVAL      # 256-byte alignment

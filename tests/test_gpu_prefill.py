@@ -20,7 +20,7 @@ def _gpu():
 
 
 def run_prefill(cid, lengths, Hk, Hv, D, sdt, in_dt="bf16", num_slots=None, slot_map=None, a_shift=0.0,
-                sample=None, pool=None, states=None, step=0, check=True):
+                sample=None, pool=None, states=None, step=0, check=True, chunk=64):
     """One prefill call on the GPU and on the oracle (optionally only sampled (seq, head) pairs)."""
     import torch
     import gated_deltanet_state_gdn_amd as gdn
@@ -36,10 +36,10 @@ def run_prefill(cid, lengths, Hk, Hv, D, sdt, in_dt="bf16", num_slots=None, slot
     cu = gen.seq_lengths_cu(lengths)
     inp = gen.token_inputs(cid, step, (int(cu[-1]),), Hk, Hv, D, D, in_dt, a_shift)
     A_log, dt_bias = gen.head_params(cid, Hv)
-    say(f"prefill cid={cid} lengths={list(lengths)[:8]} Hk={Hk} Hv={Hv} D={D} state={sdt} in={in_dt}")
+    say(f"prefill cid={cid} lengths={list(lengths)[:8]} Hk={Hk} Hv={Hv} D={D} state={sdt} in={in_dt} chunk={chunk}")
     out = gdn.gdn_chunk_prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["a"]), dev(inp["b"]),
                                 dev(A_log), dev(dt_bias), pool, torch.from_numpy(slot_map).to(DEV),
-                                torch.from_numpy(cu).to(DEV))
+                                torch.from_numpy(cu).to(DEV), chunk=chunk)
     torch.cuda.synchronize()
     o = host(out)
     assert np.all(np.isfinite(o)), "non-finite output"
@@ -81,6 +81,25 @@ def test_prefill_ragged_lengths_wide_heads(D, in_dt):
     """Head dims 64 and 128 with 16-bit inputs (the k-contiguous state kernel): partial, exact and
     empty chunks, GQA with two value heads per key head."""
     run_prefill(74 + D, [1, 63, 64, 65, 0, 130], 2, 4, D, "f32", in_dt=in_dt, a_shift=-1.0)
+
+
+@pytest.mark.parametrize("in_dt,D", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 32)])
+def test_prefill_chunk_size_invariance(in_dt, D):
+    """The chunked form is exact for any chunk length: chunks of 16, 32 and 64 tokens over lengths
+    around each size (1, 15, 16, 17, 33, 64, 65, 130; partial and exact chunks of every size) and
+    slow decay give the oracle's outputs and states at the fp32 bar, and the same results as each
+    other (at 64 with 16-bit inputs and D = 64 / 128 the k-contiguous state kernels run, at 16 and
+    32 the LDS-staged one)."""
+    lengths = [1, 15, 16, 17, 33, 64, 65, 130]
+    outs, pools = [], []
+    for chunk in (16, 32, 64):
+        pool, states, o, inp = run_prefill(120 + D, lengths, 2, 4, D, "f32", in_dt=in_dt, a_shift=-3.0, chunk=chunk)
+        outs.append(o)
+        pools.append(host(pool))
+    slots = gen.slot_permutation(120 + D, len(lengths) + 3)[:len(lengths)]
+    for i in (0, 1):
+        assert_close(outs[i], outs[2], "f32", f"outputs, chunks of {16 * 2 ** i} against 64")
+        assert_close(pools[i][slots], pools[2][slots], "f32", f"states, chunks of {16 * 2 ** i} against 64")
 
 
 @pytest.mark.parametrize("Hk,Hv", [(4, 4), (1, 3), (2, 8), (1, 5)])
