@@ -883,8 +883,10 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
   constexpr int LTF = kC + 4;      // floats per R^T / U^T row
   constexpr int LSF = D + 4;       // floats per S^T row
   constexpr int LSW = D / 2 + 4;   // words per S^T plane row
+  constexpr int LKW = D / 2 + 4;   // words per K row
   constexpr int KTL = kC * D / 8 / 512;
   __shared__ __align__(16) uint32_t s_kt[2][D * LTW];
+  __shared__ __align__(16) uint32_t s_kr[2][kC * LKW];
   __shared__ __align__(16) float s_St[BV * LSF];
   __shared__ __align__(16) uint32_t s_Sp[3][BV * LSW];
   __shared__ __align__(16) float s_Rt[BV * LTF];
@@ -933,12 +935,15 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
   // per chunk:
   //   waves 0-3  (K role): [K S] for rows 16 w.., both column tiles; R^T; U = T R
   //   waves 4-7  (Q role): [Q S] for rows 16 (w - 4).., both column tiles; outputs
-  //   waves 8-15 (S role): K^T and gate staging one chunk ahead; the state update
+  //   waves 8-15 (S role): K and gate staging one chunk ahead (K^T for the
+  //                        update, K rows for the K role); the state update
   // Every global element a work-group reads is loaded by one lane only, one
-  // chunk ahead, and each role issues the same loads every chunk.
-  // Rows past a chunk's end read the chunk's last row instead: beta is zero
-  // there, so their [K S] rows, R rows and U rows vanish, and their outputs
-  // are dropped.
+  // chunk ahead, and each role issues the same loads every chunk.  The K role
+  // takes its key rows from the S role's LDS copy: reading them from memory
+  // as well cost 3% of the kernel's time.
+  // Rows past a chunk's end read the chunk's last row instead (key rows are
+  // zero there): beta is zero there, so their [K S] rows, R rows and U rows
+  // vanish, and their outputs are dropped.
   const int I = wave & 3;
   const int arow = 16 * I + li;
   // [X S] for rows 16 I.. and both 16-column tiles, S from its three planes.
@@ -1024,6 +1029,11 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
     // ================================================================ K role
     u32x4 a1[KB];
     f32x4 a2[4];
+    auto read_rows = [&](int c) {  // K rows 16 I + li of chunk c, staged by the S role (zero past the end)
+      const uint32_t* q = s_kr[c & 1] + arow * LKW + 4 * kk;
+#pragma unroll
+      for (int b = 0; b < KB; ++b) a1[b] = *reinterpret_cast<const u32x4*>(q + 16 * b);
+    };
     uint32_t vv[2][4];
     auto load_v = [&](int c) {  // V at the accumulator positions of both [K S] tiles
       const int L = chunk_len(c);
@@ -1035,10 +1045,10 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
         vv[1][e] = q[row + 16];
       }
     };
-    load_rows(p.k, 0, a1);
     load_v(0);
     load_mat(0, 0, a2);
     __syncthreads();
+    read_rows(0);
     for (int c = 0; c < nch; ++c) {
       const int L = chunk_len(c), cn = min(c + 1, nch - 1);
       const float* g = s_g[c & 1];
@@ -1057,7 +1067,6 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
           }
           *reinterpret_cast<f32x4*>(s_Rt + (16 * J + li) * LTF + tb) = r;
         }
-        load_rows(p.k, cn, a1);
         load_v(cn);
       }
       __syncthreads();
@@ -1065,6 +1074,7 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
         f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32_tiles(a2, s_Rt, u);
         load_mat(cn, 0, a2);
+        read_rows(c + 1);  // committed before the first barrier of this chunk
         const f32x4 dc = ld4(g + 3 * kC + tb);
 #pragma unroll
         for (int J = 0; J < 2; ++J) {
@@ -1143,6 +1153,7 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
       for (int u = 0; u < KTL; ++u) {
         u32x4 w = ktr[u];
         if (dead) w = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(s_kr[c & 1] + krow * LKW + 4 * kcg + 32 * u) = w;
         // the even row keeps columns 0-3 of its group and takes the odd row's; the odd row columns 4-7
         const uint32_t give0 = kodd ? w[0] : w[2], give1 = kodd ? w[1] : w[3];
         const uint32_t own0 = kodd ? w[2] : w[0], own1 = kodd ? w[3] : w[1];
