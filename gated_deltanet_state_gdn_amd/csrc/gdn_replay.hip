@@ -129,11 +129,90 @@ __device__ __forceinline__ int64_t ring_key_base(const DecodeArgs& p, int64_t sl
 }
 __device__ __forceinline__ bool appends_keys(const DecodeArgs& p, int h) { return h % (p.Hv / p.Hk) == 0; }
 
+// ---------------------------------------------------------------- fold plan
+// Which units a fold workgroup folds.  A sequence folds when its slot is mapped
+// and its ring would overflow (count + T > L), or, in a flush (T == 0), when
+// its ring holds entries (every mapped slot in a dual flush).  Workgroup w
+// first writes the records of units w, w + G, ... (the pointers the prep will
+// see).  Then, for each window of up to kFoldPlanSeqs sequences, every
+// workgroup builds the same list of the window's folding sequences from the
+// ring counts (bit b of a mask word per 64 sequences, with prefix counts) and
+// folds units f = w, w + G, ... of it: sequence f / Hv of the list, head
+// f mod Hv.  The folds of a step are so spread evenly over the grid whichever
+// sequences they belong to (staggered rings fold about 1/L of the sequences
+// on every step), and no counter has to start at zero.
+constexpr int kFoldPlanSeqs = 4096;
+constexpr int kFoldPlanWords = kFoldPlanSeqs / 64;
+
+struct FoldPlanLds {
+  uint64_t mask[kFoldPlanWords];
+  int pref[kFoldPlanWords + 1];
+};
+
+template <bool DUAL, class F>
+__device__ __forceinline__ void fold_units(const ReplayArgs& P, FoldPlanLds& sh, F&& fold_unit) {
+  const DecodeArgs& p = P.d;
+  const RingArgs& R = P.ring;
+  const int T = P.T, L = R.L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nth = blockDim.x;
+  const int units = p.B * p.Hv, G = gridDim.x;
+  // whether sequence b folds, and the record of its units
+  auto plan_of = [&](int b, int4& rc) -> bool {
+    const int slot = p.slot_map[b];
+    rc = int4{-1, 0, 0, 0};
+    if (slot < 0 || (int64_t)slot >= p.num_slots) return false;
+    const RingPos rp = ring_pos(R, slot);
+    const bool need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || DUAL);
+    rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
+    return need;
+  };
+  if (P.rec != nullptr) {
+    for (int64_t j = tid; blockIdx.x + j * G < units; j += nth) {
+      const int x = (int)(blockIdx.x + j * G);
+      int4 rc;
+      plan_of(x / p.Hv, rc);
+      reinterpret_cast<int4*>(P.rec)[x] = rc;
+    }
+  }
+  // every value of the list walk is the same in all lanes: scalar registers
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  for (int b0 = 0; b0 < p.B; b0 += kFoldPlanSeqs) {
+    const int nwords = (min(kFoldPlanSeqs, p.B - b0) + 63) / 64;
+    for (int q0 = 0; q0 < nwords; q0 += nth / 64) {
+      const int q = q0 + wave, b = b0 + 64 * q + lane;
+      int4 rc;
+      const bool need = q < nwords && b < p.B && plan_of(b, rc);
+      const uint64_t m = __ballot(need);
+      if (q < nwords && lane == 0) sh.mask[q] = m;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int q = 0; q < nwords; ++q) {
+        sh.pref[q] = acc;
+        acc += __popcll(sh.mask[q]);
+      }
+      sh.pref[nwords] = acc;
+    }
+    __syncthreads();
+    const int64_t total = (int64_t)uni(sh.pref[nwords]) * p.Hv;
+    int q = 0;
+    for (int64_t f = blockIdx.x; f < total; f += G) {
+      const int i = (int)(f / p.Hv), h = (int)(f - (int64_t)i * p.Hv);
+      while (uni(sh.pref[q + 1]) <= i) ++q;
+      const uint64_t mw = sh.mask[q];
+      uint64_t m = ((uint64_t)(uint32_t)uni((int)(mw >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)mw);
+      for (int k = i - uni(sh.pref[q]); k > 0; --k) m &= m - 1;  // drop the set bits before the i-th
+      fold_unit((b0 + 64 * q + __builtin_ctzll(m)) * p.Hv + h);
+    }
+    __syncthreads();  // the masks are rewritten for the next window
+  }
+}
+
 // ---------------------------------------------------------------- fold
-// Persistent: workgroup w owns units w, w + G, w + 2G, ... (G the grid size,
-// sized to the resident workgroups), checks 64 of them at a time, one per
-// lane of wave 0, and folds those that need it one after another with the
-// whole workgroup, so a step without folds costs one small check per unit.
+// Persistent (G workgroups, the resident count): each workgroup folds the
+// units the fold plan above gives it, one after another with the whole
+// workgroup, so a step without folds costs one pass over the ring counts.
 // A unit folds when count + T > L; the flush (T == 0) folds every non-empty
 // ring.  CDT >= 0 selects the dual-precision checkpoint: the fp32 result is
 // also written, rounded once, to the CDT read copy (the flush then refreshes
@@ -155,14 +234,12 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
 
   extern __shared__ float s_dyn[];
   __shared__ float s_red[2][NW][D];
-  __shared__ int s_list[64];
-  __shared__ int s_n;
+  __shared__ FoldPlanLds s_plan;
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
-  const int T = P.T, L = R.L;
+  const int L = R.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int units = p.B * p.Hv;
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
   float* e_k = s_dyn;           // [L][LDE]
@@ -170,113 +247,87 @@ gdn_replay_fold_rows_kernel(const ReplayArgs P) {
   float* e_a = e_v + L * LDE;   // [L] exp(g)
   float* e_b = e_a + L;         // [L] beta
 
-  const int grid_n = gridDim.x;
-  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
-    if (wave == 0) {
-      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
-      const int x = xl < units ? (int)xl : units;
-      bool need = false;
-      if (x < units) {
-        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-        const int slot = p.slot_map[b];
-        int4 rc = {-1, 0, 0, 0};
-        if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, slot);
-          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
-          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
-        }
-        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
-      }
-      const uint64_t mask = __ballot(need);
-      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
-      if (lane == 0) s_n = __popcll(mask);
+  fold_units<(CDT >= 0)>(P, s_plan, [&](const int x) {
+    const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+    const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+    const RingPos rp = ring_pos(R, p.slot_map[b]);
+    const int st = rp.st, cnt = rp.cnt;
+
+    // the lane offset is made opaque per unit so that the per-pass addresses
+    // are not hoisted out of the unit loop (they would hold registers)
+    int lane_off = r0 * D + c0;
+    asm volatile("" : "+v"(lane_off));
+    ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
+    float s[PASSES][VEC];
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) IO::widen(IO::load_raw(tile + pp * NW * RPW * D), s[pp]);
+
+    const int64_t ring_e = unit * L;
+    const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
+    for (int t = tid; t < cnt; t += NTH) {
+      const int j = (st + t) % L;
+      e_a[t] = expf(R.g[ring_e + j]);
+      e_b[t] = R.beta[ring_e + j];
+    }
+    for (int r0s = 0; r0s < cnt; r0s += kStageRows) {
+      Stager sk, sv;
+      auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
+      auto key_row = [&](int r) { return (kring_e + (st + r0s + r) % L) * D; };
+      const int nr = min(kStageRows, cnt - r0s);
+      sk.issue(R.k, nr, key_row);
+      sv.issue(R.v, nr, ring_row);
+      sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
+      sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
     }
     __syncthreads();
-    const int n_fold = s_n;
-    for (int f = 0; f < n_fold; ++f) {
-      const int x = s_list[f];
-      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, p.slot_map[b]);
-      const int st = rp.st, cnt = rp.cnt;
 
-      // the lane offset is made opaque per unit so that the per-pass addresses
-      // are not hoisted out of the unit loop (they would hold registers)
-      int lane_off = r0 * D + c0;
-      asm volatile("" : "+v"(lane_off));
-      ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
-      float s[PASSES][VEC];
+    for (int i = 0; i < cnt; ++i) {
+      const float* ki = e_k + i * LDE;
+      float kvp[VEC];
 #pragma unroll
-      for (int pp = 0; pp < PASSES; ++pp) IO::widen(IO::load_raw(tile + pp * NW * RPW * D), s[pp]);
-
-      const int64_t ring_e = unit * L;
-      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
-      for (int t = tid; t < cnt; t += NTH) {
-        const int j = (st + t) % L;
-        e_a[t] = expf(R.g[ring_e + j]);
-        e_b[t] = R.beta[ring_e + j];
+      for (int e = 0; e < VEC; ++e) kvp[e] = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) {
+        const float kr = ki[r0 + pp * NW * RPW];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kvp[e] = fmaf(s[pp][e], kr, kvp[e]);
       }
-      for (int r0s = 0; r0s < cnt; r0s += kStageRows) {
-        Stager sk, sv;
-        auto ring_row = [&](int r) { return (ring_e + (st + r0s + r) % L) * D; };
-        auto key_row = [&](int r) { return (kring_e + (st + r0s + r) % L) * D; };
-        const int nr = min(kStageRows, cnt - r0s);
-        sk.issue(R.k, nr, key_row);
-        sv.issue(R.v, nr, ring_row);
-        sk.commit(e_k + r0s * LDE, LDE, p.in_dt, nr);
-        sv.commit(e_v + r0s * LDE, LDE, p.in_dt, nr);
+      float* red = s_red[i & 1][0];  // double-buffered: one barrier per entry
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) kvp[e] = xor_sum_from<LPR>(kvp[e]);
+      if (lane < LPR) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) red[wave * D + c0 + e] = kvp[e];
       }
       __syncthreads();
-
-      for (int i = 0; i < cnt; ++i) {
-        const float* ki = e_k + i * LDE;
-        float kvp[VEC];
+      const float al = e_a[i], be = e_b[i];
+      float delta[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) kvp[e] = 0.f;
+      for (int e = 0; e < VEC; ++e) {
+        float kv = 0.f;
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) {
-          const float kr = ki[r0 + pp * NW * RPW];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) kvp[e] = fmaf(s[pp][e], kr, kvp[e]);
-        }
-        float* red = s_red[i & 1][0];  // double-buffered: one barrier per entry
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) kvp[e] = xor_sum_from<LPR>(kvp[e]);
-        if (lane < LPR) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) red[wave * D + c0 + e] = kvp[e];
-        }
-        __syncthreads();
-        const float al = e_a[i], be = e_b[i];
-        float delta[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float kv = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) kv += red[w * D + c0 + e];
-          delta[e] = be * (e_v[i * LDE + c0 + e] - al * kv);
-        }
-#pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) {
-          const float kr = ki[r0 + pp * NW * RPW];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr * delta[e]);
-        }
+        for (int w = 0; w < NW; ++w) kv += red[w * D + c0 + e];
+        delta[e] = be * (e_v[i * LDE + c0 + e] - al * kv);
       }
-      if (cnt > 0) {
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * NW * RPW * D, s[pp]);
-      }
-      if constexpr (CDT >= 0) {
-        using CIO = TileIO<CDT, VEC, false>;
-        uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+      for (int pp = 0; pp < PASSES; ++pp) {
+        const float kr = ki[r0 + pp * NW * RPW];
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * NW * RPW * D, s[pp]);
+        for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(al, s[pp][e], kr * delta[e]);
       }
-      __syncthreads();  // LDS staging is reused by the next unit
     }
-    __syncthreads();  // s_list is rewritten by the next check
-  }
+    if (cnt > 0) {
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * NW * RPW * D, s[pp]);
+    }
+    if constexpr (CDT >= 0) {
+      using CIO = TileIO<CDT, VEC, false>;
+      uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * NW * RPW * D, s[pp]);
+    }
+    __syncthreads();  // LDS staging is reused by the next unit
+  });
 }
 
 // The fold for D >= 32, with the tile split by columns: wave w holds columns
@@ -301,14 +352,12 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
   using ST = typename StateElem<SDT>::T;
 
   extern __shared__ float s_dyn[];
-  __shared__ int s_list[64];
-  __shared__ int s_n;
+  __shared__ FoldPlanLds s_plan;
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
-  const int T = P.T, L = R.L;
+  const int L = R.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int units = p.B * p.Hv;
   const int cg = lane % CG, rs = lane / CG;
   const int c0 = wave * CW + cg * VEC;
   float* e_kp = s_dyn;           // [L][RS][PASSES]: element (j, row pp * RS + r) at j D + r PASSES + pp
@@ -317,135 +366,109 @@ __global__ void __launch_bounds__(kFoldColThreads) gdn_replay_fold_kernel(const 
   float* e_b = e_a + L;          // [L] beta
   constexpr int VE = 16 / EB, CPR = D / VE;  // ring row elements per 16-byte load, loads per row
 
-  const int grid_n = gridDim.x;
-  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
-    if (wave == 0) {
-      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
-      const int x = xl < units ? (int)xl : units;
-      bool need = false;
-      if (x < units) {
-        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-        const int slot = p.slot_map[b];
-        int4 rc = {-1, 0, 0, 0};
-        if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, slot);
-          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
-          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
-        }
-        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
-      }
-      const uint64_t mask = __ballot(need);
-      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
-      if (lane == 0) s_n = __popcll(mask);
+  fold_units<(CDT >= 0)>(P, s_plan, [&](const int x) {
+    const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+    const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+    const RingPos rp = ring_pos(R, p.slot_map[b]);
+    const int st = rp.st, cnt = rp.cnt;
+
+    // the lane offset is made opaque per unit so that the per-pass addresses
+    // are not hoisted out of the unit loop (they would hold registers)
+    int lane_off = rs * D + c0;
+    asm volatile("" : "+v"(lane_off));
+    ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
+    typename IO::Raw raw[PASSES];
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + pp * RS * D);
+
+    const int64_t ring_e = unit * L;
+    const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
+    for (int t = tid; t < cnt; t += NTH) {
+      const int j = (st + t) % L;
+      e_a[t] = expf(R.g[ring_e + j]);
+      e_b[t] = R.beta[ring_e + j];
     }
+    for (int q = tid; q < cnt * CPR; q += NTH) {  // keys (permuted) and values, widened
+      const int t = q / CPR, cc = (q - t * CPR) * VE;
+      const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float kf, vf;
+        if constexpr (EB == 4) {
+          kf = __uint_as_float(kw[e]);
+          vf = __uint_as_float(vw[e]);
+        } else {
+          const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
+          const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
+          kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
+          vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+        }
+        const int r = cc + e;
+        e_kp[t * D + (r % RS) * PASSES + r / RS] = kf;
+        e_v[t * D + r] = vf;
+      }
+    }
+    float s[PASSES][VEC];
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
     __syncthreads();
-    const int n_fold = s_n;
-    for (int f = 0; f < n_fold; ++f) {
-      const int x = s_list[f];
-      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, p.slot_map[b]);
-      const int st = rp.st, cnt = rp.cnt;
 
-      // the lane offset is made opaque per unit so that the per-pass addresses
-      // are not hoisted out of the unit loop (they would hold registers)
-      int lane_off = rs * D + c0;
-      asm volatile("" : "+v"(lane_off));
-      ST* tile = static_cast<ST*>(p.pool) + unit * (int64_t)(D * D) + lane_off;
-      typename IO::Raw raw[PASSES];
-#pragma unroll
-      for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + pp * RS * D);
-
-      const int64_t ring_e = unit * L;
-      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
-      for (int t = tid; t < cnt; t += NTH) {
-        const int j = (st + t) % L;
-        e_a[t] = expf(R.g[ring_e + j]);
-        e_b[t] = R.beta[ring_e + j];
-      }
-      for (int q = tid; q < cnt * CPR; q += NTH) {  // keys (permuted) and values, widened
-        const int t = q / CPR, cc = (q - t * CPR) * VE;
-        const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
-        const u32x4 kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          float kf, vf;
-          if constexpr (EB == 4) {
-            kf = __uint_as_float(kw[e]);
-            vf = __uint_as_float(vw[e]);
-          } else {
-            const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
-            const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
-            kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
-            vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
-          }
-          const int r = cc + e;
-          e_kp[t * D + (r % RS) * PASSES + r / RS] = kf;
-          e_v[t * D + r] = vf;
-        }
-      }
-      float s[PASSES][VEC];
-#pragma unroll
-      for (int pp = 0; pp < PASSES; ++pp) IO::widen(raw[pp], s[pp]);
-      __syncthreads();
-
-      // the cnt steps S <- e^{g} S;  d = beta (v - S^T k);  S <- S + k d^T, per column.
-      // The tile is held as S = sc * S' with the decays in the scalar sc, so a
-      // step costs one FMA per element: S' <- S' + k (d / sc).  When sc falls
-      // below 2^-64 (an underflowed decay included) it is folded into S' before
-      // the step, so 1/sc stays finite and the tile far from fp32 range.
-      float sc = 1.f;
-      for (int j = 0; j < cnt; ++j) {
-        const float be = e_b[j];
-        sc *= e_a[j];
-        if (sc < 0x1p-64f) {  // uniform over the workgroup
-#pragma unroll
-          for (int pp = 0; pp < PASSES; ++pp)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) s[pp][e] *= sc;
-          sc = 1.f;
-        }
-        float kr[PASSES];
-        const float* kp = e_kp + j * D + rs * PASSES;
-#pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) kr[pp] = kp[pp];
-        float xs[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) xs[e] = 0.f;
-#pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) xs[e] = fmaf(s[pp][e], kr[pp], xs[e]);
-        const float inv = 1.f / sc;
-        float dl[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dl[e] = inv * be * (e_v[j * D + c0 + e] - sc * xor_sum_from<CG>(xs[e]));
-#pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(kr[pp], dl[e], s[pp][e]);
-      }
-      if (sc != 1.f) {
+    // the cnt steps S <- e^{g} S;  d = beta (v - S^T k);  S <- S + k d^T, per column.
+    // The tile is held as S = sc * S' with the decays in the scalar sc, so a
+    // step costs one FMA per element: S' <- S' + k (d / sc).  When sc falls
+    // below 2^-64 (an underflowed decay included) it is folded into S' before
+    // the step, so 1/sc stays finite and the tile far from fp32 range.
+    float sc = 1.f;
+    for (int j = 0; j < cnt; ++j) {
+      const float be = e_b[j];
+      sc *= e_a[j];
+      if (sc < 0x1p-64f) {  // uniform over the workgroup
 #pragma unroll
         for (int pp = 0; pp < PASSES; ++pp)
 #pragma unroll
           for (int e = 0; e < VEC; ++e) s[pp][e] *= sc;
+        sc = 1.f;
       }
-      if (cnt > 0) {
+      float kr[PASSES];
+      const float* kp = e_kp + j * D + rs * PASSES;
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * RS * D, s[pp]);
-      }
-      if constexpr (CDT >= 0) {
-        using CIO = TileIO<CDT, VEC, false>;
-        uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+      for (int pp = 0; pp < PASSES; ++pp) kr[pp] = kp[pp];
+      float xs[VEC];
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * RS * D, s[pp]);
-      }
-      __syncthreads();  // LDS staging is reused by the next unit
+      for (int e = 0; e < VEC; ++e) xs[e] = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xs[e] = fmaf(s[pp][e], kr[pp], xs[e]);
+      const float inv = 1.f / sc;
+      float dl[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dl[e] = inv * be * (e_v[j * D + c0 + e] - sc * xor_sum_from<CG>(xs[e]));
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[pp][e] = fmaf(kr[pp], dl[e], s[pp][e]);
     }
-    __syncthreads();  // s_list is rewritten by the next check
-  }
+    if (sc != 1.f) {
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[pp][e] *= sc;
+    }
+    if (cnt > 0) {
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) IO::store(tile + pp * RS * D, s[pp]);
+    }
+    if constexpr (CDT >= 0) {
+      using CIO = TileIO<CDT, VEC, false>;
+      uint16_t* copy = static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D) + lane_off;
+#pragma unroll
+      for (int pp = 0; pp < PASSES; ++pp) CIO::store(copy + pp * RS * D, s[pp]);
+    }
+    __syncthreads();  // LDS staging is reused by the next unit
+  });
 }
 
 // e^x for x <= 0 on the hardware base-2 exponential (underflows to zero)
@@ -484,15 +507,13 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
   using ST = typename StateElem<SDT>::T;
 
   extern __shared__ float s_dyn[];
-  __shared__ int s_list[64];
-  __shared__ int s_n;
+  __shared__ FoldPlanLds s_plan;
 
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
-  const int T = P.T, L = R.L;
+  const int L = R.L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int units = p.B * p.Hv;
   float* e_kt = s_dyn;                  // [D][KTS]: key element (entry e, row r) at r KTS + e
   float* e_k = e_kt + D * KTS;          // [16][VS]: key rows
   float* e_v = e_k + 16 * VS;           // [16][VS]: value rows
@@ -518,213 +539,187 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
       __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack2<DT>(x, 0.f) & 0xffffu), rs, voff, soff, 0);
   };
 
-  const int grid_n = gridDim.x;
-  for (int64_t j0 = 0; blockIdx.x + j0 * grid_n < units; j0 += 64) {
-    if (wave == 0) {
-      const int64_t xl = blockIdx.x + (j0 + lane) * grid_n;
-      const int x = xl < units ? (int)xl : units;
-      bool need = false;
-      if (x < units) {
-        const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-        const int slot = p.slot_map[b];
-        int4 rc = {-1, 0, 0, 0};
-        if (slot >= 0 && (int64_t)slot < p.num_slots) {
-          const RingPos rp = ring_pos(R, slot);
-          need = (T > 0) ? (rp.cnt + T > L) : (rp.cnt > 0 || CDT >= 0);
-          rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
-        }
-        if (P.rec != nullptr) reinterpret_cast<int4*>(P.rec)[x] = rc;  // the pointers the prep will see
+  fold_units<(CDT >= 0)>(P, s_plan, [&](const int x) {
+    const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
+    const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
+    const RingPos rp = ring_pos(R, p.slot_map[b]);
+    const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
+
+    // ---- the checkpoint tile in the accumulator layout (lane offset made
+    // opaque per unit so the addresses are not hoisted out of the unit loop)
+    const int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
+    const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<ST*>(p.pool) + unit * (int64_t)(D * D), 0, D * D * SB, 0x00020000);
+    float s0[NI][NJ][4];
+#pragma unroll
+    for (int I = 0; I < NI; ++I)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB);
+
+    // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
+    const int64_t ring_e = unit * L;
+    const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
+    for (int q = tid; q < 16 * CPR; q += NTH) {
+      const int t = q / CPR, cc = (q - t * CPR) * VE;
+      u32x4 kw = {0u, 0u, 0u, 0u}, vw = kw;
+      if (t < cnt) {
+        const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
+        kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
+        vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
       }
-      const uint64_t mask = __ballot(need);
-      if (need) s_list[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = x;
-      if (lane == 0) s_n = __popcll(mask);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float kf, vf;
+        if constexpr (EB == 4) {
+          kf = __uint_as_float(kw[e]);
+          vf = __uint_as_float(vw[e]);
+        } else {
+          const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
+          const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
+          kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
+          vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+        }
+        e_kt[(cc + e) * KTS + t] = kf;
+        e_k[t * VS + cc + e] = kf;
+        e_v[t * VS + cc + e] = vf;
+      }
+    }
+    if (wave == 0 && lane < 16) {  // gates in live order, zero past cnt; prefix sums within the row
+      float gg = 0.f, be = 0.f;
+      if (lane < cnt) {
+        const int64_t j = ring_e + (st + lane) % L;
+        gg = R.g[j];
+        be = R.beta[j];
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float y = __shfl_up(gg, off, 16);
+        if (lane >= off) gg += y;
+      }
+      e_G[lane] = gg;
+      e_b[lane] = be;
     }
     __syncthreads();
-    const int n_fold = s_n;
-    for (int f = 0; f < n_fold; ++f) {
-      const int x = s_list[f];
-      const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-      const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-      const RingPos rp = ring_pos(R, p.slot_map[b]);
-      const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
 
-      // ---- the checkpoint tile in the accumulator layout (lane offset made
-      // opaque per unit so the addresses are not hoisted out of the unit loop)
-      const int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
-      const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
-          static_cast<ST*>(p.pool) + unit * (int64_t)(D * D), 0, D * D * SB, 0x00020000);
-      float s0[NI][NJ][4];
+    if (cnt > 0) {
+      const float Gn = e_G[15];  // gates past cnt are zero: entry 15 carries G_cnt
+      // ---- K K^T; element r of lane (c, g) is (4 g + r, c)
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int s4 = 0; s4 < D / 4; ++s4) {
+        const float a = e_kt[(4 * s4 + g) * KTS + c];
+        kk = __builtin_amdgcn_mfma_f32_16x16x4f32(a, a, kk, 0, 0, 0);
+      }
+      // M = I + diag(beta) F, strictly lower part (the unit diagonal is implicit)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        s_m[i * 17 + c] = c < i ? e_b[i] * exp_neg(e_G[i] - e_G[c]) * kk[r] : 0.f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // X = M^-1 by forward substitution (lane c < 16 owns column c), then
+      // the factor X diag(beta) replaces M in place
+      if (lane < 16) {
+        int cz = c;  // opaque: keeps the 16 identity entries from being held across units
+        asm volatile("" : "+v"(cz));
+        float xc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = i == cz ? 1.f : 0.f;
+#pragma unroll
+          for (int k = 0; k < i; ++k) v = fmaf(-s_m[i * 17 + k], xc[k], v);
+          xc[i] = v;
+        }
+        const float bc = e_b[c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_m[i * 17 + c] = xc[i] * bc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // ---- K S0 for this wave's columns, reduction over rows {16 I + 4 g + r}
+      f32x4 ks[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) ks[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int I = 0; I < NI; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = e_kt[(16 * I + 4 * g + r) * KTS + c];
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) ks[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], ks[jj], 0, 0, 0);
+        }
+      // ---- R = V - diag(e^G) K S0, then d = factor . R (reduction over entries
+      // {4 g + r}), each row scaled by e^{G_n - G_e} for the update
+      f32x4 u[NJ];
+      float eGe[4], wGe[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float Ge = e_G[4 * g + r];
+        eGe[r] = exp_neg(Ge);
+        wGe[r] = exp_neg(Gn - Ge);
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int col = 16 * (NJ * wave + jj) + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ks[jj][r] = e_v[(4 * g + r) * VS + col] - eGe[r] * ks[jj][r];
+        u[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          u[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_m[c * 17 + 4 * g + r], ks[jj][r], u[jj], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[jj][r] *= wGe[r];
+      }
+      // ---- S_n = e^{G_n} S0 + K^T (scaled d), reduction over entries {4 g + r}
+      const float eGn = exp_neg(Gn);
+#pragma unroll
+      for (int I = 0; I < NI; ++I) {
+        f32x4 acc[NJ];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[jj][r] = eGn * s0[I][jj][r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = e_k[(4 * g + r) * VS + 16 * I + c];
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, u[jj][r], acc[jj], 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
+      }
+      // ---- write back, rounded once
 #pragma unroll
       for (int I = 0; I < NI; ++I)
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB);
-
-      // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
-      const int64_t ring_e = unit * L;
-      const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
-      for (int q = tid; q < 16 * CPR; q += NTH) {
-        const int t = q / CPR, cc = (q - t * CPR) * VE;
-        u32x4 kw = {0u, 0u, 0u, 0u}, vw = kw;
-        if (t < cnt) {
-          const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
-          kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
-          vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
-        }
+          for (int r = 0; r < 4; ++r)
+            st_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB, s0[I][jj][r],
+                     std::integral_constant<int, SDT>{});
+    }
+    if constexpr (CDT >= 0) {
+      const __amdgpu_buffer_rsrc_t rs_copy = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D), 0, D * D * 2, 0x00020000);
+      const int coff = (4 * g * D + NJ * 16 * wave + c) * 2;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          float kf, vf;
-          if constexpr (EB == 4) {
-            kf = __uint_as_float(kw[e]);
-            vf = __uint_as_float(vw[e]);
-          } else {
-            const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
-            const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
-            kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
-            vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
-          }
-          e_kt[(cc + e) * KTS + t] = kf;
-          e_k[t * VS + cc + e] = kf;
-          e_v[t * VS + cc + e] = vf;
-        }
-      }
-      if (wave == 0 && lane < 16) {  // gates in live order, zero past cnt; prefix sums within the row
-        float gg = 0.f, be = 0.f;
-        if (lane < cnt) {
-          const int64_t j = ring_e + (st + lane) % L;
-          gg = R.g[j];
-          be = R.beta[j];
-        }
+      for (int I = 0; I < NI; ++I)
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float y = __shfl_up(gg, off, 16);
-          if (lane >= off) gg += y;
-        }
-        e_G[lane] = gg;
-        e_b[lane] = be;
-      }
-      __syncthreads();
-
-      if (cnt > 0) {
-        const float Gn = e_G[15];  // gates past cnt are zero: entry 15 carries G_cnt
-        // ---- K K^T; element r of lane (c, g) is (4 g + r, c)
-        f32x4 kk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s4 = 0; s4 < D / 4; ++s4) {
-          const float a = e_kt[(4 * s4 + g) * KTS + c];
-          kk = __builtin_amdgcn_mfma_f32_16x16x4f32(a, a, kk, 0, 0, 0);
-        }
-        // M = I + diag(beta) F, strictly lower part (the unit diagonal is implicit)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          s_m[i * 17 + c] = c < i ? e_b[i] * exp_neg(e_G[i] - e_G[c]) * kk[r] : 0.f;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // X = M^-1 by forward substitution (lane c < 16 owns column c), then
-        // the factor X diag(beta) replaces M in place
-        if (lane < 16) {
-          int cz = c;  // opaque: keeps the 16 identity entries from being held across units
-          asm volatile("" : "+v"(cz));
-          float xc[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = i == cz ? 1.f : 0.f;
-#pragma unroll
-            for (int k = 0; k < i; ++k) v = fmaf(-s_m[i * 17 + k], xc[k], v);
-            xc[i] = v;
-          }
-          const float bc = e_b[c];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s_m[i * 17 + c] = xc[i] * bc;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- K S0 for this wave's columns, reduction over rows {16 I + 4 g + r}
-        f32x4 ks[NJ];
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) ks[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int I = 0; I < NI; ++I)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = e_kt[(16 * I + 4 * g + r) * KTS + c];
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) ks[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], ks[jj], 0, 0, 0);
-          }
-        // ---- R = V - diag(e^G) K S0, then d = factor . R (reduction over entries
-        // {4 g + r}), each row scaled by e^{G_n - G_e} for the update
-        f32x4 u[NJ];
-        float eGe[4], wGe[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float Ge = e_G[4 * g + r];
-          eGe[r] = exp_neg(Ge);
-          wGe[r] = exp_neg(Gn - Ge);
-        }
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int col = 16 * (NJ * wave + jj) + c;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ks[jj][r] = e_v[(4 * g + r) * VS + col] - eGe[r] * ks[jj][r];
-          u[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            u[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(s_m[c * 17 + 4 * g + r], ks[jj][r], u[jj], 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) u[jj][r] *= wGe[r];
-        }
-        // ---- S_n = e^{G_n} S0 + K^T (scaled d), reduction over entries {4 g + r}
-        const float eGn = exp_neg(Gn);
-#pragma unroll
-        for (int I = 0; I < NI; ++I) {
-          f32x4 acc[NJ];
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[jj][r] = eGn * s0[I][jj][r];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = e_k[(4 * g + r) * VS + 16 * I + c];
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, u[jj][r], acc[jj], 0, 0, 0);
-          }
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
-        }
-        // ---- write back, rounded once
-#pragma unroll
-        for (int I = 0; I < NI; ++I)
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              st_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB, s0[I][jj][r],
-                       std::integral_constant<int, SDT>{});
-      }
-      if constexpr (CDT >= 0) {
-        const __amdgpu_buffer_rsrc_t rs_copy = __builtin_amdgcn_make_buffer_rsrc(
-            static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D), 0, D * D * 2, 0x00020000);
-        const int coff = (4 * g * D + NJ * 16 * wave + c) * 2;
-#pragma unroll
-        for (int I = 0; I < NI; ++I)
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              st_state(rs_copy, coff, ((16 * I + r) * D + 16 * jj) * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
-      }
-      __syncthreads();  // LDS staging is reused by the next unit
+            st_state(rs_copy, coff, ((16 * I + r) * D + 16 * jj) * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
     }
-    __syncthreads();  // s_list is rewritten by the next check
-  }
+    __syncthreads();  // LDS staging is reused by the next unit
+  });
 }
 
 // ---------------------------------------------------------------- prep

@@ -348,6 +348,25 @@ def test_replay_layer_staggered_rings(sdt):
     c.check_state("end")
 
 
+@pytest.mark.parametrize("D", [16, 32, 64])
+def test_replay_more_sequences_than_one_fold_plan_window(D):
+    """4100 sequences: the fold kernels list the folding sequences in windows of 4096, so the
+    last four sit in a second window.  Each fold kernel (rows at D = 16, columns at 32, MFMA at
+    64) runs aligned folds, then staggered ones after a seeded rollback; sampled rows on both
+    sides of the window boundary are checked against the oracle."""
+    B, L = 4100, 4
+    r = gen.rejected_counts(15, 0, B, L - 1)
+    rows = [0, 1, 2047, 4095, 4096, 4097, 4099]
+    c = ReplayCase(15, B, 1, 1, D, L, "f32", B + 16, sample=rows)
+    for step in range(2 * L):  # every ring folds at step L and is full again after step 2 L - 1
+        c.step(step, 1)
+    c.check_state("aligned fold")
+    c.rollback(2 * L, r)  # counts 1..4
+    for step in range(2 * L + 1, 4 * L + 1):
+        c.step(step, 1)
+    c.check_state("staggered folds")
+
+
 def test_replay_on_a_side_stream_with_internal_workspace():
     """A call on a stream other than the current one, with the workspace and output allocated by
     the binding: equal, bit for bit, to the same steps on the current stream."""
