@@ -977,38 +977,26 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
 #pragma unroll
       for (int e = 0; e < 4; ++e) res[J][e] = h0[J][e] + h1[J][e];
   };
-  // rows 16 I.. of (fp32 rows in a2) x (fp32 B^T rows at bt, row stride LTF), both
-  // column tiles; both blocks' B reads are issued before the MFMAs
-  auto f32_tiles = [&](const f32x4* a2, const float* bt, f32x4* acc) {
-    f32x4 bv[2][2][2];
+  // acc[J] += (rows 16 I.. of T or P, registers) (B^T rows 16 J + li at bt, row
+  // stride LTF) for both column tiles.  T and P are lower triangular, so row
+  // block IC contracts over token blocks 0..IC only; lane (li, kk) holds
+  // tokens 16 m + 4 kk + s of block m, which MFMA s contracts.  The B reads
+  // are issued before the MFMAs.
+  auto tri_tiles = [&](auto Ic, const f32x4* a2, const float* bt, f32x4* acc) {
+    constexpr int IC = decltype(Ic)::value;
+    f32x4 bv[IC + 1][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int m = 0; m <= IC; ++m)
 #pragma unroll
-      for (int J = 0; J < 2; ++J) {
-        const float* B = bt + (16 * J + li) * LTF + 8 * kk + 32 * b;
-        bv[b][J][0] = ld4(B);
-        bv[b][J][1] = ld4(B + 4);
-      }
+      for (int J = 0; J < 2; ++J) bv[m][J] = ld4(bt + (16 * J + li) * LTF + 16 * m + 4 * kk);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float a[8];
+    for (int m = 0; m <= IC; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = a2[2 * b][e];
-        a[4 + e] = a2[2 * b + 1][e];
-      }
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int J = 0; J < 2; ++J) {
-        float bb[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bb[e] = bv[b][J][0][e];
-          bb[4 + e] = bv[b][J][1][e];
-        }
-        acc[J] = mfma8(acc[J], a, bb);
-      }
-    }
+        for (int J = 0; J < 2; ++J)
+          acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[m][e], bv[m][J][e], acc[J], 0, 0, 0);
   };
   auto load_rows = [&](const void* src, int c, u32x4* a1) {  // K or Q rows 16 I + li
     const int r = min(arow, chunk_len(c) - 1);
@@ -1016,16 +1004,18 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
 #pragma unroll
     for (int b = 0; b < KB; ++b) a1[b] = *reinterpret_cast<const u32x4*>(q + 32 * b);
   };
-  auto load_mat = [&](int c, int which, f32x4* a2) {  // T (which 0) or P (which 1) rows 16 I + li
-    const float* q = chunk_ws(c) + which * kC * kC + arow * kC + 8 * kk;
+  // T (which 0) or P (which 1) rows 16 I + li, token blocks 0..IC (the blocks
+  // above the diagonal are zero)
+  auto load_tri = [&](auto Ic, int c, int which, f32x4* a2) {
+    constexpr int IC = decltype(Ic)::value;
+    const float* q = chunk_ws(c) + which * kC * kC + arow * kC + 4 * kk;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      a2[2 * b] = ld4(q + 32 * b);
-      a2[2 * b + 1] = ld4(q + 32 * b + 4);
-    }
+    for (int m = 0; m <= IC; ++m) a2[m] = ld4(q + 16 * m);
   };
 
-  if (wave < 4) {
+  // The K and Q roles are built once per row block (IC = wave mod 4), so that
+  // every wave issues a fixed set of T or P loads and MFMAs.
+  auto k_role = [&](auto Ic) {
     // ================================================================ K role
     u32x4 a1[KB];
     f32x4 a2[4];
@@ -1046,7 +1036,7 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
       }
     };
     load_v(0);
-    load_mat(0, 0, a2);
+    load_tri(Ic, 0, 0, a2);
     __syncthreads();
     read_rows(0);
     for (int c = 0; c < nch; ++c) {
@@ -1072,8 +1062,8 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
       __syncthreads();
       {  // P2: U = T R; U^T in fp32 and diag(dec) U as three bf16 planes
         f32x4 u[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        f32_tiles(a2, s_Rt, u);
-        load_mat(cn, 0, a2);
+        tri_tiles(Ic, a2, s_Rt, u);
+        load_tri(Ic, cn, 0, a2);
         read_rows(c + 1);  // committed before the first barrier of this chunk
         const f32x4 dc = ld4(g + 3 * kC + tb);
 #pragma unroll
@@ -1092,13 +1082,14 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
       __syncthreads();
       __syncthreads();
     }
-  } else if (wave < 8) {
+  };
+  auto q_role = [&](auto Ic) {
     // ================================================================ Q role
     u32x4 a1[KB];
     f32x4 a2[4];
     const int ob = p.out_dt == GDN_F32 ? 4 : 2;
     load_rows(p.q, 0, a1);
-    load_mat(0, 1, a2);
+    load_tri(Ic, 0, 1, a2);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
       const int t0 = seq_lo + c * kC;
@@ -1116,8 +1107,8 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
         for (int J = 0; J < 2; ++J)
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[J][e] = eg[e] * qs[J][e];
-        f32_tiles(a2, s_Ut, o);
-        load_mat(cn, 1, a2);
+        tri_tiles(Ic, a2, s_Ut, o);
+        load_tri(Ic, cn, 1, a2);
         // rows t0 .. t0 + L - 1 of the output; stores past the end are dropped
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             static_cast<char*>(p.out) + (int64_t)t0 * p.Hv * D * ob, (short)0, L * p.Hv * D * ob, 0x00020000);
@@ -1130,6 +1121,25 @@ __global__ void __launch_bounds__(kS16Threads) gdn_prefill_state_bf16_kernel(con
           }
       }
       __syncthreads();
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (wave < 4) {
+    switch (I) {
+      case 0: k_role(I0{}); break;
+      case 1: k_role(I1{}); break;
+      case 2: k_role(I2{}); break;
+      default: k_role(I3{}); break;
+    }
+  } else if (wave < 8) {
+    switch (I) {
+      case 0: q_role(I0{}); break;
+      case 1: q_role(I1{}); break;
+      case 2: q_role(I2{}); break;
+      default: q_role(I3{}); break;
     }
   } else {
     // ================================================================ S role
@@ -1257,11 +1267,12 @@ static hipError_t launch_state16(const PrefillArgs& a, int state_dt, unsigned gr
 template <int D, int EB, int C>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int state_dt, float* ws, hipStream_t s) {
   const int64_t ncs = prefill_chunk_slots(a.N, a.total_tokens, C);
+  constexpr bool k_contig = EB == 2 && (D == 64 || D == 128) && C == kC;
   hipLaunchKernelGGL((gdn_prefill_chunk_kernel<D, EB, C>), dim3((unsigned)ncs, (unsigned)a.Hk), dim3(256), 0, s, a, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)a.N * a.Hv;
-  if constexpr (EB == 2 && (D == 64 || D == 128) && C == kC) {  // 16-bit inputs, wide heads: the k-contiguous kernel
+  if constexpr (k_contig) {  // 16-bit inputs, wide heads: the k-contiguous kernel
     const int64_t groups = (int64_t)a.N * a.Hk;
     const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * (a.Hv / a.Hk) * (D / 32));
     return a.in_dt == GDN_BF16 ? launch_state_bf16<D>(a, state_dt, grid, ws, s)
