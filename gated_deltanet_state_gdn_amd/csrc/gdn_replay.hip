@@ -497,8 +497,11 @@ __host__ __device__ inline size_t replay_fold_mfma_lds_bytes(int D) {
   return ((size_t)D * kFoldKTS + 2 * 16 * ((size_t)D + 4) + 2 * 16 + 4 * 16 * 17) * sizeof(float);
 }
 
+// Built for three workgroups per CU: at four (128 VGPRs) the kernel spilled
+// registers to scratch, and at three it folds as fast or faster (fp32 fold
+// steps 453-467 us against 454-482, bf16 373-396 against 372-407).
 template <int SDT, int D, bool NT, int EB, int CDT>
-__global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
+__global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
   static_assert(D == 64 || D == 128, "four waves of 16-column blocks");
   constexpr int NI = D / 16;  // row blocks
   constexpr int NJ = D / 64;  // column blocks per wave
@@ -545,9 +548,14 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
     const RingPos rp = ring_pos(R, p.slot_map[b]);
     const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
 
-    // ---- the checkpoint tile in the accumulator layout (lane offset made
-    // opaque per unit so the addresses are not hoisted out of the unit loop)
-    const int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
+    // ---- the checkpoint tile in the accumulator layout.  Element (16 I + r,
+    // 16 jj) of a lane takes the row block's offset as the scalar offset (NI
+    // values) and lane offset + (r D + 16 jj) as the vector one.  The lane
+    // offset is made opaque here and again before the write-back, so those
+    // NJ 4 vector offsets live only around the loads and around the stores
+    // (as 4 NI NJ scalar offsets the constants spilled).
+    int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
+    asm volatile("" : "+v"(lane_off));
     const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<ST*>(p.pool) + unit * (int64_t)(D * D), 0, D * D * SB, 0x00020000);
     float s0[NI][NJ][4];
@@ -556,7 +564,7 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB);
+        for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off + (r * D + 16 * jj) * SB, 16 * I * D * SB);
 
     // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
     const int64_t ring_e = unit * L;
@@ -697,26 +705,29 @@ __global__ void __launch_bounds__(256, EB == 2 ? 4 : 3) gdn_replay_fold_mfma_ker
           for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
       }
       // ---- write back, rounded once
+      int lane_st = lane_off;
+      asm volatile("" : "+v"(lane_st));
 #pragma unroll
       for (int I = 0; I < NI; ++I)
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            st_state(rs_tile, lane_off, ((16 * I + r) * D + 16 * jj) * SB, s0[I][jj][r],
+            st_state(rs_tile, lane_st + (r * D + 16 * jj) * SB, 16 * I * D * SB, s0[I][jj][r],
                      std::integral_constant<int, SDT>{});
     }
     if constexpr (CDT >= 0) {
       const __amdgpu_buffer_rsrc_t rs_copy = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<uint16_t*>(P.read_pool) + unit * (int64_t)(D * D), 0, D * D * 2, 0x00020000);
-      const int coff = (4 * g * D + NJ * 16 * wave + c) * 2;
+      int coff = (4 * g * D + NJ * 16 * wave + c) * 2;
+      asm volatile("" : "+v"(coff));
 #pragma unroll
       for (int I = 0; I < NI; ++I)
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            st_state(rs_copy, coff, ((16 * I + r) * D + 16 * jj) * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
+            st_state(rs_copy, coff + (r * D + 16 * jj) * 2, 16 * I * D * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
     }
     __syncthreads();  // LDS staging is reused by the next unit
   });
