@@ -52,17 +52,17 @@ def test_mamba2_decode_parity(sdt, d, n):
         assert_close(got[s], ref[i], sdt, f"state slot {s}")
 
 
-@pytest.mark.parametrize("in_dt", ["bf16", "f32"])
-def test_mamba2_decode_full_heads_persistent_walk(in_dt):
-    """The benchmark layer's heads (128 of 64 x 128 in 8 groups, fp32 state) at B = 24: 3072
-    units, about twelve per workgroup of the persistent kernel, three padded rows spread through
-    the walk; 2 steps, every element."""
+@pytest.mark.parametrize("in_dt", ["bf16", "f32", "f16"])
+def test_mamba2_decode_full_heads_padded_rows(in_dt):
+    """The benchmark layer's heads (128 of 64 x 128 in 8 groups, fp32 state) at B = 40: 5120
+    workgroups of the one-shot kernel, with padded rows (-1 and past the pool) spread through
+    the batch, two of them back to back; 2 steps, every element."""
     import torch
     import gated_deltanet_state_gdn_amd as gdn
     lay = gen.M2_LAYER
-    cid, B, H, G, d, n, num_slots = 81, 24, lay["H"], lay["G"], lay["d"], lay["n"], 32
+    cid, B, H, G, d, n, num_slots = 81, 40, lay["H"], lay["G"], lay["d"], lay["n"], 48
     slot_map = gen.slot_permutation(cid, num_slots)[:B].copy()
-    slot_map[[2, 11, 23]] = [-1, num_slots, -4]
+    slot_map[[2, 11, 12, 39]] = [-1, num_slots, -4, num_slots + 5]
     valid = [int(s) for s in slot_map if 0 <= s < num_slots]
     pool_d, states = poisoned_pool(num_slots, H, d, n, "f32", valid, cid)
     ref = states
