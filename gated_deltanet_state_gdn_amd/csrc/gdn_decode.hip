@@ -1,5 +1,7 @@
-// Single-token GDN decode: one workgroup per (sequence, value head) streams the
-// dk x dv state tile once in and once out.
+// Single-token GDN decode: each (sequence, value head) streams its dk x dv
+// state tile once in and once out, one workgroup per tile (the one-shot
+// kernel) or, for fp32 128 x 128 tiles, one workgroup per CU walking the tiles
+// (the persistent kernel below).
 //
 // Operation (vLLM PR #52191 page, implementation item 3, the fused
 // sigmoid-gating delta-rule update; item 4, FP32 math with one rounding per

@@ -4,8 +4,8 @@
 // the Gated Delta Networks paper, restated here for this library's dk x dv
 // state; vLLM PR #52191 page, implementation items 3-4: the inter-chunk
 // recurrence runs its GEMMs in FP32 and scales chunk states by exp(g_last)).
-// Within a chunk of C = 64 tokens t = 0..C-1 (counted from the sequence start
-// of this call), with gamma_t = g_0 + ... + g_t and S the state entering the
+// Within a chunk of C tokens t = 0..C-1 (C = 16, 32 or 64; counted from the
+// sequence start of this call), with gamma_t = g_0 + ... + g_t and S the state entering the
 // chunk, every token's update unrolls to
 //     S_t = e^{gamma_t} S + sum_{s<=t} e^{gamma_t - gamma_s} k_s u_s^T
 // where the pseudo-values u solve the unit lower-triangular system
@@ -19,8 +19,9 @@
 // overflows however strong the decay.  A partial last chunk is padded with
 // k = q = v = 0, g = 0, beta = 0, which leaves every formula exact.
 //
-// Kernel 1 (chunk-parallel, one workgroup per (chunk, value head)): gates,
-// gamma, A and P by MFMA, T by blocked inversion (16x16 diagonal blocks by
+// Kernel 1 (chunk-parallel, one workgroup per (chunk, key head), for the key
+// head's value heads): K K^T and Q K^T once, then per value head its gates,
+// gamma, A and P, and T by blocked inversion (16x16 diagonal blocks by
 // substitution in registers, off-diagonal blocks by MFMA products), written to
 // the workspace.  Kernel 2 (sequential over chunks, one workgroup per
 // (sequence, value head, 32-column dv block); each dv column of S evolves on

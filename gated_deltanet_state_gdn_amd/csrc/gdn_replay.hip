@@ -5,10 +5,11 @@
 // a unit owns its checkpoint tile, its ring entries and its ring pointers.
 //
 // A step of T tokens runs three kernels:
-//   fold   - if count + T > L, fold the committed entries into S0 (sequential
-//            rank-1 updates on the tile held in VGPRs), write S0 back rounded
-//            once and empty the ring; a persistent grid checks 64 units per
-//            wave at a time, so a step without folds costs one check per unit;
+//   fold   - if count + T > L, fold the committed entries into S0 (on the tile
+//            held in VGPRs), write S0 back rounded once and empty the ring; a
+//            persistent grid lists the folding sequences from the ring counts
+//            and spreads their units evenly, so a step without folds costs one
+//            pass over the counts;
 //   prep   - stage the live entries and the window, compute per window
 //            position t the vectors w_t and acc_t below, append the window
 //            to the ring;
