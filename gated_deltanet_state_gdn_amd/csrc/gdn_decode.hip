@@ -93,13 +93,16 @@ gdn_decode_kernel(const DecodeArgs p) {
   const float alpha = expf(g);
 
   const int64_t kq_base = ((int64_t)b * p.Hk + hk) * D;
-  for (int i = tid; i < D; i += NT_THREADS) {
-    s_k[i] = load_elem(p.k, kq_base + i, p.in_dt);
-    s_q[i] = load_elem(p.q, kq_base + i, p.in_dt);
-  }
-  float vv[VEC];
+  if (tid < 2 * (D / 8)) {  // k and q staged 8 elements per lane (one access each)
+    const int which = tid / (D / 8), i = (tid - which * (D / 8)) * 8;
+    float f[8];
+    load_vec<8>(which ? p.q : p.k, kq_base + i, p.in_dt, f);
+    float* dst = (which ? s_q : s_k) + i;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) vv[e] = load_elem(p.v, row_bh * D + c0 + e, p.in_dt);
+    for (int e = 0; e < 8; ++e) dst[e] = f[e];
+  }
+  float vv[VEC];  // this lane's VEC values in one access (16-bit tiles are bound by memory instructions)
+  load_vec<VEC>(p.v, row_bh * D + c0, p.in_dt, vv);
   __syncthreads();
 
   float kvp[VEC], qsp[VEC];
@@ -147,7 +150,7 @@ gdn_decode_kernel(const DecodeArgs p) {
       for (int w = 0; w < IO::WORDS; ++w) asm volatile("" : "+v"(raw[pp][w]));
   }
   const float kq = s_kq;
-  float delta[VEC];
+  float delta[VEC], o[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     float kv = 0.f, qs = 0.f;
@@ -157,9 +160,10 @@ gdn_decode_kernel(const DecodeArgs p) {
       qs += s_red[1][w][c0 + e];
     }
     delta[e] = beta * (vv[e] - alpha * kv);
-    if (wave == 0 && lane < LPR)
-      store_elem(p.out, row_bh * D + c0 + e, p.scale * fmaf(alpha, qs, kq * delta[e]), p.out_dt);
+    o[e] = p.scale * fmaf(alpha, qs, kq * delta[e]);
   }
+  if (wave == 0 && lane < LPR)  // the row's outputs, one access per 16 bytes when out is 16-byte aligned
+    store_vec<VEC>(p.out, row_bh * D + c0, o, p.out_dt, (reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
 
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) {

@@ -69,6 +69,68 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float x, int dt) 
   }
 }
 
+// N = 4 or 8 consecutive elements from element i of a run-time-dtype tensor,
+// in one vector access per 16 bytes: the caller guarantees N x element bytes
+// alignment of element i (a 16-byte-aligned array and i a multiple of N).  A
+// per-element loop issues N memory instructions, each an address pass of the
+// texture addresser, which bounds the 16-bit decode tiles' kernels.
+template <int N>
+__device__ __forceinline__ void load_vec(const void* p, int64_t i, int dt, float (&f)[N]) {
+  static_assert(N == 4 || N == 8, "4 or 8 elements");
+  if (dt == GDN_F32) {
+    const float* q = static_cast<const float*>(p) + i;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(q + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[e + j] = w[j];
+    }
+    return;
+  }
+  const uint16_t* q = static_cast<const uint16_t*>(p) + i;
+  uint32_t w[N / 2];
+  if constexpr (N == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = v[j];
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(q);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    f[2 * j] = dt == GDN_BF16 ? unpack_lo<GDN_BF16>(w[j]) : unpack_lo<GDN_F16>(w[j]);
+    f[2 * j + 1] = dt == GDN_BF16 ? unpack_hi<GDN_BF16>(w[j]) : unpack_hi<GDN_F16>(w[j]);
+  }
+}
+
+// N = 4 or 8 consecutive elements stored at element i of a run-time-dtype
+// tensor, rounded once: one vector access per 16 bytes when that is aligned
+// (`vec`, uniform), else one access per element.
+template <int N>
+__device__ __forceinline__ void store_vec(void* p, int64_t i, const float (&f)[N], int dt, bool vec) {
+  static_assert(N == 4 || N == 8, "4 or 8 elements");
+  if (!vec) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) store_elem(p, i + e, f[e], dt);
+    return;
+  }
+  if (dt == GDN_F32) {
+    float* q = static_cast<float*>(p) + i;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) *reinterpret_cast<f32x4*>(q + e) = f32x4{f[e], f[e + 1], f[e + 2], f[e + 3]};
+    return;
+  }
+  uint32_t w[N / 2];
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j)
+    w[j] = dt == GDN_BF16 ? pack2<GDN_BF16>(f[2 * j], f[2 * j + 1]) : pack2<GDN_F16>(f[2 * j], f[2 * j + 1]);
+  uint16_t* q = static_cast<uint16_t*>(p) + i;
+  if constexpr (N == 8) *reinterpret_cast<u32x4*>(q) = u32x4{w[0], w[1], w[2], w[3]};
+  else *reinterpret_cast<u32x2*>(q) = u32x2{w[0], w[1]};
+}
+
 // Raw copy of one element (ring append keeps the input bytes bit-exact).
 __device__ __forceinline__ void copy_elem(void* dst, int64_t di, const void* src, int64_t si, int dt) {
   if (dt == GDN_F32) {
