@@ -68,21 +68,32 @@ __device__ __forceinline__ M2Pos m2_pos(const M2Args& a, int64_t slot) {
 }
 
 // ---------------------------------------------------------------- decode
+// x (P values) is staged in LDS and the row outputs gathered there, so both
+// move with one vector access per 8 elements, and B and C load VEC elements
+// per access: per-element loads and stores cost the texture addresser an
+// address pass each, which bounds these 32 KiB tiles as it does the 16-bit
+// GDN ones.  Unaligned x, B, C or y take the per-element accesses.
 template <int SDT, int P, int N, bool NT>
 __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kernel(const M2Args a) {
   using G = M2G<SDT, P, N>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
+  static_assert(P % 8 == 0 && P / 8 <= NW * 64, "x staged 8 values per lane");
   using IO = TileIO<SDT, VEC, NT>;
   using ST = typename StateElem<SDT>::T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float s_x[P], s_y[P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
   const int gr = h / (a.H / a.G);
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
   const int64_t yb = ((int64_t)b * a.H + h) * P;
   const int slot = a.slot_map[b];
+  const bool vy = (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
   if (slot < 0 || (int64_t)slot >= a.num_slots) {  // padded row
-    for (int i = threadIdx.x; i < P; i += NW * 64) store_elem(a.y, yb + i, 0.f, a.out_dt);
+    if (tid < P / 8) {
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      store_vec<8>(a.y, yb + 8 * tid, z, a.out_dt, vy);
+    }
     return;
   }
   ST* tile = static_cast<ST*>(a.pool) + ((int64_t)slot * a.H + h) * (int64_t)(P * N);
@@ -90,20 +101,39 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kerne
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * N + c0);
 
+  if (tid < P / 8) {
+    float f[8];
+    if ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0) {
+      load_vec<8>(a.x, yb + 8 * tid, a.in_dt, f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = load_elem(a.x, yb + 8 * tid + e, a.in_dt);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_x[8 * tid + e] = f[e];
+  }
   const float dtp = softplus_f(load_elem(a.dt, (int64_t)b * a.H + h, a.in_dt) + a.dt_bias[h]);
   const float alpha = expf(-expf(a.A_log[h]) * dtp);
   const float Dh = a.Dskip[h];
   const int64_t bc = ((int64_t)b * a.G + gr) * N + c0;
   float Bc[VEC], Cc[VEC];
+  if (((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) & 15) == 0) {
+    load_vec<VEC>(a.Bm, bc, a.in_dt, Bc);
+    load_vec<VEC>(a.Cm, bc, a.in_dt, Cc);
+  } else {
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    Bc[e] = dtp * load_elem(a.Bm, bc + e, a.in_dt);
-    Cc[e] = load_elem(a.Cm, bc + e, a.in_dt);
+    for (int e = 0; e < VEC; ++e) {
+      Bc[e] = load_elem(a.Bm, bc + e, a.in_dt);
+      Cc[e] = load_elem(a.Cm, bc + e, a.in_dt);
+    }
   }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) Bc[e] *= dtp;
+  __syncthreads();
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) {
     const int r = r0 + pp * NW * RPW;
-    const float xr = load_elem(a.x, yb + r, a.in_dt);
+    const float xr = s_x[r];
     float s[VEC];
     IO::widen(raw[pp], s);
     float part = 0.f;
@@ -114,7 +144,14 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kerne
     }
     IO::store(tile + r * N + c0, s);
     part = row_sum<LPR>(part);
-    if ((lane % LPR) == 0) store_elem(a.y, yb + r, fmaf(Dh, xr, part), a.out_dt);
+    if ((lane % LPR) == 0) s_y[r] = fmaf(Dh, xr, part);
+  }
+  __syncthreads();
+  if (tid < P / 8) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = s_y[8 * tid + e];
+    store_vec<8>(a.y, yb + 8 * tid, f, a.out_dt, vy);
   }
 }
 
