@@ -251,12 +251,22 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
     else return f16_bits_to_f32(x);
   };
   auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
+  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
   // the values of this lane's columns, packed as loaded (VEC inputs in one access)
   typedef unsigned int VRaw __attribute__((ext_vector_type(VEC * sizeof(IT) / 4)));
+  // The RPW key (or query) elements of one pass's rows of this wave, adjacent
+  // in memory, in one access: lane j < PASSES holds the keys of pass j, lane
+  // PASSES + j the queries (the other lanes repeat lane 0's).  One load per
+  // wave replaces 2 PASSES per-element ones; each lane takes its row's element
+  // with a lane read.
+  constexpr int KQWORDS = RPW * (int)sizeof(IT) / 4;
+  static_assert(RPW * sizeof(IT) % 4 == 0 && KQWORDS <= 4 && 2 * PASSES <= 64, "row-group key loads");
+  typedef unsigned int KQW __attribute__((ext_vector_type(KQWORDS)));
   struct In {
     Raw raw[PASSES];
     VRaw vv;
-    uint32_t kr[PASSES], qr[PASSES], ga, gb;
+    KQW kq;
+    uint32_t ga, gb;
   };
   // Every load is issued unconditionally (a branch around them would make the
   // compiler wait for all loads in flight where the paths join): a padded row's
@@ -274,10 +284,10 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
       x.raw[pp] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
                                               rs, (r0 * D + c0) * (int)sizeof(ST),
                                               pp * NW * RPW * D * (int)sizeof(ST), NTL ? 2 : 0));
-#pragma unroll
-    for (int pp = 0; pp < PASSES; ++pp) {
-      x.kr[pp] = kin[kq_base + r0 + pp * NW * RPW];
-      x.qr[pp] = qin[kq_base + r0 + pp * NW * RPW];
+    {
+      const bool isq = lane >= PASSES && lane < 2 * PASSES;
+      const int jp = lane < 2 * PASSES ? lane % PASSES : 0;
+      x.kq = *reinterpret_cast<const KQW*>((isq ? qin : kin) + kq_base + RPW * wave + NW * RPW * jp);
     }
     x.vv = *reinterpret_cast<const VRaw*>(vin + row_bh * D + c0);
     x.ga = ain[row_bh + zl];
@@ -288,6 +298,20 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
   // a wave may run ahead through it to the next live tile while a slower wave
   // still reads the k . q partials of the previous one: the two live tiles
   // must use different buffers, whatever the padded tiles between them.
+  // element of this lane's row (lane / LPR within the group) from lane j's row group
+  auto kq_at = [&](const KQW& w, int j) -> uint32_t {
+    const int i = lane / LPR;
+    uint32_t word[KQWORDS];
+#pragma unroll
+    for (int q = 0; q < KQWORDS; ++q) word[q] = __builtin_amdgcn_readlane(w[q], j);
+    if constexpr (IDT == GDN_F32) {
+      return word[i];
+    } else {
+      const uint32_t v = word[i >> 1];
+      return (i & 1) ? (v >> 16) : (v & 0xffffu);
+    }
+  };
+
   In cur, nxt;
   fetch(t, s_slot[0], cur);
   for (int it = 0, par = 0; t < units; t += G, ++it) {
@@ -309,8 +333,8 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
       for (int e = 0; e < VEC; ++e) kvp[e] = qsp[e] = 0.f;
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) {
-        kr[pp] = widen(cur.kr[pp]);
-        const float qr = widen(cur.qr[pp]);
+        kr[pp] = widen(kq_at(cur.kq, pp));
+        const float qr = widen(kq_at(cur.kq, PASSES + pp));
         float sv[VEC];
         IO::widen(cur.raw[pp], sv);
 #pragma unroll
@@ -360,16 +384,16 @@ __global__ void __launch_bounds__(persist_waves<SDT>() * 64, 4) gdn_decode_persi
       float kq = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) kq += s_kqw[par][w];
-      float delta[VEC];
+      float delta[VEC], o[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float ve;
         if constexpr (IDT == GDN_F32) ve = __uint_as_float(cur.vv[e]);
         else ve = widen((e & 1) ? (cur.vv[e >> 1] >> 16) : (cur.vv[e >> 1] & 0xffffu));
         delta[e] = beta * (ve - alpha * kv[e]);
-        if (wave == 0 && lane < LPR)
-          store_elem(p.out, row_bh * D + c0 + e, p.scale * fmaf(alpha, qs[e], kq * delta[e]), p.out_dt);
+        o[e] = p.scale * fmaf(alpha, qs[e], kq * delta[e]);
       }
+      if (wave == 0 && lane < LPR) store_vec<VEC>(p.out, row_bh * D + c0, o, p.out_dt, out_vec);
       ST* tile = static_cast<ST*>(p.pool) + ((int64_t)slot_c * p.Hv + h) * (int64_t)(D * D);
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) {
