@@ -1255,7 +1255,7 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   constexpr int NTH = NW * 64;
   using IO = TileIO<SDT, VEC, NT>;
   using ST = typename StateElem<SDT>::T;
-  extern __shared__ float s_w[];  // [T][D]
+  extern __shared__ __align__(16) float s_w[];  // [T][D] (read 4 floats at a time)
   __shared__ float s_out[TB][NW][D];
 
   const DecodeArgs& p = P.d;
@@ -1278,9 +1278,9 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
   const float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
-  for (int i = tid; i < T * D; i += NTH) {
+  for (int i = 4 * tid; i < T * D; i += 4 * NTH) {  // 4 elements per access
     const int t = i / D, c = i - t * D;
-    s_w[t * D + c] = wsu[2 * t * D + c];
+    *reinterpret_cast<f32x4*>(s_w + t * D + c) = *reinterpret_cast<const f32x4*>(wsu + 2 * t * D + c);
   }
   __syncthreads();
 
@@ -1317,12 +1317,19 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < nt * D; i += NTH) {
+    const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+    for (int i = 4 * tid; i < nt * D; i += 4 * NTH) {  // 4 outputs per thread, one access each way
       const int tb = i / D, c = i - tb * D;
-      float o = wsu[(2 * (t0 + tb) + 1) * D + c];
+      const f32x4 acc = *reinterpret_cast<const f32x4*>(wsu + (2 * (t0 + tb) + 1) * D + c);
+      float o[4];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) o += s_out[tb][w][c];
-      store_elem(p.out, (((int64_t)b * T + t0 + tb) * p.Hv + h) * D + c, p.scale * o, p.out_dt);
+      for (int j = 0; j < 4; ++j) {
+        float x = acc[j];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += s_out[tb][w][c + j];
+        o[j] = p.scale * x;
+      }
+      store_vec<4>(p.out, (((int64_t)b * T + t0 + tb) * p.Hv + h) * D + c, o, p.out_dt, out_vec);
     }
     __syncthreads();
   }
@@ -1346,7 +1353,7 @@ __global__ void __launch_bounds__(kStreamPersistNW * 64, 4)
 gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   constexpr int D = 128, NW = kStreamPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
   static_assert(PASSES == 4, "four rows per lane");
-  static_assert(TMAX * D <= NW * 64, "one w / acc element per thread");
+  static_assert(TMAX * D <= 4 * NW * 64, "four w / acc elements per thread");
   typedef unsigned int Raw __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float s_red[2][TMAX][NW][D];  // [parity][position][wave][column]
   __shared__ __attribute__((aligned(16))) float s_sum[2][TMAX][D];      // [parity][position][column]
@@ -1365,16 +1372,19 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t + i * G) / p.Hv];
 
   auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
-  // thread tid < T D carries element tid of the unit's w and acc vectors (w_t, acc_t by position)
-  const int wi = tid < T * D ? tid : T * D - 1, wt = wi / D, wc = wi - wt * D;
+  // thread tid < T D / 4 carries elements 4 tid.. of the unit's w and acc vectors
+  // (w_t, acc_t by position), one access each
+  const bool wthr = tid < T * D / 4;
+  const int wi = wthr ? 4 * tid : 0, wt = wi / D, wc = wi - wt * D;
+  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
   struct In {
     Raw raw[PASSES];
-    float w, acc;
+    f32x4 w, acc;
   };
   auto fetch = [&](int u, int slot, In& x) {
     const float* wsu = ws + (int64_t)u * T * 2 * D;  // per position: w, then acc
-    x.w = wsu[2 * wt * D + wc];  // before the tile: waiting for these leaves the tile in flight
-    x.acc = wsu[(2 * wt + 1) * D + wc];
+    x.w = *reinterpret_cast<const f32x4*>(wsu + 2 * wt * D + wc);  // before the tile: waiting for these leaves the tile in flight
+    x.acc = *reinterpret_cast<const f32x4*>(wsu + (2 * wt + 1) * D + wc);
     const int h = u % p.Hv;
     const bool ok = valid(slot);
     const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
@@ -1389,9 +1399,9 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   In cur, nxt;
   __syncthreads();  // s_slot
   fetch(t, s_slot[0], cur);
-  if (tid < T * D) {
-    s_w[0][wt][wc] = cur.w;
-    s_acc[0][wt][wc] = cur.acc;
+  if (wthr) {
+    *reinterpret_cast<f32x4*>(&s_w[0][wt][wc]) = cur.w;
+    *reinterpret_cast<f32x4*>(&s_acc[0][wt][wc]) = cur.acc;
   }
   __syncthreads();
   for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
@@ -1432,14 +1442,17 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
       }
     }
     // the next unit's w and acc, published by the barrier below
-    if (tid < T * D) {
-      s_w[par ^ 1][wt][wc] = nxt.w;
-      s_acc[par ^ 1][wt][wc] = nxt.acc;
+    if (wthr) {
+      *reinterpret_cast<f32x4*>(&s_w[par ^ 1][wt][wc]) = nxt.w;
+      *reinterpret_cast<f32x4*>(&s_acc[par ^ 1][wt][wc]) = nxt.acc;
     }
     __syncthreads();
-    if (tid < T * D)  // position wt, column wc (padded rows: zeros)
-      store_elem(p.out, out_row(wt) + wc, live ? p.scale * (s_acc[par][wt][wc] + s_sum[par][wt][wc]) : 0.f,
-                 p.out_dt);
+    if (wthr) {  // position wt, columns wc.. (padded rows: zeros)
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = live ? p.scale * (s_acc[par][wt][wc + j] + s_sum[par][wt][wc + j]) : 0.f;
+      store_vec<4>(p.out, out_row(wt) + wc, o, p.out_dt, out_vec);
+    }
     cur = nxt;
   }
 }
