@@ -87,9 +87,10 @@ gdn_decode_kernel(const DecodeArgs p) {
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = TileIO<SDT, VEC, NT || NTL>::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
 
-  // gates (uniform over the workgroup)
-  const float g = gate_g(load_elem(p.a, row_bh, p.in_dt), p.A_log[h], p.dt_bias[h]);
-  const float beta = sigmoid_f(load_elem(p.b, row_bh, p.in_dt));
+  // gates (uniform over the workgroup): both inputs in one access, lane 0 reading a and lane 1 b
+  const uint32_t gab = __float_as_uint(load_elem(lane == 1 ? p.b : p.a, row_bh, p.in_dt));
+  const float g = gate_g(__uint_as_float(__builtin_amdgcn_readlane(gab, 0)), p.A_log[h], p.dt_bias[h]);
+  const float beta = sigmoid_f(__uint_as_float(__builtin_amdgcn_readlane(gab, 1)));
   const float alpha = expf(g);
 
   const int64_t kq_base = ((int64_t)b * p.Hk + hk) * D;
