@@ -143,8 +143,21 @@ __device__ __forceinline__ void copy_elem(void* dst, int64_t di, const void* src
 // ------------------------------------------------------------------ gates
 // g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b); softplus is the
 // exact max(x,0) + log1p(exp(-|x|)) (no threshold linearisation).
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+//
+// log1p(t) for t in [0, 1] by Goldberg's identity (D. Goldberg, "What every
+// computer scientist should know about floating-point arithmetic", 1991, Theorem
+// 4): with u = 1 + t rounded, log1p(t) = log(u) t / (u - 1) to a few ulps, since
+// the ratio t / (u - 1) undoes the rounding of u (u - 1 is exact).  u == 1 means
+// t is below half an ulp of 1, where log1p(t) rounds to t.  This replaces the
+// library log1p, whose double-float evaluation cost about 100 instructions per
+// lane in the kernels that form gates per lane.
+__device__ __forceinline__ float log1p_unit(float t) {
+  const float u = 1.f + t;
+  return u == 1.f ? t : logf(u) * (t * __builtin_amdgcn_rcpf(u - 1.f));
+}
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1p_unit(expf(-fabsf(x))); }
+// the hardware reciprocal (1 ulp) in place of a correctly rounded division
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + expf(-x)); }
 __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
   return -expf(A_log) * softplus_f(a + dt_bias);
 }

@@ -1065,12 +1065,20 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   // written by the fold's check) and the window queries (lane e: query e)
   const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
   const int slot = rc.x;
+  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
   u32x4 qx[NS];
   {
     const bool qv = e < T;
     const char* src = static_cast<const char*>(p.q) + (((int64_t)b * T + (qv ? e : 0)) * p.Hk + hk) * RB + coff;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qx[s] = qv ? *reinterpret_cast<const u32x4*>(src + 16 * s) : z4;
+    for (int s = 0; s < NS; ++s) {  // every lane loads (a valid row), so no branch splits the round
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + 16 * s);
+      qx[s] = qv ? x : z4;
+    }
+    // taken here, so the compiler issues the query loads beside the record load instead
+    // of after the record's test (that had made them a dependent round of their own)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qx[s]));
   }
   if (slot < 0) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
@@ -1092,33 +1100,49 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   // columns: row j is one load over the wave.
   const bool live = e < n_all, committed = e < cnt;
   const int tw = committed ? 0 : min(e - cnt, T - 1);
-  const int64_t rj = unit * L + (st + e) % L, krj = ring_key_base(p, slot, h, L) + (st + e) % L;
+  // ring position of live entry j: st < L and j < n_all <= L, so one subtraction wraps it
+  auto ring_at = [&](int j) { const int x = st + j; return x >= L ? x - L : x; };
+  const int pe = live ? ring_at(e) : 0;
+  const int64_t rj = unit * L + pe, krj = ring_key_base(p, slot, h, L) + pe;
   const char* ks = committed ? static_cast<const char*>(R.k) + krj * RB
                              : static_cast<const char*>(p.k) + (((int64_t)b * T + tw) * p.Hk + hk) * RB;
   u32x4 kx[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) kx[s] = live ? *reinterpret_cast<const u32x4*>(ks + coff + 16 * s) : z4;
+  for (int s = 0; s < NS; ++s) {  // a lane past the live entries reads window row T - 1
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ks + coff + 16 * s);
+    kx[s] = live ? x : z4;
+  }
+  // value rows through two buffer resources, the unit's ring entries and its
+  // window rows in the inputs, with the row's byte offset as the scalar offset
+  const __amdgpu_buffer_rsrc_t rs_vring = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<char*>(R.v) + unit * L * RB, 0, L * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_vwin = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(p.v)) + ((int64_t)b * T * p.Hv + h) * RB, 0,
+      ((T - 1) * p.Hv + 1) * RB, 0x00020000);
+  const int vstep = p.Hv * RB;
+  auto vcols = [&](__amdgpu_buffer_rsrc_t rs, int soff) -> uint32_t {
+    if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(rs, 2 * ccol, soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b16(rs, 2 * ccol, soff, 0);
+  };
   uint32_t vr[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     uint32_t x = 0u;
-    if (j < n_all) {  // uniform
-      const char* row = j < cnt ? static_cast<const char*>(R.v) + (unit * L + (st + j) % L) * RB
-                                : static_cast<const char*>(p.v) + (((int64_t)b * T + (j - cnt)) * p.Hv + h) * RB;
-      x = cols_at(row);
-    }
+    if (j < n_all) x = j < cnt ? vcols(rs_vring, ring_at(j) * RB) : vcols(rs_vwin, (j - cnt) * vstep);  // uniform
     vr[j] = x;
   }
-  float gl = 0.f, bl = 0.f;
-  if (live) {
-    if (committed) {
-      gl = R.g[rj];
-      bl = R.beta[rj];
-    } else {
-      const int64_t gi = ((int64_t)b * T + tw) * p.Hv + h;
-      gl = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
-      bl = sigmoid_f(load_elem(p.b, gi, p.in_dt));
-    }
+  // both gate sources are read in every lane (in range for any lane) and selected
+  float gl, bl;
+  {
+    float gr = R.g[rj], br = R.beta[rj];
+    const int64_t gi = ((int64_t)b * T + tw) * p.Hv + h;
+    // the input dtype as a constant: a run-time switch put a full wait between the two loads
+    float ga = load_elem(p.a, gi, IDT), gb = load_elem(p.b, gi, IDT);
+    // taken here, so that all four loads go out in this round (the compiler had sunk
+    // some of them into the branches below, each a dependent round of its own)
+    asm volatile("" : "+v"(gr), "+v"(br), "+v"(ga), "+v"(gb));
+    gl = live ? (committed ? gr : gate_g(ga, A_log, dt_bias)) : 0.f;
+    bl = live ? (committed ? br : sigmoid_f(gb)) : 0.f;
   }
 
   // ---- prefix sums G of g in live order (each 16-lane row alike)
@@ -1146,9 +1170,8 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j >= cnt && j < n_all) {  // uniform
-      char* row = static_cast<char*>(R.v) + (unit * L + (st + j) % L) * RB + 2 * ccol;
-      if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(row) = vr[j];
-      else *reinterpret_cast<uint16_t*>(row) = (uint16_t)vr[j];
+      if constexpr (CPL == 2) __builtin_amdgcn_raw_buffer_store_b32(vr[j], rs_vring, 2 * ccol, ring_at(j) * RB, 0);
+      else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)vr[j], rs_vring, 2 * ccol, ring_at(j) * RB, 0);
     }
   }
   if (lane == 0 && h == 0) {  // the slot's pointers, once per slot
