@@ -53,8 +53,8 @@ namespace gdn {
 template <int SDT, int D>
 using DecodeGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_DECODE_WAVES : GDN_DECODE_WAVES_16>;
 
-// NT: non-temporal stores (and loads); NTL: non-temporal loads
-template <int SDT, int D, bool NT, bool NTL>
+// NT: non-temporal stores (and loads); NTL: non-temporal loads; IDT: the input dtype
+template <int SDT, int D, bool NT, bool NTL, int IDT>
 __global__ void __launch_bounds__((DecodeGeom<SDT, D>::NW * 64))
 gdn_decode_kernel(const DecodeArgs p) {
   using G = DecodeGeom<SDT, D>;
@@ -83,27 +83,38 @@ gdn_decode_kernel(const DecodeArgs p) {
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;  // row of pass 0; pass pp adds pp * NW * RPW
 
+  // The small loads go out first, as raw bits: both gate inputs in one access
+  // (lane 0 reads a, lane 1 b), k and q for staging (8 elements per lane, one
+  // access each) and this lane's VEC values (one access).  Loads complete in
+  // order, so the waits for them do not cover the tile loads issued after.
+  const uint32_t gab = in_bits<IDT>(lane == 1 ? p.b : p.a, row_bh);
+  const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
+  const int64_t kq_base = ((int64_t)b * p.Hk + hk) * D;
+  const bool stager = tid < 2 * (D / 8);
+  const int which = tid / (D / 8), kq_i = (tid - which * (D / 8)) * 8;
+  InVec<IDT, 8> kqr;
+  if (stager) kqr.load(which ? p.q : p.k, kq_base + kq_i);
+  InVec<IDT, VEC> vr;
+  vr.load(p.v, row_bh * D + c0);
+
   typename IO::Raw raw[PASSES];
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = TileIO<SDT, VEC, NT || NTL>::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
 
-  // gates (uniform over the workgroup): both inputs in one access, lane 0 reading a and lane 1 b
-  const uint32_t gab = __float_as_uint(load_elem(lane == 1 ? p.b : p.a, row_bh, p.in_dt));
-  const float g = gate_g(__uint_as_float(__builtin_amdgcn_readlane(gab, 0)), p.A_log[h], p.dt_bias[h]);
-  const float beta = sigmoid_f(__uint_as_float(__builtin_amdgcn_readlane(gab, 1)));
+  // gates (uniform over the workgroup)
+  const float g = gate_g(in_value<IDT>(__builtin_amdgcn_readlane(gab, 0)), A_log, dt_bias);
+  const float beta = sigmoid_f(in_value<IDT>(__builtin_amdgcn_readlane(gab, 1)));
   const float alpha = expf(g);
 
-  const int64_t kq_base = ((int64_t)b * p.Hk + hk) * D;
-  if (tid < 2 * (D / 8)) {  // k and q staged 8 elements per lane (one access each)
-    const int which = tid / (D / 8), i = (tid - which * (D / 8)) * 8;
+  if (stager) {
     float f[8];
-    load_vec<8>(which ? p.q : p.k, kq_base + i, p.in_dt, f);
-    float* dst = (which ? s_q : s_k) + i;
+    kqr.widen(f);
+    float* dst = (which ? s_q : s_k) + kq_i;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = f[e];
   }
-  float vv[VEC];  // this lane's VEC values in one access (16-bit tiles are bound by memory instructions)
-  load_vec<VEC>(p.v, row_bh * D + c0, p.in_dt, vv);
+  float vv[VEC];
+  vr.widen(vv);
   __syncthreads();
 
   float kvp[VEC], qsp[VEC];
@@ -448,12 +459,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if (!NT && stream_tile_writes(tile_bytes))
-    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, true, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
-  else if (stream_tile_reads(tile_bytes))
-    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, true>), dim3(grid), dim3(G::NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((gdn_decode_kernel<SDT, D, NT, false>), dim3(grid), dim3(G::NW * 64), 0, s, a);
+  auto one_shot = [&](auto nt_c, auto ntl_c) {
+    constexpr bool N = decltype(nt_c)::value, L = decltype(ntl_c)::value;
+    void (*k)(const DecodeArgs) = a.in_dt == GDN_F32    ? &gdn_decode_kernel<SDT, D, N, L, GDN_F32>
+                                  : a.in_dt == GDN_BF16 ? &gdn_decode_kernel<SDT, D, N, L, GDN_BF16>
+                                                        : &gdn_decode_kernel<SDT, D, N, L, GDN_F16>;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(G::NW * 64), 0, s, a);
+  };
+  if (!NT && stream_tile_writes(tile_bytes)) one_shot(std::true_type{}, std::true_type{});
+  else if (stream_tile_reads(tile_bytes)) one_shot(std::integral_constant<bool, NT>{}, std::true_type{});
+  else one_shot(std::integral_constant<bool, NT>{}, std::false_type{});
   return hipGetLastError();
 }
 

@@ -105,6 +105,60 @@ __device__ __forceinline__ void load_vec(const void* p, int64_t i, int dt, float
   }
 }
 
+// N = 4 or 8 consecutive input elements of compile-time dtype IDT kept as raw
+// bits: the load is issued early and widened later, with no wait between the
+// load and the loads issued after it (a run-time dtype switch widens inside
+// its branches, where the compiler waits for every load issued so far).
+template <int IDT, int N>
+struct InVec {
+  static_assert(N == 4 || N == 8, "4 or 8 elements");
+  static constexpr int W = IDT == GDN_F32 ? N : N / 2;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const void* p, int64_t i) {
+    if constexpr (IDT == GDN_F32) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i);
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) {
+        const u32x4 v = q[c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[4 * c + j] = v[j];
+      }
+    } else if constexpr (N == 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = v[j];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+      w[0] = v[0];
+      w[1] = v[1];
+    }
+  }
+  __device__ __forceinline__ void widen(float (&f)[N]) const {
+    if constexpr (IDT == GDN_F32) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) f[e] = __uint_as_float(w[e]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < N / 2; ++j) {
+        f[2 * j] = unpack_lo<IDT>(w[j]);
+        f[2 * j + 1] = unpack_hi<IDT>(w[j]);
+      }
+    }
+  }
+};
+
+// One input element of compile-time dtype IDT as raw bits, and its value.
+template <int IDT>
+__device__ __forceinline__ uint32_t in_bits(const void* p, int64_t i) {
+  if constexpr (IDT == GDN_F32) return static_cast<const uint32_t*>(p)[i];
+  else return static_cast<const uint16_t*>(p)[i];
+}
+template <int IDT>
+__device__ __forceinline__ float in_value(uint32_t bits) {
+  if constexpr (IDT == GDN_F32) return __uint_as_float(bits);
+  else return unpack_lo<IDT>(bits);
+}
+
 // N = 4 or 8 consecutive elements stored at element i of a run-time-dtype
 // tensor, rounded once: one vector access per 16 bytes when that is aligned
 // (`vec`, uniform), else one access per element.
