@@ -72,8 +72,10 @@ __device__ __forceinline__ M2Pos m2_pos(const M2Args& a, int64_t slot) {
 // move with one vector access per 8 elements, and B and C load VEC elements
 // per access: per-element loads and stores cost the texture addresser an
 // address pass each, which bounds these 32 KiB tiles as it does the 16-bit
-// GDN ones.  Unaligned x, B, C or y take the per-element accesses.
-template <int SDT, int P, int N, bool NT>
+// GDN ones.  Unaligned x, B, C or y take the per-element accesses.  The small
+// loads (x, dt, B, C, as raw bits of the input dtype IDT) go out before the
+// tile: loads complete in order, so their waits do not cover the tile.
+template <int SDT, int P, int N, bool NT, int IDT>
 __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kernel(const M2Args a) {
   using G = M2G<SDT, P, N>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
@@ -97,34 +99,45 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kerne
     return;
   }
   ST* tile = static_cast<ST*>(a.pool) + ((int64_t)slot * a.H + h) * (int64_t)(P * N);
+  const bool vx = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  const bool vbc = ((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) & 15) == 0;
+  const int xi = 8 * min(tid, P / 8 - 1);  // threads past P / 8 reload the last group (no branch)
+  const int64_t bc = ((int64_t)b * a.G + gr) * N + c0;
+  const uint32_t dtb = in_bits<IDT>(a.dt, (int64_t)b * a.H + h);
+  const float dt_bias = a.dt_bias[h], A_log = a.A_log[h], Dh = a.Dskip[h];
+  InVec<IDT, 8> xv;
+  InVec<IDT, VEC> bv, cv;
+  if (vx) xv.load(a.x, yb + xi);
+  if (vbc) {
+    bv.load(a.Bm, bc);
+    cv.load(a.Cm, bc);
+  }
   typename IO::Raw raw[PASSES];
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * N + c0);
 
   if (tid < P / 8) {
     float f[8];
-    if ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0) {
-      load_vec<8>(a.x, yb + 8 * tid, a.in_dt, f);
+    if (vx) {
+      xv.widen(f);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = load_elem(a.x, yb + 8 * tid + e, a.in_dt);
+      for (int e = 0; e < 8; ++e) f[e] = load_elem(a.x, yb + xi + e, IDT);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_x[8 * tid + e] = f[e];
+    for (int e = 0; e < 8; ++e) s_x[xi + e] = f[e];
   }
-  const float dtp = softplus_f(load_elem(a.dt, (int64_t)b * a.H + h, a.in_dt) + a.dt_bias[h]);
-  const float alpha = expf(-expf(a.A_log[h]) * dtp);
-  const float Dh = a.Dskip[h];
-  const int64_t bc = ((int64_t)b * a.G + gr) * N + c0;
+  const float dtp = softplus_f(in_value<IDT>(dtb) + dt_bias);
+  const float alpha = expf(-expf(A_log) * dtp);
   float Bc[VEC], Cc[VEC];
-  if (((reinterpret_cast<uintptr_t>(a.Bm) | reinterpret_cast<uintptr_t>(a.Cm)) & 15) == 0) {
-    load_vec<VEC>(a.Bm, bc, a.in_dt, Bc);
-    load_vec<VEC>(a.Cm, bc, a.in_dt, Cc);
+  if (vbc) {
+    bv.widen(Bc);
+    cv.widen(Cc);
   } else {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      Bc[e] = load_elem(a.Bm, bc + e, a.in_dt);
-      Cc[e] = load_elem(a.Cm, bc + e, a.in_dt);
+      Bc[e] = load_elem(a.Bm, bc + e, IDT);
+      Cc[e] = load_elem(a.Cm, bc + e, IDT);
     }
   }
 #pragma unroll
@@ -485,7 +498,10 @@ static hipError_t m2_launch_t(const M2Args& a, int what, hipStream_t s) {
   constexpr bool NT = (SDT == GDN_F32) && (GDN_M2_NT_F32 != 0);
   const unsigned units = (unsigned)((int64_t)a.B * a.H);
   if (what == 0) {
-    hipLaunchKernelGGL((gdn_m2_decode_kernel<SDT, P, N, NT>), dim3(units), dim3(G::NW * 64), 0, s, a);
+    void (*k)(const M2Args) = a.in_dt == GDN_F32    ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F32>
+                              : a.in_dt == GDN_BF16 ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_BF16>
+                                                    : &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F16>;
+    hipLaunchKernelGGL(k, dim3(units), dim3(G::NW * 64), 0, s, a);
     return hipGetLastError();
   }
   // fold (persistent, sized to the resident workgroups)
