@@ -1297,11 +1297,23 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   const ST* tile = static_cast<const ST*>(p.pool) + ((int64_t)slot * p.Hv + h) * (int64_t)(D * D);
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
+  const float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
+  // The first 4 NTH elements of w and this thread's 4 acc elements of the first
+  // TB positions go out before the tile, every thread loading (indices clamped
+  // into the unit's rows): loads complete in order, so their waits do not cover
+  // the tile, and the acc load is no longer a dependent round after the
+  // reduction.
+  const int nt0 = T < TB ? T : TB;
+  const int iw = min(4 * tid, T * D - 4), ia = min(4 * tid, nt0 * D - 4);
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(wsu + 2 * (iw / D) * D + iw % D);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(wsu + (2 * (ia / D) + 1) * D + ia % D);
   typename IO::Raw raw[PASSES];
 #pragma unroll
   for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + (r0 + pp * NW * RPW) * D + c0);
-  const float* wsu = ws + ((int64_t)b * p.Hv + h) * T * 2 * D;
-  for (int i = 4 * tid; i < T * D; i += 4 * NTH) {  // 4 elements per access
+  // unconditional (threads past T D / 4 rewrite the last group with the same values),
+  // so the compiler cannot sink the w load below the tile's into a branch
+  *reinterpret_cast<f32x4*>(s_w + iw) = w0;
+  for (int i = 4 * (tid + NTH); i < T * D; i += 4 * NTH) {  // windows past 4 NTH elements
     const int t = i / D, c = i - t * D;
     *reinterpret_cast<f32x4*>(s_w + t * D + c) = *reinterpret_cast<const f32x4*>(wsu + 2 * t * D + c);
   }
@@ -1343,7 +1355,7 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
     const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
     for (int i = 4 * tid; i < nt * D; i += 4 * NTH) {  // 4 outputs per thread, one access each way
       const int tb = i / D, c = i - tb * D;
-      const f32x4 acc = *reinterpret_cast<const f32x4*>(wsu + (2 * (t0 + tb) + 1) * D + c);
+      const f32x4 acc = (t0 == 0 && i == ia) ? a0 : *reinterpret_cast<const f32x4*>(wsu + (2 * (t0 + tb) + 1) * D + c);
       float o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
