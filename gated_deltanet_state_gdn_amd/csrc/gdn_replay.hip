@@ -545,8 +545,12 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
 
   fold_units<(CDT >= 0)>(P, s_plan, [&](const int x) {
     const int b = x / p.Hv, h = x - (x / p.Hv) * p.Hv;
-    const int64_t unit = (int64_t)p.slot_map[b] * p.Hv + h;
-    const RingPos rp = ring_pos(R, p.slot_map[b]);
+    // the slot as a scalar: with it in a vector register (where per-lane ring
+    // addresses below put it) the tile's buffer descriptor would not be known
+    // uniform, and every tile access would become a loop over distinct values
+    const int slot = __builtin_amdgcn_readfirstlane(p.slot_map[b]);
+    const int64_t unit = (int64_t)slot * p.Hv + h;
+    const RingPos rp = ring_pos(R, slot);
     const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
 
     // ---- the checkpoint tile in the accumulator layout.  Element (16 I + r,
@@ -555,6 +559,30 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
     // offset is made opaque here and again before the write-back, so those
     // NJ 4 vector offsets live only around the loads and around the stores
     // (as 4 NI NJ scalar offsets the constants spilled).
+    // ---- first the committed entries' rows and gates, as raw bits: loads
+    // complete in order, so waiting for them does not wait for the tile issued
+    // after them.  Every thread loads a ring row in range (entry min(t, cnt - 1),
+    // entry 0 of an empty ring) and the rows past cnt are zeroed when widened.
+    const int64_t ring_e = unit * L;
+    const int64_t kring_e = ring_key_base(p, slot, h, L);
+    constexpr int QN = (16 * CPR + NTH - 1) / NTH;  // entry-row loads per thread
+    const int clast = (cnt > 0 ? cnt : 1) - 1;
+    auto ring_at = [&](int t) { const int x = st + t; return x >= L ? x - L : x; };  // st < L, t < L
+    u32x4 kw[QN], vw[QN];
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+      const int q = min(tid + u * NTH, 16 * CPR - 1), t = q / CPR, cc = (q - t * CPR) * VE;
+      const int pos = ring_at(min(t, clast));
+      kw[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + ((kring_e + pos) * D + cc) * EB);
+      vw[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + ((ring_e + pos) * D + cc) * EB);
+    }
+    float gg, be;
+    {
+      const int64_t j = ring_e + ring_at(min(lane & 15, clast));
+      gg = R.g[j];
+      be = R.beta[j];
+    }
+
     int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
     asm volatile("" : "+v"(lane_off));
     const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
@@ -568,40 +596,34 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
         for (int r = 0; r < 4; ++r) s0[I][jj][r] = ld_state(rs_tile, lane_off + (r * D + 16 * jj) * SB, 16 * I * D * SB);
 
     // ---- committed entries, widened: keys twice (transposed and by rows), values by rows
-    const int64_t ring_e = unit * L;
-    const int64_t kring_e = ring_key_base(p, p.slot_map[b], h, L);
-    for (int q = tid; q < 16 * CPR; q += NTH) {
-      const int t = q / CPR, cc = (q - t * CPR) * VE;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = kw;
-      if (t < cnt) {
-        const int64_t row = (ring_e + (st + t) % L) * D + cc, krow = (kring_e + (st + t) % L) * D + cc;
-        kw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.k) + krow * EB);
-        vw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(R.v) + row * EB);
-      }
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        float kf, vf;
-        if constexpr (EB == 4) {
-          kf = __uint_as_float(kw[e]);
-          vf = __uint_as_float(vw[e]);
-        } else {
-          const uint32_t kh = (e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu);
-          const uint32_t vh = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xffffu);
-          kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
-          vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+    for (int u = 0; u < QN; ++u) {
+      const int q = tid + u * NTH, t = q / CPR, cc = (q - t * CPR) * VE;
+      if (q < 16 * CPR) {
+        const bool live = t < cnt;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          float kf, vf;
+          if constexpr (EB == 4) {
+            kf = __uint_as_float(kw[u][e]);
+            vf = __uint_as_float(vw[u][e]);
+          } else {
+            const uint32_t kh = (e & 1) ? (kw[u][e >> 1] >> 16) : (kw[u][e >> 1] & 0xffffu);
+            const uint32_t vh = (e & 1) ? (vw[u][e >> 1] >> 16) : (vw[u][e >> 1] & 0xffffu);
+            kf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(kh) : f16_bits_to_f32(kh);
+            vf = p.in_dt == GDN_BF16 ? bf16_bits_to_f32(vh) : f16_bits_to_f32(vh);
+          }
+          kf = live ? kf : 0.f;
+          vf = live ? vf : 0.f;
+          e_kt[(cc + e) * KTS + t] = kf;
+          e_k[t * VS + cc + e] = kf;
+          e_v[t * VS + cc + e] = vf;
         }
-        e_kt[(cc + e) * KTS + t] = kf;
-        e_k[t * VS + cc + e] = kf;
-        e_v[t * VS + cc + e] = vf;
       }
     }
     if (wave == 0 && lane < 16) {  // gates in live order, zero past cnt; prefix sums within the row
-      float gg = 0.f, be = 0.f;
-      if (lane < cnt) {
-        const int64_t j = ring_e + (st + lane) % L;
-        gg = R.g[j];
-        be = R.beta[j];
-      }
+      gg = lane < cnt ? gg : 0.f;
+      be = lane < cnt ? be : 0.f;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) {
         const float y = __shfl_up(gg, off, 16);
