@@ -114,6 +114,18 @@ __device__ __forceinline__ f32x4_t rows_xyt(const uint32_t* X, const uint32_t* Y
   return acc;
 }
 
+// Gate input element i as raw bits (EB = 4: fp32; 2: bf16 or f16), and its value.
+template <int EB>
+__device__ __forceinline__ uint32_t gate_bits(const void* p, int64_t i) {
+  if constexpr (EB == 4) return static_cast<const uint32_t*>(p)[i];
+  else return static_cast<const uint16_t*>(p)[i];
+}
+template <int EB>
+__device__ __forceinline__ float gate_value(uint32_t x, int dt) {
+  if constexpr (EB == 4) return __uint_as_float(x);
+  else return dt == GDN_BF16 ? bf16_bits_to_f32(x) : f16_bits_to_f32(x);
+}
+
 // ---------------------------------------------------------------- kernel 1
 // One workgroup per (chunk slot, key head) for its R = Hv / Hk value heads:
 // the key and query rows are loaded and K K^T, Q K^T formed once, then each
@@ -159,45 +171,40 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
   const int len = min(C, seq_hi - t0);
 
   // keys and queries stay packed in their input dtype, rows >= len zeroed; thread
-  // (r, t) = (tid / C, tid mod C) loads the gate inputs of value head hk R + r, token t
+  // (r, t) = (tid / C, tid mod C) loads the gate inputs of value head hk R + r, token t.
+  // Every thread loads (indices clamped into the chunk and the heads) and the
+  // gate inputs go as raw bits of EB bytes, so all of them are one round: a
+  // branch around a load, or a run-time dtype switch that widens inside its
+  // branches, made the compiler wait for every load issued before.
   {
     constexpr int IT = (C * CPR + 255) / 256;
     u32x4 xk[IT], xq[IT];
 #pragma unroll
     for (int u = 0; u < IT; ++u) {
-      const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zq = zk;
-      if (x < C * CPR && r < len) {
-        const int64_t off = (((int64_t)(t0 + r) * p.Hk + hk) * D + cc * VE) * EB;
-        zk = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
-        zq = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
-      }
-      xk[u] = zk;
-      xq[u] = zq;
+      const int x = min(tid + u * 256, C * CPR - 1), r = x / CPR, cc = x - r * CPR;
+      const int64_t off = (((int64_t)(t0 + min(r, len - 1)) * p.Hk + hk) * D + cc * VE) * EB;
+      xk[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) + off);
+      xq[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.q) + off);
     }
     const int gr = tid / C, gt = tid - gr * C;
     const bool gl = gr < RMAX && gr < R;
-    float ga = 0.f, gb = 0.f, al = 0.f, db = 0.f;
-    if (gl) {
-      const int h = hk * R + gr;
-      const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + h;
-      ga = load_elem(p.a, gi, p.in_dt);
-      gb = load_elem(p.b, gi, p.in_dt);
-      al = p.A_log[h];
-      db = p.dt_bias[h];
-    }
+    const int h = hk * R + min(gr, min(RMAX, R) - 1);
+    const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + h;
+    const uint32_t ra = gate_bits<EB>(p.a, gi), rb = gate_bits<EB>(p.b, gi);
+    const float al = p.A_log[h], db = p.dt_bias[h];
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < IT; ++u) {
       const int x = tid + u * 256, r = x / CPR, cc = x - r * CPR;
       if (x < C * CPR) {
-        *reinterpret_cast<u32x4*>(s_k + r * LDW + cc * 4) = xk[u];
-        *reinterpret_cast<u32x4*>(s_q + r * LDW + cc * 4) = xq[u];
+        *reinterpret_cast<u32x4*>(s_k + r * LDW + cc * 4) = r < len ? xk[u] : z4;
+        *reinterpret_cast<u32x4*>(s_q + r * LDW + cc * 4) = r < len ? xq[u] : z4;
       }
     }
     if (gl) {
       const bool live = gt < len;
-      s_g[gr][gt] = live ? gate_g(ga, al, db) : 0.f;
-      s_beta[gr][gt] = live ? sigmoid_f(gb) : 0.f;
+      s_g[gr][gt] = live ? gate_g(gate_value<EB>(ra, p.in_dt), al, db) : 0.f;
+      s_beta[gr][gt] = live ? sigmoid_f(gate_value<EB>(rb, p.in_dt)) : 0.f;
     }
   }
   __syncthreads();
@@ -226,13 +233,14 @@ __global__ void __launch_bounds__(256) gdn_prefill_chunk_kernel(const PrefillArg
     __syncthreads();  // the key and query rows are read (first head), s_T is written out (later heads)
     if (rg == 0 && r > 0) {  // the next heads' gates
       const int gr = tid / C, gt = tid - gr * C;
+      const int hg = h + min(gr, min(RMAX, R - r) - 1);  // every thread loads, as above
+      const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + hg;
+      const uint32_t ra = gate_bits<EB>(p.a, gi), rb = gate_bits<EB>(p.b, gi);
+      const float al = p.A_log[hg], db = p.dt_bias[hg];
       if (gr < RMAX && r + gr < R) {
-        const int hg = h + gr;
-        const int64_t gi = (int64_t)(t0 + min(gt, len - 1)) * p.Hv + hg;
-        const float ga = load_elem(p.a, gi, p.in_dt), gb = load_elem(p.b, gi, p.in_dt);
         const bool live = gt < len;
-        s_g[gr][gt] = live ? gate_g(ga, p.A_log[hg], p.dt_bias[hg]) : 0.f;
-        s_beta[gr][gt] = live ? sigmoid_f(gb) : 0.f;
+        s_g[gr][gt] = live ? gate_g(gate_value<EB>(ra, p.in_dt), al, db) : 0.f;
+        s_beta[gr][gt] = live ? sigmoid_f(gate_value<EB>(rb, p.in_dt)) : 0.f;
       }
       __syncthreads();
     }
