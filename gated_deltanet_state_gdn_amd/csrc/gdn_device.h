@@ -133,6 +133,18 @@ struct InVec {
       w[1] = v[1];
     }
   }
+  // the raw bits back to memory (a bit-exact copy of the input)
+  __device__ __forceinline__ void store(void* p, int64_t i) const {
+    if constexpr (IDT == GDN_F32) {
+      u32x4* q = reinterpret_cast<u32x4*>(static_cast<float*>(p) + i);
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) q[c] = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+    } else if constexpr (N == 8) {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p) + i) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + i) = u32x2{w[0], w[1]};
+    }
+  }
   __device__ __forceinline__ void widen(float (&f)[N]) const {
     if constexpr (IDT == GDN_F32) {
 #pragma unroll

@@ -57,14 +57,15 @@ struct M2Pos {
 
 // Pointers as the step sees them: a fold (count + T > L; the flush, T == 0,
 // folds any non-empty ring) empties the ring first.
-__device__ __forceinline__ M2Pos m2_pos(const M2Args& a, int64_t slot) {
-  const int L = a.L;
-  int st = a.start[slot], cnt = a.count[slot];
+__device__ __forceinline__ M2Pos m2_fix(int L, int T, int st, int cnt) {
   st = ((st % L) + L) % L;
   cnt = cnt < 0 ? 0 : (cnt > L ? L : cnt);
-  const bool fold = a.T > 0 ? (cnt + a.T > L) : (cnt > 0);
+  const bool fold = T > 0 ? (cnt + T > L) : (cnt > 0);
   if (fold) return M2Pos{(st + cnt) % L, 0, true};
   return M2Pos{st, cnt, false};
+}
+__device__ __forceinline__ M2Pos m2_pos(const M2Args& a, int64_t slot) {
+  return m2_fix(a.L, a.T, a.start[slot], a.count[slot]);
 }
 
 // ---------------------------------------------------------------- decode
@@ -297,24 +298,7 @@ __host__ __device__ inline size_t m2_step_floats(int P, int N, int L, int T, int
          (size_t)HPG * T + (size_t)HPG * T * P;
 }
 
-// Four consecutive input elements (16-byte aligned for f32, 8 for 16-bit) as floats.
-__device__ __forceinline__ void load4(const void* p, int64_t i, int dt, float (&f)[4]) {
-  if (dt == GDN_F32) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = v[e];
-  } else {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const uint32_t lo = w[e] & 0xffffu, hi = w[e] >> 16;
-      f[2 * e] = dt == GDN_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
-      f[2 * e + 1] = dt == GDN_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
-    }
-  }
-}
-
-template <int SDT, int P, int N, bool NT>
+template <int SDT, int P, int N, bool NT, int IDT>
 __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(const M2Args a) {
   using G = M2G<SDT, P, N>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
@@ -336,10 +320,11 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
     }
     return;
   }
+  // Order of the loads: the ring pointers; the first batch of every phase-A
+  // part (they need the pointers); the first head's tile.  Loads return in
+  // order, so waiting for the phase-A loads does not wait for the tile.
+  const int st_raw = a.start[slot], ct_raw = a.count[slot];
   const ST* tiles = static_cast<const ST*>(a.pool) + ((int64_t)slot * a.H + h0) * (int64_t)(P * N);
-  typename IO::Raw cur[PASSES];
-#pragma unroll
-  for (int pp = 0; pp < PASSES; ++pp) cur[pp] = IO::load_raw(tiles + (r0 + pp * NW * RPW) * N + c0);
 
   float* rB = s_dyn;               // [L][N] ring order
   float* wB = rB + L * N;          // [T][N]
@@ -351,43 +336,151 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
   float* edec = ew + HPG * T * L;  // [HPG][T] e^{G_e}
   float* acc = edec + HPG * T;     // [HPG][T][P]
 
-  const M2Pos pos = m2_pos(a, slot);
+  const M2Pos pos = m2_fix(L, T, st_raw, ct_raw);
   const int st = pos.st, cnt = pos.cnt, n_all = cnt + T;  // n_all <= L
+  auto ring_at = [&](int e) { const int x = st + e; return x >= L ? x - L : x; };  // st < L, e < L
   const int64_t rgp = ((int64_t)slot * a.G + gr) * L;
-  // ---- phase A: group rows, appends, gates
-  for (int i = tid; i < cnt * N; i += NTH) {
-    const int e = i / N, c = i - e * N;
-    const int j = (st + e) % L;
-    rB[j * N + c] = load_elem(a.rB, (rgp + j) * N + c, a.in_dt);
-  }
-  for (int i = tid; i < T * N; i += NTH) {
-    const int t = i / N, c = i - t * N;
-    const int64_t src = (((int64_t)b * T + t) * a.G + gr) * N + c;
-    wB[i] = load_elem(a.Bm, src, a.in_dt);
-    wC[i] = load_elem(a.Cm, src, a.in_dt);
-    copy_elem(a.rB, (rgp + (st + cnt + t) % L) * N + c, a.Bm, src, a.in_dt);  // append B
-  }
-  for (int i = tid; i < HPG * T * P; i += NTH) {  // append x
-    const int hi = i / (T * P), rem = i - hi * T * P, t = rem / P, c = rem - t * P;
-    const int64_t rh = ((int64_t)slot * a.H + h0 + hi) * L;
-    copy_elem(a.rx, (rh + (st + cnt + t) % L) * P + c, a.x, (((int64_t)b * T + t) * a.H + h0 + hi) * P + c,
-              a.in_dt);
-  }
-  for (int hi = wave; hi < HPG; hi += NW) {  // per head: lane j takes live entry j
-    const int h = h0 + hi, j = lane;
-    const int64_t rh = ((int64_t)slot * a.H + h) * L;
-    float gj = 0.f, dj = 0.f;
-    if (j < cnt) {
-      gj = a.rg[rh + (st + j) % L];
-      dj = a.rdtp[rh + (st + j) % L];
-    } else if (j < n_all) {
-      const int t = j - cnt;
-      dj = softplus_f(load_elem(a.dt, ((int64_t)b * T + t) * a.H + h, a.in_dt) + a.dt_bias[h]);
-      gj = -expf(a.A_log[h]) * dj;
-      a.rg[rh + (st + cnt + t) % L] = gj;  // append g and dt'
-      a.rdtp[rh + (st + cnt + t) % L] = dj;
+  // ---- phase A.  Each part issues all its loads (8 elements per access, every
+  // thread loading, indices clamped) before its first store, so a part is one
+  // memory round; one element per access, or a load whose value a branch waits
+  // for, had made every element a round of its own.
+  // Part 1, the group's rows: committed ring B rows to LDS (ring order), window
+  // B and C rows to LDS with B appended to the ring, window x appended to the
+  // heads' rings.  B rows as vectors need 16-byte aligned ring and inputs.  The
+  // first batch is straight-line code, one source per load (a per-lane choice
+  // among argument pointers compiles to a load of the pointer itself) and all
+  // its loads before its first store; longer rings and windows loop after it.
+  constexpr int NV = N / 8, PV = P / 8;
+  constexpr int K1 = (16 * NV + NTH - 1) / NTH;  // ring B groups per thread in the first batch (up to 16 entries)
+  const int n1 = cnt * NV, n2 = T * NV, n3 = HPG * T * PV;
+  const bool vB = ((reinterpret_cast<uintptr_t>(a.rB) | reinterpret_cast<uintptr_t>(a.Bm) |
+                    reinterpret_cast<uintptr_t>(a.Cm)) & 15) == 0;
+  auto ring_b = [&](int q) { const int e = q / NV; return (rgp + ring_at(e)) * N + (q - e * NV) * 8; };
+  auto win_bc = [&](int q) {
+    const int t = q / NV;
+    return (((int64_t)b * T + t) * a.G + gr) * N + (q - t * NV) * 8;
+  };
+  auto win_x = [&](int q) {
+    const int hi = q / (T * PV), rem = q - hi * T * PV, t = rem / PV;
+    return (((int64_t)b * T + t) * a.H + h0 + hi) * P + (rem - t * PV) * 8;
+  };
+  auto put_b = [&](int q, const InVec<IDT, 8>& r) {  // committed ring B row group q
+    const int e = q / NV, c = (q - e * NV) * 8;
+    float f[8];
+    r.widen(f);
+    float* d = rB + ring_at(e) * N + c;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d[k] = f[k];
+  };
+  auto put_bc = [&](int q, const InVec<IDT, 8>& rb, const InVec<IDT, 8>& rc) {  // window B and C group q
+    const int t = q / NV, c = (q - t * NV) * 8;
+    float f[8], g[8];
+    rb.widen(f);
+    rc.widen(g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      wB[t * N + c + k] = f[k];
+      wC[t * N + c + k] = g[k];
     }
-    float Gs = gj;
+    rb.store(a.rB, (rgp + ring_at(cnt + t)) * N + c);  // append B
+  };
+  auto put_x = [&](int q, const InVec<IDT, 8>& r) {  // window x group q, appended to its head's ring
+    const int hi = q / (T * PV), rem = q - hi * T * PV, t = rem / PV;
+    r.store(a.rx, (((int64_t)slot * a.H + h0 + hi) * L + ring_at(cnt + t)) * P + (rem - t * PV) * 8);
+  };
+  // Part 2, gates: pair (head hi, live entry j); committed entries read g and
+  // dt' from the ring, window ones form them from dt and append them.  Both
+  // sources are read in every thread (the ring position is in range for any
+  // pair) and selected.
+  const int ng = HPG * n_all;
+  struct GateIn {
+    float g, d, dtb, al;
+    uint32_t dt;
+  };
+  auto gate_ld = [&](int q) {
+    const int hi = q / n_all, j = q - hi * n_all, h = h0 + hi;
+    const int64_t rh = ((int64_t)slot * a.H + h) * L + ring_at(j);
+    return GateIn{a.rg[rh], a.rdtp[rh], a.dt_bias[h], a.A_log[h],
+                  in_bits<IDT>(a.dt, ((int64_t)b * T + max(j - cnt, 0)) * a.H + h)};
+  };
+  auto gate_put = [&](int q, const GateIn& x) {
+    const int hi = q / n_all, j = q - hi * n_all;
+    float gj = x.g, dj = x.d;
+    if (j >= cnt) {
+      dj = softplus_f(in_value<IDT>(x.dt) + x.dtb);
+      gj = -expf(x.al) * dj;
+      const int64_t rh = ((int64_t)slot * a.H + h0 + hi) * L + ring_at(j);
+      a.rg[rh] = gj;  // append g and dt'
+      a.rdtp[rh] = dj;
+    }
+    eG[hi * L + j] = gj;
+    ed[hi * L + j] = dj;
+  };
+  typename IO::Raw cur[PASSES];
+  {
+    InVec<IDT, 8> r1[K1], r2b, r2c, r3;
+    GateIn g2[2];
+    if (vB) {
+      if (n1 > 0) {
+#pragma unroll
+        for (int u = 0; u < K1; ++u) r1[u].load(a.rB, ring_b(min(u * NTH + tid, n1 - 1)));
+      }
+      r2b.load(a.Bm, win_bc(min(tid, n2 - 1)));
+      r2c.load(a.Cm, win_bc(min(tid, n2 - 1)));
+    }
+    r3.load(a.x, win_x(min(tid, n3 - 1)));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) g2[u] = gate_ld(min(u * NTH + tid, ng - 1));
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads stay together, ahead of the tile's
+#pragma unroll
+    for (int pp = 0; pp < PASSES; ++pp) cur[pp] = IO::load_raw(tiles + (r0 + pp * NW * RPW) * N + c0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (vB) {
+#pragma unroll
+      for (int u = 0; u < K1; ++u)
+        if (u * NTH + tid < n1) put_b(u * NTH + tid, r1[u]);
+      if (tid < n2) put_bc(tid, r2b, r2c);
+    }
+    if (tid < n3) put_x(tid, r3);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (u * NTH + tid < ng) gate_put(u * NTH + tid, g2[u]);
+  }
+  if (vB) {  // beyond the first batch
+    for (int q = K1 * NTH + tid; q < n1; q += NTH) {
+      InVec<IDT, 8> r;
+      r.load(a.rB, ring_b(q));
+      put_b(q, r);
+    }
+    for (int q = NTH + tid; q < n2; q += NTH) {
+      InVec<IDT, 8> rb, rc;
+      rb.load(a.Bm, win_bc(q));
+      rc.load(a.Cm, win_bc(q));
+      put_bc(q, rb, rc);
+    }
+  } else {  // unaligned B rows: one element per access
+    for (int i = tid; i < cnt * N; i += NTH) {
+      const int e = i / N, c = i - e * N, j = ring_at(e);
+      rB[j * N + c] = load_elem(a.rB, (rgp + j) * N + c, IDT);
+    }
+    for (int i = tid; i < T * N; i += NTH) {
+      const int t = i / N, c = i - t * N;
+      const int64_t src = (((int64_t)b * T + t) * a.G + gr) * N + c;
+      wB[i] = load_elem(a.Bm, src, IDT);
+      wC[i] = load_elem(a.Cm, src, IDT);
+      copy_elem(a.rB, (rgp + ring_at(cnt + t)) * N + c, a.Bm, src, IDT);  // append B
+    }
+  }
+  for (int q = NTH + tid; q < n3; q += NTH) {
+    InVec<IDT, 8> r;
+    r.load(a.x, win_x(q));
+    put_x(q, r);
+  }
+  for (int q = 2 * NTH + tid; q < ng; q += NTH) gate_put(q, gate_ld(q));  // beyond the first batch
+  __syncthreads();
+  for (int hi = wave; hi < HPG; hi += NW) {  // prefix sums of g per head (lane j: entry j)
+    const int j = lane;
+    float Gs = j < n_all ? eG[hi * L + j] : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(Gs, off, 64);
@@ -395,14 +488,14 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
     }
     if (j < L) {
       eG[hi * L + j] = Gs;
-      ed[hi * L + j] = dj;
+      if (j >= n_all) ed[hi * L + j] = 0.f;
     }
   }
   __syncthreads();
   for (int item = wave; item < T * L; item += NW) {  // B_j . C_t, one wave per pair, lanes over n
     const int t = item / L, j = item - t * L;
     if (j > cnt + t) continue;
-    const float* Bj = j < cnt ? rB + ((st + j) % L) * N : wB + (j - cnt) * N;
+    const float* Bj = j < cnt ? rB + ring_at(j) * N : wB + (j - cnt) * N;
     const float* Ct = wC + t * N;
     float d = 0.f;
     for (int c = lane; c < N; c += 64) d = fmaf(Bj[c], Ct[c], d);
@@ -417,26 +510,57 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_step_kernel(
     if (j == 0) edec[hi * T + t] = expf(eG[hi * L + e_last]);
   }
   __syncthreads();
-  // acc[hi][t][r..r+3] = sum_j w x_j + D x_t, four rows per thread, x read from the ring and the window
+  // acc[hi][t][r..r+3] = sum_j w x_j + D x_t, four rows per thread, x read from the
+  // ring and the window.  Up to 16 live entries all of a thread's rows go out
+  // before its sums (a pointer and an index selected per entry, no branch).
   for (int i = tid; i < HPG * T * (P / 4); i += NTH) {
     const int hi = i / (T * (P / 4)), rem = i - hi * T * (P / 4), t = rem / (P / 4), r = (rem - t * (P / 4)) * 4;
-    const int h = h0 + hi;
+    const int h = h0 + hi, e_last = cnt + t;
     const int64_t rh = ((int64_t)slot * a.H + h) * L;
     const int64_t xw = ((int64_t)b * T * a.H + h) * P + r;  // window x of position 0
-    float v[4], xt[4];
-    load4(a.x, xw + (int64_t)t * a.H * P, a.in_dt, xt);
-    const float Dh = a.Dskip[h];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = Dh * xt[e];
     const float* w = ew + (hi * T + t) * L;
-    for (int j = 0; j <= cnt + t; ++j) {
-      float xj[4];
-      if (j < cnt)
-        load4(a.rx, (rh + (st + j) % L) * P + r, a.in_dt, xj);
-      else
-        load4(a.x, xw + (int64_t)(j - cnt) * a.H * P, a.in_dt, xj);
+    auto x_src = [&](int j, const void*& p) -> int64_t {
+      p = j < cnt ? a.rx : a.x;
+      return j < cnt ? (rh + ring_at(j)) * P + r : xw + (int64_t)(j - cnt) * a.H * P;
+    };
+    InVec<IDT, 4> xtr;
+    xtr.load(a.x, xw + (int64_t)t * a.H * P);
+    const float Dh = a.Dskip[h];
+    float v[4], f[4];
+    if (L <= 16) {
+      InVec<IDT, 4> xr[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = fmaf(w[j], xj[e], v[e]);
+      for (int j = 0; j < 16; ++j) {
+        const void* p = nullptr;
+        const int64_t k = x_src(min(j, e_last), p);
+        xr[j].load(p, k);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the rows' loads stay together
+      xtr.widen(f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = Dh * f[e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j <= e_last) {
+          xr[j].widen(f);
+          const float wj = w[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = fmaf(wj, f[e], v[e]);
+        }
+      }
+    } else {
+      xtr.widen(f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = Dh * f[e];
+      for (int j = 0; j <= e_last; ++j) {
+        const void* p = nullptr;
+        const int64_t k = x_src(j, p);
+        InVec<IDT, 4> xj;
+        xj.load(p, k);
+        xj.widen(f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(w[j], f[e], v[e]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[(hi * T + t) * P + r + e] = v[e];
@@ -517,7 +641,10 @@ static hipError_t m2_launch_t(const M2Args& a, int what, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.T > 0) {
-    hipLaunchKernelGGL((gdn_m2_step_kernel<SDT, P, N, NT>), dim3((unsigned)((int64_t)a.B * a.G)), dim3(G::NW * 64),
+    void (*k)(const M2Args) = a.in_dt == GDN_F32    ? &gdn_m2_step_kernel<SDT, P, N, NT, GDN_F32>
+                              : a.in_dt == GDN_BF16 ? &gdn_m2_step_kernel<SDT, P, N, NT, GDN_BF16>
+                                                    : &gdn_m2_step_kernel<SDT, P, N, NT, GDN_F16>;
+    hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)a.B * a.G)), dim3(G::NW * 64),
                        m2_step_floats(P, N, a.L, a.T, a.H / a.G) * sizeof(float), s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
