@@ -174,7 +174,7 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kerne
 // 64 at a time (one per lane of wave 0) and folds those whose slot folds this
 // step, one after another.  Pointers are left to the advance kernel.
 // Dynamic LDS (floats): x rows [L][P], B rows [L][N], weights [L].
-template <int SDT, int P, int N, bool NT>
+template <int SDT, int P, int N, bool NT, int IDT>
 __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_fold_kernel(const M2Args a) {
   using G = M2G<SDT, P, N>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
@@ -222,33 +222,79 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_fold_kernel(
       st = ((st % L) + L) % L;
       cnt = cnt < 0 ? 0 : (cnt > L ? L : cnt);
 
+      auto ring_at = [&](int e) { const int y = st + e; return y >= L ? y - L : y; };  // st < L, e < L
+      const int64_t rh = (slot * a.H + h) * L, rg = (slot * a.G + gr) * L;
+      // The committed entries (x rows, B rows, g and dt') go out first, 8
+      // elements per access, as one batch (every thread loading, indices clamped
+      // into the live entries), then the tile: loads return in order, so
+      // waiting for the entries does not wait for the tile.  Element loops had
+      // made each element a dependent round after the whole tile.  B rows as
+      // vectors need a 16-byte aligned ring; rings past 16 entries loop after.
+      constexpr int PV = P / 8, NV = N / 8;
+      constexpr int KX = (16 * PV + NTH - 1) / NTH, KB = (16 * NV + NTH - 1) / NTH;
+      const int nx = cnt * PV, nb = cnt * NV, clast = (cnt > 0 ? cnt : 1) - 1;
+      const bool vB = (reinterpret_cast<uintptr_t>(a.rB) & 15) == 0;
+      auto x_at = [&](int q) { const int e = q / PV; return (rh + ring_at(min(e, clast))) * P + (q - e * PV) * 8; };
+      auto b_at = [&](int q) { const int e = q / NV; return (rg + ring_at(min(e, clast))) * N + (q - e * NV) * 8; };
+      auto put8 = [&](float* d, const InVec<IDT, 8>& r) {
+        float f[8];
+        r.widen(f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = f[k];
+      };
+      InVec<IDT, 8> xr[KX], br[KB];
+#pragma unroll
+      for (int u = 0; u < KX; ++u) xr[u].load(a.rx, x_at(min(u * NTH + tid, max(nx, 1) - 1)));
+      if (vB) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) br[u].load(a.rB, b_at(min(u * NTH + tid, max(nb, 1) - 1)));
+      }
+      const int64_t gj_at = rh + ring_at(min(lane, clast));
+      const float g_raw = a.rg[gj_at], d_raw = a.rdtp[gj_at];
+      __builtin_amdgcn_sched_barrier(0);  // the entries' loads stay ahead of the tile's
+
       int lane_off = r0 * N + c0;
       asm volatile("" : "+v"(lane_off));
       ST* tile = static_cast<ST*>(a.pool) + (slot * a.H + h) * (int64_t)(P * N) + lane_off;
       typename IO::Raw raw[PASSES];
 #pragma unroll
       for (int pp = 0; pp < PASSES; ++pp) raw[pp] = IO::load_raw(tile + pp * NW * RPW * N);
+      __builtin_amdgcn_sched_barrier(0);
 
       // committed entries in live order, widened
-      const int64_t rh = (slot * a.H + h) * L, rg = (slot * a.G + gr) * L;
-      for (int i = tid; i < cnt * P; i += NTH) {
-        const int e = i / P, c = i - e * P;
-        ex[i] = load_elem(a.rx, (rh + (st + e) % L) * P + c, a.in_dt);
+#pragma unroll
+      for (int u = 0; u < KX; ++u)
+        if (u * NTH + tid < nx) put8(ex + 8 * (u * NTH + tid), xr[u]);
+      for (int q = KX * NTH + tid; q < nx; q += NTH) {
+        InVec<IDT, 8> r;
+        r.load(a.rx, x_at(q));
+        put8(ex + 8 * q, r);
       }
-      for (int i = tid; i < cnt * N; i += NTH) {
-        const int e = i / N, c = i - e * N;
-        eB[i] = load_elem(a.rB, (rg + (st + e) % L) * N + c, a.in_dt);
+      if (vB) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+          if (u * NTH + tid < nb) put8(eB + 8 * (u * NTH + tid), br[u]);
+        for (int q = KB * NTH + tid; q < nb; q += NTH) {
+          InVec<IDT, 8> r;
+          r.load(a.rB, b_at(q));
+          put8(eB + 8 * q, r);
+        }
+      } else {  // unaligned ring B rows: one element per access
+        for (int i = tid; i < cnt * N; i += NTH) {
+          const int e = i / N, c = i - e * N;
+          eB[i] = load_elem(a.rB, (rg + ring_at(e)) * N + c, IDT);
+        }
       }
       if (wave == 0) {  // weights e^{G_c - G_j} dt'_j from a suffix sum of g, and the decay e^{G_c}
         const int j = lane;
-        const float gj = j < cnt ? a.rg[rh + (st + j) % L] : 0.f;
+        const float gj = j < cnt ? g_raw : 0.f;
         float suf = gj;  // sum of g over entries j..cnt-1
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float y = __shfl_down(suf, off, 64);
           if (j + off < 64) suf += y;
         }
-        if (j < cnt) ew[j] = expf(suf - gj) * a.rdtp[rh + (st + j) % L];
+        if (j < cnt) ew[j] = expf(suf - gj) * d_raw;
         const float total = __shfl(suf, 0, 64);
         if (j == 0) s_decay = expf(total);
       }
@@ -631,13 +677,14 @@ static hipError_t m2_launch_t(const M2Args& a, int what, hipStream_t s) {
   // fold (persistent, sized to the resident workgroups)
   const size_t fold_lds = ((size_t)a.L * (P + N + 1)) * sizeof(float);
   int per_cu = 0, cus = 0;
-  hipError_t e = resident_blocks(reinterpret_cast<const void*>(&gdn_m2_fold_kernel<SDT, P, N, NT>), G::NW * 64,
-                                 fold_lds, &per_cu);
+  void (*fold)(const M2Args) = a.in_dt == GDN_F32    ? &gdn_m2_fold_kernel<SDT, P, N, NT, GDN_F32>
+                               : a.in_dt == GDN_BF16 ? &gdn_m2_fold_kernel<SDT, P, N, NT, GDN_BF16>
+                                                     : &gdn_m2_fold_kernel<SDT, P, N, NT, GDN_F16>;
+  hipError_t e = resident_blocks(reinterpret_cast<const void*>(fold), G::NW * 64, fold_lds, &per_cu);
   if (e == hipSuccess) e = device_cus(&cus);
   if (e != hipSuccess) return e;
   const int64_t fill = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
-  hipLaunchKernelGGL((gdn_m2_fold_kernel<SDT, P, N, NT>), dim3((unsigned)(units < fill ? units : fill)),
-                     dim3(G::NW * 64), fold_lds, s, a);
+  hipLaunchKernelGGL(fold, dim3((unsigned)(units < fill ? units : fill)), dim3(G::NW * 64), fold_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.T > 0) {
