@@ -1413,9 +1413,7 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   static_assert(TMAX * D <= 4 * NW * 64, "four w / acc elements per thread");
   typedef unsigned int Raw __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float s_red[2][TMAX][NW][D];  // [parity][position][wave][column]
-  __shared__ __attribute__((aligned(16))) float s_sum[2][TMAX][D];      // [parity][position][column]
   __shared__ __attribute__((aligned(16))) float s_w[2][TMAX][D];        // [parity][position][row]: w
-  __shared__ __attribute__((aligned(16))) float s_acc[2][TMAX][D];      // [parity][position][column]: acc
   __shared__ int s_slot[kStreamPersistMaxIter];
 
   const DecodeArgs& p = P.d;
@@ -1429,19 +1427,22 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t + i * G) / p.Hv];
 
   auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
-  // thread tid < T D / 4 carries elements 4 tid.. of the unit's w and acc vectors
-  // (w_t, acc_t by position), one access each
+  // thread tid < T D / 4 carries elements 4 tid.. of the unit's w vectors (w_t by
+  // position), one access; thread tid < T D sums column sc of position st and
+  // writes that output, with its acc element in a register
   const bool wthr = tid < T * D / 4;
   const int wi = wthr ? 4 * tid : 0, wt = wi / D, wc = wi - wt * D;
-  const bool out_vec = (reinterpret_cast<uintptr_t>(p.out) & 15) == 0;
+  const bool sthr = tid < T * D;
+  const int si = sthr ? tid : 0, st = si / D, sc = si - st * D;
   struct In {
     Raw raw[PASSES];
-    f32x4 w, acc;
+    f32x4 w;
+    float acc;
   };
   auto fetch = [&](int u, int slot, In& x) {
     const float* wsu = ws + (int64_t)u * T * 2 * D;  // per position: w, then acc
     x.w = *reinterpret_cast<const f32x4*>(wsu + 2 * wt * D + wc);  // before the tile: waiting for these leaves the tile in flight
-    x.acc = *reinterpret_cast<const f32x4*>(wsu + (2 * wt + 1) * D + wc);
+    x.acc = wsu[(2 * st + 1) * D + sc];
     const int h = u % p.Hv;
     const bool ok = valid(slot);
     const float* tile = static_cast<const float*>(p.pool) + (ok ? ((int64_t)slot * p.Hv + h) * (int64_t)(D * D) : 0);
@@ -1453,13 +1454,16 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
           Raw, __builtin_amdgcn_raw_buffer_load_b128(rs, (r0 * D + c0) * 4, pp * NW * RPW * D * 4, NTL ? 2 : 0));
   };
 
+  // One barrier per unit: the partial column sums of unit i (buffer i mod 2) are
+  // written before its barrier and summed after it; the next write to that buffer
+  // is unit i + 2's, after the barrier of unit i + 1, which every thread reaches
+  // only when its sums of unit i are done.  w of unit i + 1 is written before the
+  // barrier of unit i and read before the barrier of unit i + 1, so two buffers
+  // serve it too.  acc never passes through LDS.
   In cur, nxt;
   __syncthreads();  // s_slot
   fetch(t, s_slot[0], cur);
-  if (wthr) {
-    *reinterpret_cast<f32x4*>(&s_w[0][wt][wc]) = cur.w;
-    *reinterpret_cast<f32x4*>(&s_acc[0][wt][wc]) = cur.acc;
-  }
+  if (wthr) *reinterpret_cast<f32x4*>(&s_w[0][wt][wc]) = cur.w;
   __syncthreads();
   for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
     const int tn = t + G;
@@ -1488,27 +1492,13 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
         }
       }
     }
+    if (wthr) *reinterpret_cast<f32x4*>(&s_w[par ^ 1][wt][wc]) = nxt.w;  // the next unit's w
     __syncthreads();
-    if (live) {
-      for (int i = tid; i < T * D; i += NW * 64) {  // one (position, column) per thread
-        const int tt = i / D, col = i - tt * D;
-        float a = 0.f;
+    if (sthr) {  // position st, column sc (padded rows: zeros)
+      float a = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) a += s_red[par][tt][w][col];
-        s_sum[par][tt][col] = a;
-      }
-    }
-    // the next unit's w and acc, published by the barrier below
-    if (wthr) {
-      *reinterpret_cast<f32x4*>(&s_w[par ^ 1][wt][wc]) = nxt.w;
-      *reinterpret_cast<f32x4*>(&s_acc[par ^ 1][wt][wc]) = nxt.acc;
-    }
-    __syncthreads();
-    if (wthr) {  // position wt, columns wc.. (padded rows: zeros)
-      float o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = live ? p.scale * (s_acc[par][wt][wc + j] + s_sum[par][wt][wc + j]) : 0.f;
-      store_vec<4>(p.out, out_row(wt) + wc, o, p.out_dt, out_vec);
+      for (int w = 0; w < NW; ++w) a += s_red[par][st][w][sc];
+      store_elem(p.out, out_row(st) + sc, live ? p.scale * (cur.acc + a) : 0.f, p.out_dt);
     }
     cur = nxt;
   }
