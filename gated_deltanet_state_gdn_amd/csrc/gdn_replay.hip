@@ -16,6 +16,12 @@
 //   stream - o_t = scale (S0^T w_t + acc_t): one read pass over S0 for all T
 //            positions, a plain batched matrix-vector product that runs at
 //            high occupancy.
+// With 16-bit inputs, rings of at most 16 entries and D = 64 (or 128 with fp32
+// checkpoints) the order is prep, fold, stream instead (fused fold): the prep
+// takes each unit's fold decision itself and forms w and acc against the
+// folded ring, the fold also writes the outputs of the units it folds from
+// the new S0 it holds in registers, and the stream skips those units' tiles,
+// so a fold step reads each folded tile once instead of twice.
 //
 // prep unrolls S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T
 // (a_i = exp(g_i)).  Transposing gives S_n^T q = S0^T w + acc with
@@ -110,8 +116,9 @@ struct RingPos {
 // the slot's entries.  Within a step no kernel writes a pair that another
 // kernel of the same step reads: the fold's check records each unit's pointers
 // after any fold, the prep reads only those records and the first value head's
-// prep writes the slot's new pair; a flush moves the pairs in a kernel of its
-// own after the fold.
+// prep writes the slot's new pair (fused fold: the prep reads the pairs and
+// records them, the fold reads the records, the stream writes the new pairs);
+// a flush moves the pairs in a kernel of its own after the fold.
 __device__ __forceinline__ RingPos ring_pos(const RingArgs& R, int64_t slot) {
   const int L = R.L;
   int st = R.start[slot], cnt = R.count[slot];
@@ -150,8 +157,12 @@ struct FoldPlanLds {
   int pref[kFoldPlanWords + 1];
 };
 
-template <bool DUAL, class F>
-__device__ __forceinline__ void fold_units(const ReplayArgs& P, FoldPlanLds& sh, F&& fold_unit) {
+// FUSED: the prep ran first and wrote every unit's record (slot, pointers
+// before the step, fold flag); the plan reads the flag of each sequence's first
+// unit and writes nothing.
+template <bool DUAL, class F, bool FUSED = false>
+__device__ __forceinline__ void fold_units(const ReplayArgs& P, FoldPlanLds& sh, F&& fold_unit,
+                                           std::integral_constant<bool, FUSED> = {}) {
   const DecodeArgs& p = P.d;
   const RingArgs& R = P.ring;
   const int T = P.T, L = R.L;
@@ -159,6 +170,10 @@ __device__ __forceinline__ void fold_units(const ReplayArgs& P, FoldPlanLds& sh,
   const int units = p.B * p.Hv, G = gridDim.x;
   // whether sequence b folds, and the record of its units
   auto plan_of = [&](int b, int4& rc) -> bool {
+    if constexpr (FUSED) {
+      rc = reinterpret_cast<const int4*>(P.rec)[(int64_t)b * p.Hv];
+      return rc.x >= 0 && rc.w != 0;
+    }
     const int slot = p.slot_map[b];
     rc = int4{-1, 0, 0, 0};
     if (slot < 0 || (int64_t)slot >= p.num_slots) return false;
@@ -167,7 +182,7 @@ __device__ __forceinline__ void fold_units(const ReplayArgs& P, FoldPlanLds& sh,
     rc = need ? int4{slot, (rp.st + rp.cnt) % L, 0, 0} : int4{slot, rp.st, rp.cnt, 0};
     return need;
   };
-  if (P.rec != nullptr) {
+  if (!FUSED && P.rec != nullptr) {
     for (int64_t j = tid; blockIdx.x + j * G < units; j += nth) {
       const int x = (int)(blockIdx.x + j * G);
       int4 rc;
@@ -494,15 +509,24 @@ __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2
 // staging.  Entries past n are zero rows with zero gates and drop out.
 constexpr int kFoldKTS = 20;  // LDS stride of the transposed keys: 16 entries + 4 (conflict-free reads)
 
-__host__ __device__ inline size_t replay_fold_mfma_lds_bytes(int D) {
-  return ((size_t)D * kFoldKTS + 2 * 16 * ((size_t)D + 4) + 2 * 16 + 4 * 16 * 17) * sizeof(float);
+// The fused fold (windows of up to TW positions) adds the window's w
+// transposed [D][kFoldKTS] and its acc rows [TW][D].
+__host__ __device__ inline size_t replay_fold_mfma_lds_bytes(int D, int TW = 0) {
+  const size_t fused = TW > 0 ? (size_t)D * kFoldKTS + (size_t)TW * D : 0;
+  return ((size_t)D * kFoldKTS + 2 * 16 * ((size_t)D + 4) + 2 * 16 + 4 * 16 * 17 + fused) * sizeof(float);
 }
 
 // Built for three workgroups per CU: at four (128 VGPRs) the kernel spilled
 // registers to scratch, and at three it folds as fast or faster (fp32 fold
 // steps 453-467 us against 454-482, bf16 373-396 against 372-407).
-template <int SDT, int D, bool NT, int EB, int CDT>
+// TW > 0, fused (the prep ran first, see the prep): each folded unit also writes
+// its window's outputs, o_t = scale (S^T w_t + acc_t) from the tile as stored, so
+// the stream kernel skips its tile; windows of up to TW <= 16 positions.  W S for
+// all positions at once is the K S0 product's shape (positions in place of
+// entries): one pass of MFMAs whatever the window.
+template <int SDT, int D, bool NT, int EB, int CDT, int TW = 0>
 __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const ReplayArgs P) {
+  constexpr bool FUSED = TW > 0;
   static_assert(D == 64 || D == 128, "four waves of 16-column blocks");
   constexpr int NI = D / 16;  // row blocks
   constexpr int NJ = D / 64;  // column blocks per wave
@@ -524,7 +548,12 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
   float* e_G = e_v + 16 * VS;           // [16] prefix sums of g
   float* e_b = e_G + 16;                // [16] beta
   float* s_m = e_b + 16 + wave * 16 * 17;  // this wave's [16][17] factor
+  float* e_wt = e_b + 16 + 4 * 16 * 17;    // FUSED: [D][KTS] w transposed: w_t[r] at r KTS + t
+  float* e_acc = e_wt + D * KTS;           // FUSED: [TW][D] acc rows
   constexpr int VE = 16 / EB, CPR = D / VE;  // ring row elements per 16-byte load, loads per row
+  const int T = P.T;
+  // FUSED: the prep's vectors, [B Hv][T][2][D] floats right before the records in the workspace
+  const float* ws_vec = FUSED ? reinterpret_cast<const float*>(P.rec) - (int64_t)p.B * p.Hv * T * 2 * D : nullptr;
 
   // Tile elements go through buffer instructions: one per-lane byte offset and
   // a scalar offset per element, so the 4 NI NJ accesses of a lane need no
@@ -548,10 +577,19 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
     // the slot as a scalar: with it in a vector register (where per-lane ring
     // addresses below put it) the tile's buffer descriptor would not be known
     // uniform, and every tile access would become a loop over distinct values
-    const int slot = __builtin_amdgcn_readfirstlane(p.slot_map[b]);
+    int slot, st, cnt;
+    if constexpr (FUSED) {  // the prep's record: slot and the pointers before the step
+      const int4 rc = reinterpret_cast<const int4*>(P.rec)[x];
+      slot = __builtin_amdgcn_readfirstlane(rc.x);
+      st = __builtin_amdgcn_readfirstlane(rc.y);
+      cnt = min(__builtin_amdgcn_readfirstlane(rc.z), 16);
+    } else {
+      slot = __builtin_amdgcn_readfirstlane(p.slot_map[b]);
+      const RingPos rp = ring_pos(R, slot);
+      st = rp.st;
+      cnt = rp.cnt < 16 ? rp.cnt : 16;
+    }
     const int64_t unit = (int64_t)slot * p.Hv + h;
-    const RingPos rp = ring_pos(R, slot);
-    const int st = rp.st, cnt = rp.cnt < 16 ? rp.cnt : 16;
 
     // ---- the checkpoint tile in the accumulator layout.  Element (16 I + r,
     // 16 jj) of a lane takes the row block's offset as the scalar offset (NI
@@ -581,6 +619,23 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
       const int64_t j = ring_e + ring_at(min(lane & 15, clast));
       gg = R.g[j];
       be = R.beta[j];
+    }
+    // FUSED: the window's w and acc, 4 floats per load, all before the tile.  w
+    // chunk q is rows 4 (q / TW).. of position q mod TW (consecutive lanes take
+    // consecutive positions, so the transposed LDS writes below do not conflict);
+    // acc chunk q is columns 4 (q mod D/4).. of position q / (D/4).  Positions
+    // past T load position T - 1 (their w is zeroed, their acc never read).
+    constexpr int QW = FUSED ? (TW * D / 4 + NTH - 1) / NTH : 1;
+    f32x4 wq[QW], aq[QW];
+    const float* wsu = FUSED ? ws_vec + (int64_t)x * T * 2 * D : nullptr;
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int u = 0; u < QW; ++u) {
+        const int q = min(tid + u * NTH, TW * D / 4 - 1);
+        const int tw = min(q % TW, T - 1), ta = min(q / (D / 4), T - 1);
+        wq[u] = *reinterpret_cast<const f32x4*>(wsu + 2 * tw * D + 4 * (q / TW));
+        aq[u] = *reinterpret_cast<const f32x4*>(wsu + (2 * ta + 1) * D + 4 * (q % (D / 4)));
+      }
     }
 
     int lane_off = (4 * g * D + NJ * 16 * wave + c) * SB;
@@ -621,6 +676,20 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
         }
       }
     }
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int u = 0; u < QW; ++u) {
+        const int q = tid + u * NTH;
+        // used here, so the loads stay ahead of the tile's instead of sinking into the test
+        asm volatile("" ::"v"(wq[u]), "v"(aq[u]));
+        if (QW * NTH == TW * D / 4 || q < TW * D / 4) {
+          const int t = q % TW, r0 = 4 * (q / TW);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) e_wt[(r0 + k) * KTS + t] = t < T ? wq[u][k] : 0.f;
+          *reinterpret_cast<f32x4*>(e_acc + 4 * q) = aq[u];  // position q / (D/4), columns 4 (q mod D/4)..
+        }
+      }
+    }
     if (wave == 0 && lane < 16) {  // gates in live order, zero past cnt; prefix sums within the row
       gg = lane < cnt ? gg : 0.f;
       be = lane < cnt ? be : 0.f;
@@ -634,7 +703,10 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
     }
     __syncthreads();
 
-    if (cnt > 0) {
+    // (FUSED: a folding unit has entries; with none the update below would return S0
+    // unchanged, and without the test the tile's loads are known complete before
+    // the outputs read it, so no wait there also covers the write-back)
+    if (FUSED || cnt > 0) {
       const float Gn = e_G[15];  // gates past cnt are zero: entry 15 carries G_cnt
       // ---- K K^T; element r of lane (c, g) is (4 g + r, c)
       f32x4 kk = {0.f, 0.f, 0.f, 0.f};
@@ -727,6 +799,46 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
 #pragma unroll
           for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
       }
+      if constexpr (FUSED) {
+        // the window's outputs from the tile as stored, before the write-back:
+        // O = W S with W [positions][rows] as the MFMA's A operand (lane (c, g)
+        // gives w_c at rows 16 I + 4 g + r) and the tile as B, two chains per
+        // column block; element r of lane (c, g) is position 4 g + r, column c
+        if constexpr (SDT != GDN_F32) {  // rounded in place (the write-back's rounding then changes nothing)
+#pragma unroll
+          for (int I = 0; I < NI; ++I)
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s0[I][jj][r] = unpack_lo<SDT>(pack2<SDT>(s0[I][jj][r], 0.f));
+        }
+        constexpr int NC = 2;  // chains per column block
+        f32x4 o[NC][NJ];
+#pragma unroll
+        for (int hh = 0; hh < NC; ++hh)
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) o[hh][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < NI; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = c < T ? e_wt[(16 * I + 4 * g + r) * KTS + c] : 0.f;  // columns past TW unwritten
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+              o[I % NC][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], o[I % NC][jj], 0, 0, 0);
+          }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int col = 16 * (NJ * wave + jj) + c;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            if (t < T)
+              store_elem(p.out, (((int64_t)b * T + t) * p.Hv + h) * D + col,
+                         p.scale * (o[0][jj][r] + o[1][jj][r] + e_acc[t * D + col]), p.out_dt);
+          }
+        }
+      }
       // ---- write back, rounded once
       int lane_st = lane_off;
       asm volatile("" : "+v"(lane_st));
@@ -753,7 +865,7 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
             st_state(rs_copy, coff + (r * D + 16 * jj) * 2, 16 * I * D * 2, s0[I][jj][r], std::integral_constant<int, CDT>{});
     }
     __syncthreads();  // LDS staging is reused by the next unit
-  });
+  }, std::integral_constant<bool, FUSED>{});
 }
 
 // ---------------------------------------------------------------- prep
@@ -1039,6 +1151,15 @@ __global__ void __launch_bounds__(NWP * 64) gdn_replay_prep_kernel(const ReplayA
 // one row per instruction) and of every key row (read back from LDS), so both
 // are plain sums over the entries with the coefficients in scalar registers.
 // The window goes to the ring straight from the registers that loaded it.
+//
+// FUSED: the prep runs first in the step and decides each unit's fold itself
+// (count + T > L).  It writes the unit's record for the fold and the stream
+// (slot, ring pointers before the step, fold flag), forms w and acc over the
+// live entries after any fold, and appends the window to the ring only for
+// units that do not fold: a folding unit's window would overwrite the entries
+// the fold still reads, so the stream appends it.  The ring pointers are not
+// moved here (another value head's prep of the slot may still be reading them):
+// the stream, the last kernel of the step, moves them.
 
 // Dynamic LDS of the one-wave prep (bytes): window queries [T][D] and key rows
 // [16][D] (16-bit), the strictly lower decay-weighted key products packed by
@@ -1048,7 +1169,7 @@ __host__ __device__ inline size_t replay_prep16_lds_bytes(int D, int T) {
   return (size_t)T * D * 2 + 16 * (size_t)D * 2 + 120 * sizeof(float) + 16 * (size_t)T * sizeof(float);
 }
 
-template <int D, int IDT>
+template <int D, int IDT, bool FUSED>
 __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayArgs P, float* __restrict__ ws) {
   static_assert(D == 64 || D == 128, "two or four 16-byte chunks per lane");
   static_assert(IDT == GDN_BF16 || IDT == GDN_F16, "16-bit inputs");
@@ -1084,8 +1205,15 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   };
 
   // ---- load round 1: the unit record (slot and the ring pointers after any fold,
-  // written by the fold's check) and the window queries (lane e: query e)
-  const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
+  // written by the fold's check; FUSED: the slot, then the pointers in a round of
+  // their own) and the window queries (lane e: query e)
+  int4 rc;
+  if constexpr (FUSED) {
+    rc.x = p.slot_map[b];
+    if (rc.x < 0 || (int64_t)rc.x >= p.num_slots) rc.x = -1;
+  } else {
+    rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];
+  }
   const int slot = rc.x;
   const float A_log = p.A_log[h], dt_bias = p.dt_bias[h];
   u32x4 qx[NS];
@@ -1101,6 +1229,18 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
     // of after the record's test (that had made them a dependent round of their own)
 #pragma unroll
     for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qx[s]));
+  }
+  bool folds = false;  // FUSED: this unit folds in this step
+  if constexpr (FUSED) {
+    if (slot < 0) {  // padded row: a record that neither folds nor streams a tile
+      if (lane == 0) reinterpret_cast<int4*>(P.rec)[blockIdx.x] = int4{-1, 0, 0, 0};
+      return;
+    }
+    const RingPos rp = ring_pos(R, slot);
+    folds = rp.cnt + T > L;
+    if (lane == 0) reinterpret_cast<int4*>(P.rec)[blockIdx.x] = int4{slot, rp.st, rp.cnt, folds ? 1 : 0};
+    rc.y = folds ? (rp.st + rp.cnt) % L : rp.st;  // the pointers after any fold, as the fold's check gives them
+    rc.z = folds ? 0 : rp.cnt;
   }
   if (slot < 0) return;  // padded row (the stream kernel writes zeros)
   const int64_t unit = (int64_t)slot * p.Hv + h;
@@ -1178,7 +1318,7 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   // ---- key rows to LDS for the column layout; append the window to the ring
 #pragma unroll
   for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(s_k + e * D + 8 * (NS * g + s)) = kx[s];
-  if (live && !committed) {
+  if (live && !committed && !folds) {  // a folding unit's window is appended by the stream
     if (appends_keys(p, h)) {
       char* kd = static_cast<char*>(R.k) + krj * RB + coff;
 #pragma unroll
@@ -1191,12 +1331,12 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    if (j >= cnt && j < n_all) {  // uniform
+    if (j >= cnt && j < n_all && !folds) {  // uniform
       if constexpr (CPL == 2) __builtin_amdgcn_raw_buffer_store_b32(vr[j], rs_vring, 2 * ccol, ring_at(j) * RB, 0);
       else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)vr[j], rs_vring, 2 * ccol, ring_at(j) * RB, 0);
     }
   }
-  if (lane == 0 && h == 0) {  // the slot's pointers, once per slot
+  if (!FUSED && lane == 0 && h == 0) {  // the slot's pointers, once per slot
     R.start[slot] = st;
     R.count[slot] = n_all;
   }
@@ -1292,7 +1432,51 @@ __global__ void __launch_bounds__(64, 8) gdn_replay_prep16_kernel(const ReplayAr
 }
 
 // ---------------------------------------------------------------- stream
-template <int SDT, int D, bool NT, int TB>
+// Fused fold (16-bit inputs): the prep runs first and writes every unit's record
+// {slot, start, count before the step, folds}, the fold then folds the flagged
+// units and writes their windows' outputs, and the stream kernel streams only
+// the tiles of the other units.  The window of a folded unit goes to the ring
+// here, after the fold has read the committed entries it overwrites (the prep
+// appends the windows of the other units), and the first value head of each
+// slot writes the slot's new pointers.
+template <int D>
+__device__ void replay_fused_tail(const ReplayArgs& P, int b, int h, const int4 rc, int tid, int nth) {
+  const DecodeArgs& p = P.d;
+  const RingArgs& R = P.ring;
+  const int T = P.T, L = R.L, slot = rc.x;
+  const bool folded = rc.w != 0;
+  const int st = folded ? (rc.y + rc.z) % L : rc.y;  // rc.y < L, rc.z <= L
+  if (folded) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per 16-bit row
+    const int64_t unit = (int64_t)slot * p.Hv + h, krow = ring_key_base(p, slot, h, L);
+    const int hk = h / (p.Hv / p.Hk);
+    const bool keys = appends_keys(p, h);
+    for (int i = tid; i < T * CPR; i += nth) {
+      const int t = i / CPR, c = 16 * (i - t * CPR);
+      const int pos = st + t >= L ? st + t - L : st + t;  // st < L, t < T <= L
+      const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.v) +
+                                                      (((int64_t)b * T + t) * p.Hv + h) * D * 2 + c);
+      *reinterpret_cast<u32x4*>(static_cast<char*>(R.v) + (unit * L + pos) * D * 2 + c) = v;
+      if (keys) {
+        const u32x4 k = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.k) +
+                                                        (((int64_t)b * T + t) * p.Hk + hk) * D * 2 + c);
+        *reinterpret_cast<u32x4*>(static_cast<char*>(R.k) + (krow + pos) * D * 2 + c) = k;
+      }
+    }
+    if (tid < T) {
+      const int pos = st + tid >= L ? st + tid - L : st + tid;
+      const int64_t gi = ((int64_t)b * T + tid) * p.Hv + h;
+      R.g[unit * L + pos] = gate_g(load_elem(p.a, gi, p.in_dt), p.A_log[h], p.dt_bias[h]);
+      R.beta[unit * L + pos] = sigmoid_f(load_elem(p.b, gi, p.in_dt));
+    }
+  }
+  if (tid == 0 && h == 0) {  // the slot's pointers, once per slot
+    R.start[slot] = st;
+    R.count[slot] = folded ? T : rc.z + T;
+  }
+}
+
+template <int SDT, int D, bool NT, int TB, bool FUSED>
 __global__ void __launch_bounds__((ReplayGeom<SDT, D>::NW * 64))
 gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   using G = ReplayGeom<SDT, D>;
@@ -1308,7 +1492,15 @@ gdn_replay_stream_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / p.Hv;
   const int h = blockIdx.x - b * p.Hv;
-  const int slot = p.slot_map[b];
+  int slot;
+  if constexpr (FUSED) {
+    const int4 rc = reinterpret_cast<const int4*>(P.rec)[blockIdx.x];  // the prep's record
+    slot = rc.x;
+    if (slot >= 0) replay_fused_tail<D>(P, b, h, rc, tid, NTH);
+    if (slot >= 0 && rc.w != 0) return;  // folded: the fold wrote the outputs
+  } else {
+    slot = p.slot_map[b];
+  }
   if (slot < 0 || (int64_t)slot >= p.num_slots) {  // padded row
     for (int i = tid; i < T * D; i += NTH) {
       const int t = i / D, c = i - t * D;
@@ -1405,7 +1597,11 @@ constexpr int kStreamPersistNW = 16;
 constexpr int kStreamPersistMaxIter = 512;
 constexpr int kStreamPersistTMax = 5;  // window positions per unit (LDS: 80 KiB of partials at 5)
 
-template <bool NTL, int TMAX>
+// FUSED: units come from the prep's records.  The workgroup's streamed units
+// (mapped or padded) are listed from the front of the staging arrays and its
+// folded units from the back; a folded unit only appends its window (a wave per
+// unit, before the stream), so the stream walks the first list alone.
+template <bool NTL, int TMAX, bool FUSED>
 __global__ void __launch_bounds__(kStreamPersistNW * 64, 4)
 gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ ws) {
   constexpr int D = 128, NW = kStreamPersistNW, VEC = 4, LPR = 32, RPW = 2, PASSES = D / (RPW * NW);
@@ -1415,16 +1611,39 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   __shared__ __attribute__((aligned(16))) float s_red[2][TMAX][NW][D];  // [parity][position][wave][column]
   __shared__ __attribute__((aligned(16))) float s_w[2][TMAX][D];        // [parity][position][row]: w
   __shared__ int s_slot[kStreamPersistMaxIter];
+  __shared__ int s_unit[FUSED ? kStreamPersistMaxIter : 1];  // FUSED: the units of both lists
+  __shared__ int s_n[2];                                     // FUSED: streamed and folded units
 
   const DecodeArgs& p = P.d;
   const int T = P.T;  // 1 <= T <= TMAX (launcher)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = (lane % LPR) * VEC, r0 = wave * RPW + lane / LPR;
   const int units = p.B * p.Hv, G = gridDim.x;
-  int t = blockIdx.x;
-  if (t >= units) return;
-  const int n_iter = (units - t + G - 1) / G;  // <= kStreamPersistMaxIter (launcher)
-  for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t + i * G) / p.Hv];
+  const int t0 = blockIdx.x;
+  if (t0 >= units) return;
+  const int n_iter = (units - t0 + G - 1) / G;  // <= kStreamPersistMaxIter (launcher)
+  if constexpr (FUSED) {
+    if (tid < 2) s_n[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n_iter; i += NW * 64) {
+      const int u = t0 + i * G;
+      const int4 rc = reinterpret_cast<const int4*>(P.rec)[u];
+      if (rc.x >= 0 && rc.w != 0) {
+        const int k = n_iter - 1 - atomicAdd(&s_n[1], 1);
+        s_unit[k] = u;
+      } else {
+        const int k = atomicAdd(&s_n[0], 1);
+        s_unit[k] = u;
+        s_slot[k] = rc.x;
+        if (rc.x >= 0 && u % p.Hv == 0) {  // the slot's pointers, once per slot
+          P.ring.start[rc.x] = rc.y;
+          P.ring.count[rc.x] = rc.z + T;
+        }
+      }
+    }
+  } else {
+    for (int i = tid; i < n_iter; i += NW * 64) s_slot[i] = p.slot_map[(t0 + i * G) / p.Hv];
+  }
 
   auto valid = [&](int slot) { return slot >= 0 && (int64_t)slot < p.num_slots; };
   // thread tid < T D / 4 carries elements 4 tid.. of the unit's w vectors (w_t by
@@ -1461,17 +1680,33 @@ gdn_replay_stream_persist_kernel(const ReplayArgs P, const float* __restrict__ w
   // barrier of unit i and read before the barrier of unit i + 1, so two buffers
   // serve it too.  acc never passes through LDS.
   In cur, nxt;
-  __syncthreads();  // s_slot
-  fetch(t, s_slot[0], cur);
+  __syncthreads();  // s_slot, s_unit, s_n
+  int n_run = n_iter;  // units streamed
+  if constexpr (FUSED) {
+    n_run = s_n[0];
+    // the folded units' windows (and their slots' pointers), a unit per wave
+    for (int k = wave; k < s_n[1]; k += NW) {
+      const int u = __builtin_amdgcn_readfirstlane(s_unit[n_iter - 1 - k]), h = u % p.Hv;
+      replay_fused_tail<D>(P, u / p.Hv, h, reinterpret_cast<const int4*>(P.rec)[u], lane, 64);
+    }
+    if (n_run == 0) return;  // uniform
+  }
+  auto unit_at = [&](int i) {
+    if constexpr (FUSED) return s_unit[i];
+    else return t0 + i * G;
+  };
+  fetch(unit_at(0), s_slot[0], cur);
   if (wthr) *reinterpret_cast<f32x4*>(&s_w[0][wt][wc]) = cur.w;
   __syncthreads();
-  for (int it = 0, par = 0; t < units; t += G, ++it, par ^= 1) {
-    const int tn = t + G;
+  for (int it = 0, par = 0; it < n_run; ++it, par ^= 1) {
+    const int t = unit_at(it);
+    const bool more = it + 1 < n_run;
     // past the last unit the loads repeat this unit's, with no tile
-    fetch(tn < units ? tn : t, tn < units ? s_slot[it + 1] : -1, nxt);
+    fetch(more ? unit_at(it + 1) : t, more ? s_slot[it + 1] : -1, nxt);
     const int b = t / p.Hv, h = t - b * p.Hv;
     auto out_row = [&](int tt) { return (((int64_t)b * T + tt) * p.Hv + h) * D; };
-    const bool live = valid(s_slot[it]);  // uniform over the workgroup
+    const int sl = s_slot[it];
+    const bool live = valid(sl);  // uniform over the workgroup
     if (live) {
 #pragma unroll
       for (int tt = 0; tt < TMAX; ++tt) {
@@ -1532,14 +1767,21 @@ __global__ void gdn_replay_advance_kernel(const ReplayArgs P) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <int SDT, int D, int EB, int CDT>
+template <int SDT, int D, int EB, int CDT, bool FUSED = false>
 static hipError_t launch_fold(const ReplayArgs& a, hipStream_t s) {
+  constexpr int kFusedTW = 4;  // windows of up to 4 positions use the smaller prefetch
   using G = FoldGeom<SDT, D>;
   constexpr bool NT = (SDT == GDN_F32) && (GDN_REPLAY_NT_F32 != 0);
   void (*kern)(const ReplayArgs);
   int threads;
   size_t lds = replay_fold_lds_bytes(D, a.ring.L);
-  if constexpr ((D == 64 || D == 128) && CDT < 0) {  // the dual-precision fold measured faster on the VALU
+  if constexpr (FUSED) {  // the caller checked L <= 16
+    static_assert((D == 64 || D == 128) && CDT < 0 && EB == 2, "fused fold: 16-bit inputs, MFMA fold");
+    kern = a.T <= kFusedTW ? &gdn_replay_fold_mfma_kernel<SDT, D, NT, EB, CDT, kFusedTW>
+                           : &gdn_replay_fold_mfma_kernel<SDT, D, NT, EB, CDT, 16>;
+    threads = 256;
+    lds = replay_fold_mfma_lds_bytes(D, a.T <= kFusedTW ? kFusedTW : 16);
+  } else if constexpr ((D == 64 || D == 128) && CDT < 0) {  // the dual-precision fold measured faster on the VALU
     if (a.ring.L <= 16) {
       kern = &gdn_replay_fold_mfma_kernel<SDT, D, NT, EB, CDT>;
       threads = 256;
@@ -1575,14 +1817,14 @@ static hipError_t launch_fold_any(const ReplayArgs& a, hipStream_t s) {
   return launch_fold<SDT, D, EB, -1>(a, s);
 }
 
-template <int SDT, int D, bool NT, int TB>
+template <int SDT, int D, bool NT, int TB, bool FUSED>
 static void launch_stream(const ReplayArgs& a, unsigned grid, size_t lds, float* ws, hipStream_t s) {
   using G = ReplayGeom<SDT, D>;
-  hipLaunchKernelGGL((gdn_replay_stream_kernel<SDT, D, NT, TB>), dim3(grid), dim3(G::NW * 64), lds, s, a, ws);
+  hipLaunchKernelGGL((gdn_replay_stream_kernel<SDT, D, NT, TB, FUSED>), dim3(grid), dim3(G::NW * 64), lds, s, a, ws);
 }
 
 // Outputs read the checkpoint itself, or its 16-bit read copy (dual precision).
-template <int D>
+template <int D, bool FUSED>
 static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   const size_t lds = (size_t)a.T * D * sizeof(float);
@@ -1591,8 +1833,9 @@ static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws,
   if constexpr (D == 128) {
     if (read_dt == GDN_F32 && a.T >= 1 && a.T <= kStreamPersistTMax && GDN_REPLAY_STREAM_PERSIST != 0) {
       constexpr bool NTL = GDN_REPLAY_NT_F32 != 0;
-      void (*kern)(const ReplayArgs, const float*) = a.T == 1 ? &gdn_replay_stream_persist_kernel<NTL, 1>
-                                                              : &gdn_replay_stream_persist_kernel<NTL, kStreamPersistTMax>;
+      void (*kern)(const ReplayArgs, const float*) = a.T == 1
+                                                         ? &gdn_replay_stream_persist_kernel<NTL, 1, FUSED>
+                                                         : &gdn_replay_stream_persist_kernel<NTL, kStreamPersistTMax, FUSED>;
       int per_cu = 0, cus = 0;
       hipError_t e = resident_blocks(reinterpret_cast<const void*>(kern), kStreamPersistNW * 64, 0, &per_cu);
       // one workgroup per CU even where two fit (T = 1: 164 against 168 us per call)
@@ -1609,24 +1852,24 @@ static hipError_t launch_stream_any(const ReplayArgs& a, int read_dt, float* ws,
   }
   switch (read_dt) {
     case GDN_F32:
-      one ? launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, 1>(a, grid, lds, ws, s)
-          : launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, kStreamTB>(a, grid, lds, ws, s);
+      one ? launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, 1, FUSED>(a, grid, lds, ws, s)
+          : launch_stream<GDN_F32, D, GDN_REPLAY_NT_F32 != 0, kStreamTB, FUSED>(a, grid, lds, ws, s);
       break;
     case GDN_BF16:
       if (nt16)
-        one ? launch_stream<GDN_BF16, D, true, 1>(a, grid, lds, ws, s)
-            : launch_stream<GDN_BF16, D, true, kStreamTB>(a, grid, lds, ws, s);
+        one ? launch_stream<GDN_BF16, D, true, 1, FUSED>(a, grid, lds, ws, s)
+            : launch_stream<GDN_BF16, D, true, kStreamTB, FUSED>(a, grid, lds, ws, s);
       else
-        one ? launch_stream<GDN_BF16, D, false, 1>(a, grid, lds, ws, s)
-            : launch_stream<GDN_BF16, D, false, kStreamTB>(a, grid, lds, ws, s);
+        one ? launch_stream<GDN_BF16, D, false, 1, FUSED>(a, grid, lds, ws, s)
+            : launch_stream<GDN_BF16, D, false, kStreamTB, FUSED>(a, grid, lds, ws, s);
       break;
     case GDN_F16:
       if (nt16)
-        one ? launch_stream<GDN_F16, D, true, 1>(a, grid, lds, ws, s)
-            : launch_stream<GDN_F16, D, true, kStreamTB>(a, grid, lds, ws, s);
+        one ? launch_stream<GDN_F16, D, true, 1, FUSED>(a, grid, lds, ws, s)
+            : launch_stream<GDN_F16, D, true, kStreamTB, FUSED>(a, grid, lds, ws, s);
       else
-        one ? launch_stream<GDN_F16, D, false, 1>(a, grid, lds, ws, s)
-            : launch_stream<GDN_F16, D, false, kStreamTB>(a, grid, lds, ws, s);
+        one ? launch_stream<GDN_F16, D, false, 1, FUSED>(a, grid, lds, ws, s)
+            : launch_stream<GDN_F16, D, false, kStreamTB, FUSED>(a, grid, lds, ws, s);
       break;
     default:
       return hipErrorInvalidValue;
@@ -1641,21 +1884,36 @@ static hipError_t launch_replay_t(const ReplayArgs& a0, float* ws, hipStream_t s
   a.rec = nullptr;
   if (a.T > 0)  // the preps read the unit records the fold's check writes
     a.rec = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + replay_vectors_bytes(a.d.B, a.d.Hv, a.T, D));
+  const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
+  // fused fold: prep, fold, stream (16-bit 128 x 128 tiles stay apart: the fold's
+  // outputs pushed those kernels past their registers)
+  if constexpr (D == 64 || (D == 128 && SDT == GDN_F32)) {
+    if (a.T > 0 && !f32_in && a.ring.L <= 16 && a.read_pool == nullptr) {
+      const size_t lds = replay_prep16_lds_bytes(D, a.T);
+      if (a.d.in_dt == GDN_BF16)
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_BF16, true>), dim3(grid), dim3(64), lds, s, a, ws);
+      else
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_F16, true>), dim3(grid), dim3(64), lds, s, a, ws);
+      hipError_t e = hipGetLastError();
+      if (e == hipSuccess) e = launch_fold<SDT, D, 2, -1, true>(a, s);
+      if (e != hipSuccess) return e;
+      return launch_stream_any<D, true>(a, SDT, ws, s);
+    }
+  }
   hipError_t e = f32_in ? launch_fold_any<SDT, D, 4>(a, s) : launch_fold_any<SDT, D, 2>(a, s);
   if (e != hipSuccess) return e;
   if (a.T == 0) {  // flush: the slots' pointers move once every head has folded
     hipLaunchKernelGGL(gdn_replay_advance_kernel, dim3((unsigned)((a.d.B + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const unsigned grid = (unsigned)((int64_t)a.d.B * a.d.Hv);
   constexpr int NWP = GDN_REPLAY_PREP_WAVES;
   if constexpr (D == 64 || D == 128) {
     if (!f32_in && a.ring.L <= 16) {
       const size_t lds = replay_prep16_lds_bytes(D, a.T);
       if (a.d.in_dt == GDN_BF16)
-        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_BF16>), dim3(grid), dim3(64), lds, s, a, ws);
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_BF16, false>), dim3(grid), dim3(64), lds, s, a, ws);
       else
-        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_F16>), dim3(grid), dim3(64), lds, s, a, ws);
+        hipLaunchKernelGGL((gdn_replay_prep16_kernel<D, GDN_F16, false>), dim3(grid), dim3(64), lds, s, a, ws);
       goto prep_done;
     }
   }
@@ -1668,10 +1926,10 @@ static hipError_t launch_replay_t(const ReplayArgs& a0, float* ws, hipStream_t s
 prep_done:
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.read_pool == nullptr) return launch_stream_any<D>(a, SDT, ws, s);
+  if (a.read_pool == nullptr) return launch_stream_any<D, false>(a, SDT, ws, s);
   ReplayArgs r = a;
   r.d.pool = a.read_pool;
-  return launch_stream_any<D>(r, a.read_dt, ws, s);
+  return launch_stream_any<D, false>(r, a.read_dt, ws, s);
 }
 
 template <int SDT>
