@@ -799,8 +799,11 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
 #pragma unroll
           for (int r = 0; r < 4; ++r) s0[I][jj][r] = acc[jj][r];
       }
+      constexpr int NC = 2;  // FUSED: MFMA chains per column block of the outputs
+      [[maybe_unused]] f32x4 o[NC][NJ];
       if constexpr (FUSED) {
-        // the window's outputs from the tile as stored, before the write-back:
+        // the window's outputs from the tile as stored (formed here, stored after
+        // the write-back):
         // O = W S with W [positions][rows] as the MFMA's A operand (lane (c, g)
         // gives w_c at rows 16 I + 4 g + r) and the tile as B, two chains per
         // column block; element r of lane (c, g) is position 4 g + r, column c
@@ -812,8 +815,6 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
 #pragma unroll
               for (int r = 0; r < 4; ++r) s0[I][jj][r] = unpack_lo<SDT>(pack2<SDT>(s0[I][jj][r], 0.f));
         }
-        constexpr int NC = 2;  // chains per column block
-        f32x4 o[NC][NJ];
 #pragma unroll
         for (int hh = 0; hh < NC; ++hh)
 #pragma unroll
@@ -828,16 +829,9 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
               o[I % NC][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], o[I % NC][jj], 0, 0, 0);
           }
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int col = 16 * (NJ * wave + jj) + c;
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            if (t < T)
-              store_elem(p.out, (((int64_t)b * T + t) * p.Hv + h) * D + col,
-                         p.scale * (o[0][jj][r] + o[1][jj][r] + e_acc[t * D + col]), p.out_dt);
-          }
-        }
+          for (int r = 0; r < 4; ++r) o[0][jj][r] += o[1][jj][r];
       }
       // ---- write back, rounded once
       int lane_st = lane_off;
@@ -850,6 +844,24 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
           for (int r = 0; r < 4; ++r)
             st_state(rs_tile, lane_st + (r * D + 16 * jj) * SB, 16 * I * D * SB, s0[I][jj][r],
                      std::integral_constant<int, SDT>{});
+      if constexpr (FUSED) {  // the outputs after the write-back, one test of their dtype
+        auto put = [&](auto odt) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) {
+            const int col = 16 * (NJ * wave + jj) + c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * g + r;
+              if (t < T)
+                store_elem(p.out, (((int64_t)b * T + t) * p.Hv + h) * D + col,
+                           p.scale * (o[0][jj][r] + e_acc[t * D + col]), decltype(odt)::value);
+            }
+          }
+        };
+        if (p.out_dt == GDN_BF16) put(std::integral_constant<int, GDN_BF16>{});
+        else if (p.out_dt == GDN_F16) put(std::integral_constant<int, GDN_F16>{});
+        else put(std::integral_constant<int, GDN_F32>{});
+      }
     }
     if constexpr (CDT >= 0) {
       const __amdgpu_buffer_rsrc_t rs_copy = __builtin_amdgcn_make_buffer_rsrc(
