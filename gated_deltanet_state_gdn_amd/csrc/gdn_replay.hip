@@ -819,19 +819,50 @@ __global__ void __launch_bounds__(256, 3) gdn_replay_fold_mfma_kernel(const Repl
         for (int hh = 0; hh < NC; ++hh)
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj) o[hh][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (TW <= 4 && T == 1) {
+          // one position: lane (c, g) sums its rows {16 I + 4 g + r} on the vector
+          // ALU (a short chain per row block) and the four row groups meet in two
+          // lane exchanges; the MFMA would form 16 positions for the one
+          float part[NJ][NI];
 #pragma unroll
-        for (int I = 0; I < NI; ++I)
+          for (int I = 0; I < NI; ++I) {
+            float w[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = c < T ? e_wt[(16 * I + 4 * g + r) * KTS + c] : 0.f;  // columns past TW unwritten
+            for (int r = 0; r < 4; ++r) w[r] = e_wt[(16 * I + 4 * g + r) * KTS];
 #pragma unroll
-            for (int jj = 0; jj < NJ; ++jj)
-              o[I % NC][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], o[I % NC][jj], 0, 0, 0);
+            for (int jj = 0; jj < NJ; ++jj) {
+              float x = s0[I][jj][0] * w[0];
+#pragma unroll
+              for (int r = 1; r < 4; ++r) x = fmaf(s0[I][jj][r], w[r], x);
+              part[jj][I] = x;
+            }
           }
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
+          for (int jj = 0; jj < NJ; ++jj) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[0][jj][r] += o[1][jj][r];
+            for (int n = NI / 2; n >= 1; n /= 2)
+#pragma unroll
+              for (int I = 0; I < n; ++I) part[jj][I] += part[jj][I + n];
+            float x = part[jj][0];
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            o[0][jj][0] = x;  // position 0 in the lanes with g = 0, as from the MFMA
+          }
+        } else {
+#pragma unroll
+          for (int I = 0; I < NI; ++I)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float a = c < T ? e_wt[(16 * I + 4 * g + r) * KTS + c] : 0.f;  // columns past TW unwritten
+#pragma unroll
+              for (int jj = 0; jj < NJ; ++jj)
+                o[I % NC][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s0[I][jj][r], o[I % NC][jj], 0, 0, 0);
+            }
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[0][jj][r] += o[1][jj][r];
+        }
       }
       // ---- write back, rounded once
       int lane_st = lane_off;
