@@ -260,13 +260,16 @@ def test_replay_layer_bf16_spec_sampled():
     c.check_state("flush")
 
 
-@pytest.mark.parametrize("T", [1, 3, 5])
-def test_replay_persistent_stream_padded_rows(T):
-    """fp32 128 x 128 checkpoints, 80 rows x 32 value heads (2560 units, about ten per workgroup of
-    the persistent stream) with padded rows spread through the walk, windows of T tokens over
-    enough steps to cross folds.  Padded rows read as zero outputs, the others match the oracle."""
+@pytest.mark.parametrize("T,D,sdt", [(1, 128, "f32"), (3, 128, "f32"), (5, 128, "f32"), (7, 128, "f32"),
+                                     (1, 64, "bf16")])
+def test_replay_persistent_stream_padded_rows(T, D, sdt):
+    """80 rows x 32 value heads (2560 units, about ten per workgroup of the persistent stream) with
+    padded rows spread through the walk, windows of T tokens over enough steps to cross folds.
+    fp32 128 x 128 checkpoints with T <= 5 take the persistent stream, T = 7 and the 64 x 64 bf16
+    checkpoints the one-shot one; all of them the fused fold (its stream lists and appends).
+    Padded rows read as zero outputs, the others match the oracle."""
     import torch
-    c = ReplayCase(44 + T, 80, 16, 32, 128, 16, "f32", 96, sample=[0, 5, 41, 78])
+    c = ReplayCase(44 + T + (D != 128), 80, 16, 32, D, 16, sdt, 96, sample=[0, 5, 41, 78])
     pad = [3, 17, 40, 79]
     sm = c.slot_map.copy()
     sm[pad] = [-1, 96, -7, 200]
