@@ -22,8 +22,9 @@
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
-// Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles,
-// 2 for 16-bit ones, which then carry as many bytes per lane); fp32 tiles are
+// Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles;
+// for 16-bit ones 2, which then carry as many bytes per lane, and 4 once the
+// launch's tiles exceed the Infinity Cache); fp32 tiles are
 // read and written non-temporally (+7%), 16-bit ones read non-temporally when
 // the launch's tiles exceed the Infinity Cache (stream_tile_reads) and also
 // written so past twice that (stream_tile_writes).
@@ -32,6 +33,12 @@
 #endif
 #ifndef GDN_DECODE_WAVES_16
 #define GDN_DECODE_WAVES_16 2
+#endif
+// 16-bit tiles read past the Infinity Cache (stream_tile_reads): bf16 B = 256
+// 0.0939 -> 0.0897 ms, B = 512 0.2059 -> 0.2017 ms against two waves; at B = 64
+// (cache-resident) two waves stay ahead, 0.0228 against 0.0248 ms
+#ifndef GDN_DECODE_WAVES_16_STREAM
+#define GDN_DECODE_WAVES_16_STREAM 4
 #endif
 #ifndef GDN_DECODE_NT_F32
 #define GDN_DECODE_NT_F32 1
@@ -50,14 +57,15 @@
 
 namespace gdn {
 
-template <int SDT, int D>
-using DecodeGeom = TileGeom<SDT, D, SDT == GDN_F32 ? GDN_DECODE_WAVES : GDN_DECODE_WAVES_16>;
+template <int SDT, int D, int NWG = (SDT == GDN_F32 ? GDN_DECODE_WAVES : GDN_DECODE_WAVES_16)>
+using DecodeGeom = TileGeom<SDT, D, NWG>;
 
-// NT: non-temporal stores (and loads); NTL: non-temporal loads; IDT: the input dtype
-template <int SDT, int D, bool NT, bool NTL, int IDT>
-__global__ void __launch_bounds__((DecodeGeom<SDT, D>::NW * 64))
+// NT: non-temporal stores (and loads); NTL: non-temporal loads; IDT: the input dtype;
+// NWG: waves per workgroup
+template <int SDT, int D, bool NT, bool NTL, int IDT, int NWG>
+__global__ void __launch_bounds__(NWG * 64)
 gdn_decode_kernel(const DecodeArgs p) {
-  using G = DecodeGeom<SDT, D>;
+  using G = DecodeGeom<SDT, D, NWG>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
   constexpr int NT_THREADS = NW * 64;
   using IO = TileIO<SDT, VEC, NT>;
@@ -461,10 +469,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   }
   auto one_shot = [&](auto nt_c, auto ntl_c) {
     constexpr bool N = decltype(nt_c)::value, L = decltype(ntl_c)::value;
-    void (*k)(const DecodeArgs) = a.in_dt == GDN_F32    ? &gdn_decode_kernel<SDT, D, N, L, GDN_F32>
-                                  : a.in_dt == GDN_BF16 ? &gdn_decode_kernel<SDT, D, N, L, GDN_BF16>
-                                                        : &gdn_decode_kernel<SDT, D, N, L, GDN_F16>;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(G::NW * 64), 0, s, a);
+    // 16-bit tiles streamed from HBM: more waves per workgroup
+    constexpr int W = (SDT != GDN_F32 && L) ? GDN_DECODE_WAVES_16_STREAM : G::NW;
+    void (*k)(const DecodeArgs) = a.in_dt == GDN_F32    ? &gdn_decode_kernel<SDT, D, N, L, GDN_F32, W>
+                                  : a.in_dt == GDN_BF16 ? &gdn_decode_kernel<SDT, D, N, L, GDN_BF16, W>
+                                                        : &gdn_decode_kernel<SDT, D, N, L, GDN_F16, W>;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(W * 64), 0, s, a);
   };
   if (!NT && stream_tile_writes(tile_bytes)) one_shot(std::true_type{}, std::true_type{});
   else if (stream_tile_reads(tile_bytes)) one_shot(std::integral_constant<bool, NT>{}, std::true_type{});
