@@ -376,6 +376,18 @@ inline bool stream_tile_reads(long long bytes) { return bytes > kCacheResidentBy
 // 1 to 5%.  fp32 tiles are always streamed.
 inline bool stream_tile_writes(long long bytes) { return bytes > 2 * kCacheResidentBytes; }
 
+// ------------------------------------------------------------------ XCD-aware order
+// MI355X hands workgroup i of a launch to XCD i mod 8.  A one-shot launch whose
+// workgroups first fetch a small index (a slot) before their tile maps workgroup
+// i to unit u so that each XCD takes one contiguous run of units, about G / 8
+// long: the units of one sequence (its heads) then run on one XCD, whose L2 and
+// scalar caches hold that sequence's index line as its heads go by.  A
+// bijection of [0, G) for every G.
+__device__ __forceinline__ int xcd_unit(int i, int G) {
+  const int x = i & 7, k = i >> 3, q = G >> 3, r = G & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // ------------------------------------------------------------------ wave64 reductions
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

@@ -22,6 +22,11 @@
 #ifndef GDN_M2_NT_F32
 #define GDN_M2_NT_F32 1
 #endif
+// one-shot decode workgroups over 16-bit tiles take their units in XCD-aware
+// order (xcd_unit) when the tiles stream past the Infinity Cache both ways
+#ifndef GDN_M2_XCD
+#define GDN_M2_XCD 1
+#endif
 
 namespace gdn {
 
@@ -76,7 +81,7 @@ __device__ __forceinline__ M2Pos m2_pos(const M2Args& a, int64_t slot) {
 // GDN ones.  Unaligned x, B, C or y take the per-element accesses.  The small
 // loads (x, dt, B, C, as raw bits of the input dtype IDT) go out before the
 // tile: loads complete in order, so their waits do not cover the tile.
-template <int SDT, int P, int N, bool NT, int IDT>
+template <int SDT, int P, int N, bool NT, int IDT, bool XO>
 __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kernel(const M2Args a) {
   using G = M2G<SDT, P, N>;
   constexpr int VEC = G::VEC, LPR = G::LPR, RPW = G::RPW, NW = G::NW, PASSES = G::PASSES;
@@ -85,7 +90,8 @@ __global__ void __launch_bounds__((M2G<SDT, P, N>::NW * 64)) gdn_m2_decode_kerne
   using ST = typename StateElem<SDT>::T;
   __shared__ float s_x[P], s_y[P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+  const int u = XO ? xcd_unit(blockIdx.x, gridDim.x) : (int)blockIdx.x;  // XO: XCD-aware order
+  const int b = u / a.H, h = u - (u / a.H) * a.H;
   const int gr = h / (a.H / a.G);
   const int c0 = (lane % LPR) * VEC;
   const int r0 = wave * RPW + lane / LPR;
@@ -668,9 +674,19 @@ static hipError_t m2_launch_t(const M2Args& a, int what, hipStream_t s) {
   constexpr bool NT = (SDT == GDN_F32) && (GDN_M2_NT_F32 != 0);
   const unsigned units = (unsigned)((int64_t)a.B * a.H);
   if (what == 0) {
-    void (*k)(const M2Args) = a.in_dt == GDN_F32    ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F32>
-                              : a.in_dt == GDN_BF16 ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_BF16>
-                                                    : &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F16>;
+    // 16-bit tiles that stream past the Infinity Cache both ways: XCD-aware unit
+    // order (bf16 B = 512: 0.416 -> 0.406 ms; fp32 tiles lost 3% to it)
+    const bool xo = GDN_M2_XCD != 0 && SDT != GDN_F32 &&
+                    stream_tile_writes((long long)units * P * N * (long long)sizeof(typename StateElem<SDT>::T));
+    void (*k)(const M2Args);
+    auto pick = [&](auto xo_c) {
+      constexpr bool X = decltype(xo_c)::value;
+      k = a.in_dt == GDN_F32    ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F32, X>
+          : a.in_dt == GDN_BF16 ? &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_BF16, X>
+                                : &gdn_m2_decode_kernel<SDT, P, N, NT, GDN_F16, X>;
+    };
+    if (xo) pick(std::true_type{});
+    else pick(std::false_type{});
     hipLaunchKernelGGL(k, dim3(units), dim3(G::NW * 64), 0, s, a);
     return hipGetLastError();
   }
