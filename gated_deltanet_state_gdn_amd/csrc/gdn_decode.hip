@@ -23,8 +23,9 @@
 #include "gdn_launch.h"
 
 // Launch tuning (measured on MI355X): waves per workgroup (4 for fp32 tiles;
-// for 16-bit ones 2, which then carry as many bytes per lane, and 4 once the
-// launch's tiles exceed the Infinity Cache); fp32 tiles are
+// for 16-bit ones 2, which then carry as many bytes per lane, 4 once the
+// launch's tiles exceed the Infinity Cache, and 8 once its stores stream too);
+// fp32 tiles are
 // read and written non-temporally (+7%), 16-bit ones read non-temporally when
 // the launch's tiles exceed the Infinity Cache (stream_tile_reads) and also
 // written so past twice that (stream_tile_writes).
